@@ -1,0 +1,281 @@
+/*
+ * moe.h — C-ABI of the routed-expert MoE layer run through a bounded, quantized
+ * expert cache, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; cited by title and section):
+ *   [HF-PR]  "POC: Experts offload" (huggingface/transformers draft PR 50717):
+ *            PR description and its three commit messages.
+ *   [RFC]    "RFC: stream MoE experts from disk in from_pretrained":
+ *            sections "Feature request", "Motivation", "How the prototype works",
+ *            "Questions for maintainers".
+ *   [SUBST]  BigMoeOnEdge docs "Limitations and prior art" with the commit message
+ *            that adds cache-aware substitution (Skliar et al., arXiv:2412.00099).
+ *   [CLASS]  "moe: expert slots in size classes" (1bit engine PR 137): PR
+ *            description, commit message, and the ExpertCache constructor quoted
+ *            in its review.
+ *
+ * ---------------------------------------------------------------------------
+ * Shared conventions
+ * ---------------------------------------------------------------------------
+ * Ownership.  The caller allocates and owns every buffer and every stream/event.
+ *   Device pointers are plain device addresses; the library never frees them.
+ *   The only memory the library allocates is host memory inside a moe_cache.
+ * Asynchrony.  Every GPU entry point only enqueues work on the given stream and
+ *   returns.  Its status covers host-side argument checks and launch errors.
+ * Errors.  Entry points return MOE_OK (0) or a negative MOE_E_* code and set a
+ *   thread-local message readable with moe_last_error().  Faults found on the
+ *   device (an expert that is not resident, a slot out of range, a non-finite
+ *   logit, an expert id out of range) are OR-ed as MOE_ERRW_* bits into the
+ *   caller-owned device word `err_word` (uint32), which the caller reads after
+ *   synchronising; rows touched by such a fault hold unspecified values.
+ *   `err_word` may be NULL, in which case device faults are not reported.
+ * Limits.  1 <= E <= 1024; 1 <= k <= min(E, 32); H and I multiples of 64;
+ *   bits in {3, 4, 6, 8}; T >= 0 (T == 0 is a no-op returning MOE_OK).
+ * Streams.  hipStream_t 0 is the null stream.  No entry point synchronises.
+ *
+ * ---------------------------------------------------------------------------
+ * Byte format of one expert row in a slot ([RFC] "How the prototype works":
+ * experts are gated, concatenated, untransposed, without bias, and each expert
+ * is one contiguous row; the weights are group-wise affine quantized)
+ * ---------------------------------------------------------------------------
+ * An expert with hidden size H and intermediate size I is two matrices:
+ *   gate_up : 2I rows x H columns, rows 0..I-1 are the gate projection and rows
+ *             I..2I-1 the up projection (out x in, like a linear layer: y = W x);
+ *   down    : H rows x I columns.
+ * Each matrix is stored as a code block followed by a scale/bias block.  The four
+ * blocks sit in this order, each starting at a multiple of `align` (256) bytes:
+ *   [gate_up codes][gate_up scale/bias][down codes][down scale/bias]
+ * and slot_bytes is the end of the last block rounded up to `align`.
+ *
+ * Code block of an R x C matrix with b bits per code: row n occupies C*b/8 bytes
+ * starting at n*C*b/8.  Inside a row, values come in pack units of 32: unit u
+ * (columns 32u..32u+31) is b little-endian uint32 words at byte 4*b*u of the
+ * row, and column 32u+i holds bits [b*i, b*i+b) of the 32*b-bit little-endian
+ * integer those words form (for b = 3 and 6 a code may straddle two words).
+ *
+ * Scale/bias block: for row n and group g (columns 64g..64g+63), 4 bytes at
+ * byte offset 4*(n*(C/64) + g): an IEEE fp16 scale s then an IEEE fp16 bias z,
+ * both little-endian.  The dequantized weight is  w[n][c] = s*q + z  with q the
+ * unsigned code; s*q is exact in fp32, so the only rounding is the add.
+ *
+ * ---------------------------------------------------------------------------
+ * Routing numeric contract ([RFC] "Motivation": each token uses k of E experts;
+ * [SUBST] commit message: cache-aware substitution).  Per token, in fp32 with
+ * no contraction of multiplies into adds unless a fused multiply-add is named:
+ *   m   = max_e logit[e]
+ *   e_i = exp_c(logit[i] - m)
+ *   exp_c(x): x < -86 -> 0; n = rint(x * 1.44269502f); r = fma(-n, ln2_hi, x);
+ *             r = fma(-n, ln2_lo, r) with ln2_hi = 0x3f317218, ln2_lo = 0xb102e308;
+ *             degree-7 Taylor polynomial of e^r by Horner with fma, coefficients
+ *             1/7!, 1/6!, 1/5!, 1/4!, 1/3!, 1/2, 1, 1 rounded to fp32;
+ *             result times 2^n (exact).  exp_c(0) == 1.
+ *   Z   = sum of e_i in a fixed order: 64 partials S_l = e_l + e_{l+64} + ...
+ *         (ascending), then S_l += S_{l+32} for l < 32, S_l += S_{l+16} for
+ *         l < 16, ..., S_0 += S_1; Z = S_0.
+ *   p_i = e_i / Z, correctly rounded.
+ *   key_i = p_i (plain mode), or p_i + c for experts with slot_table[i] >= 0 in
+ *         substitution mode, where c = L * (max_e p - min_e p) (one rounded
+ *         subtract, then one rounded multiply).
+ *   ids  = top-k of key by repeated argmax; larger key first, equal keys ->
+ *         smaller expert id first.  Output in that order.
+ *   w_j  = p_{ids_j} / (p_{ids_0} + p_{ids_1} + ... summed left to right).
+ * Substitution changes which experts are chosen, never how they are weighted.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define MOE_OK               0
+#define MOE_E_INVALID       (-1) /* bad dims, bits, k, E, alignment, null pointer */
+#define MOE_E_UNSUPPORTED   (-2) /* valid but not implemented                   */
+#define MOE_E_NOT_RESIDENT  (-3) /* host-side check found a non-resident expert */
+#define MOE_E_NO_SLOT       (-4) /* every slot of the size class is reserved   */
+#define MOE_E_HIP           (-5) /* a HIP runtime call failed                   */
+#define MOE_E_BUSY          (-6) /* a fill of this entry is still in flight     */
+#define MOE_E_WORKSPACE     (-7) /* workspace smaller than the size query says  */
+
+/* ---- device error-word bits --------------------------------------------- */
+#define MOE_ERRW_NOT_RESIDENT  0x1u /* routed expert has slot_table[e] < 0      */
+#define MOE_ERRW_BAD_SLOT      0x2u /* slot_table[e] >= n_slots                 */
+#define MOE_ERRW_NONFINITE     0x4u /* a router logit is NaN or infinite        */
+#define MOE_ERRW_BAD_ID        0x8u /* a top-k id outside [0, E)                */
+
+/* ---- routing modes ------------------------------------------------------- */
+#define MOE_ROUTE_PLAIN  0
+#define MOE_ROUTE_SUBST  1
+
+/* ---- forward path selection --------------------------------------------- */
+#define MOE_PATH_AUTO  0 /* GEMV for few pairs per expert, MFMA otherwise       */
+#define MOE_PATH_GEMV  1 /* dequant-GEMV kernels (decode)                       */
+#define MOE_PATH_MFMA  2 /* dequant + bf16 MFMA grouped GEMM (prefill)          */
+
+/* ---- cache install sources ----------------------------------------------- */
+#define MOE_SRC_HOST    0 /* pinned host memory (hipHostMalloc)                 */
+#define MOE_SRC_DEVICE  1 /* device memory                                      */
+
+/*
+ * Size class: every expert whose row has the same byte size shares one pool of
+ * slots and one LRU ([CLASS] PR description: layers are grouped by the bytes one
+ * expert needs, and each group has its own slots and LRU).  Filled by
+ * moe_size_class_init; all offsets are bytes from the start of a slot row.
+ */
+typedef struct moe_size_class_desc {
+    int32_t H;            /* hidden size (multiple of 64)                      */
+    int32_t I;            /* expert intermediate size (multiple of 64)         */
+    int32_t bits_gu;      /* code width of gate_up: 3, 4, 6 or 8               */
+    int32_t bits_d;       /* code width of down:    3, 4, 6 or 8               */
+    int32_t group;        /* quantization group along the input dim: 64        */
+    int32_t align;        /* block alignment in bytes: 256                     */
+    int64_t n_slots;      /* slots in this class's pool                        */
+    int64_t off_gu_codes; /* = 0                                               */
+    int64_t off_gu_sb;
+    int64_t off_d_codes;
+    int64_t off_d_sb;
+    int64_t slot_bytes;   /* bytes of one slot row (multiple of align)         */
+} moe_size_class_desc;
+
+/*
+ * Fill `d` for an expert of the given shape and code widths.  group must be 64
+ * and align 256 in this version.  Returns MOE_E_INVALID on bad arguments.
+ * Source: [RFC] "How the prototype works" (one contiguous row per expert) and
+ * [CLASS] PR description (bytes one expert needs = sum of its aligned windows).
+ */
+int moe_size_class_init(moe_size_class_desc* d, int H, int I, int bits_gu, int bits_d,
+                        int group, int align, int64_t n_slots);
+
+/*
+ * Router: softmax over E logits, top-k, renormalised weights, per the routing
+ * numeric contract above.  In MOE_ROUTE_SUBST mode every expert with
+ * slot_table[e] >= 0 gets L times the token's probability range added to its
+ * selection key before top-k is taken ([SUBST] commit message); the weights
+ * still come from the unbiased probabilities.
+ *   logits     device fp32 [T, E], row-major.
+ *   slot_table device int32 [E]; read only in MOE_ROUTE_SUBST mode (else NULL ok).
+ *   topk_ids   device int32 [T, k] (out);  topk_w device fp32 [T, k] (out).
+ *   err_word   device uint32 (may be NULL): MOE_ERRW_NONFINITE on NaN/inf logits.
+ * Sources: [RFC] "Motivation" (each token uses 10 of 512 experts, only the top-k
+ * are read); [SUBST] commit message.
+ */
+int moe_route_topk(const float* logits, int T, int E, int k, int mode, float L,
+                   const int32_t* slot_table, int32_t* topk_ids, float* topk_w,
+                   uint32_t* err_word, hipStream_t stream);
+
+/*
+ * Sort the T*k (token, slot j) pairs by expert.  Pair id p = t*k + j.
+ *   expert_offsets device int32 [E+1] (out): offsets[e] = number of pairs routed
+ *                  to experts < e; offsets[E] = T*k.
+ *   sorted_pairs   device int32 [T*k] (out): pairs of expert e, ascending pair id,
+ *                  at [offsets[e], offsets[e+1]).
+ *   pass_table     device int32 [moe_pass_table_size(E, pass_experts)] (out):
+ *                  [0] = n_hit (experts with at least one pair), [1] = n_passes,
+ *                  [2 .. 2+E) = hit expert ids ascending, then -1;
+ *                  [2+E .. 2+E+ceil(E/P)+1) = pass starts into the hit list:
+ *                  pass q covers hit-list entries [start_q, start_{q+1}), at most
+ *                  pass_experts (P) each; unused starts equal n_hit.
+ *   ws             device scratch of moe_sort_workspace_size(T, k, E) bytes.
+ *   err_word       MOE_ERRW_BAD_ID if an id is outside [0, E); such pairs are dropped.
+ * Sources: [HF-PR] commit messages (sorted prefill runs 64 experts at a time);
+ * [RFC] "How the prototype works", Prefill bullet (sorted gather in groups of 64).
+ */
+int moe_sort_by_expert(const int32_t* topk_ids, int T, int k, int E, int pass_experts,
+                       int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pass_table,
+                       void* ws, size_t ws_bytes, uint32_t* err_word, hipStream_t stream);
+size_t moe_sort_workspace_size(int T, int k, int E);
+int    moe_pass_table_size(int E, int pass_experts);
+
+/*
+ * The routed experts of one layer:
+ *   out[t] = sum_j topk_w[t,j] * down_e( silu(gate_e(x[t])) * up_e(x[t]) ),
+ *   e = topk_ids[t,j], each linear map using the dequantized weights of the slot
+ *   slot_table[e] of the pool `slot_pool` laid out as described by `d`.
+ * Runs the sort internally (into ws), then gate/up + SwiGLU, down and the
+ * weighted combine in fixed order (bit-reproducible run to run).
+ *   x          device bf16 [T, H] (hipBfloat16 bits as uint16).
+ *   topk_ids   device int32 [T, k];  topk_w device fp32 [T, k].
+ *   slot_table device int32 [E]: slot of each expert, -1 if not resident.
+ *   slot_pool  device bytes [d->n_slots * d->slot_bytes].
+ *   out        device bf16 [T, H] (overwritten; round to nearest even).
+ *   ws         device scratch of moe_forward_workspace_size(...) bytes.
+ *   err_word   MOE_ERRW_NOT_RESIDENT / MOE_ERRW_BAD_SLOT / MOE_ERRW_BAD_ID.
+ * `path` selects the kernels (MOE_PATH_*); moe_experts_forward uses AUTO.
+ * Sources: [HF-PR] PR description (experts run through gather_qmm on the cache);
+ * [RFC] "How the prototype works" (Cache, Prefill and Quantized experts bullets).
+ */
+int moe_experts_forward(const void* x, int T, const int32_t* topk_ids, const float* topk_w,
+                        int k, int E, const int32_t* slot_table, const void* slot_pool,
+                        const moe_size_class_desc* d, void* out, void* ws, size_t ws_bytes,
+                        uint32_t* err_word, hipStream_t stream);
+int moe_experts_forward_ex(const void* x, int T, const int32_t* topk_ids, const float* topk_w,
+                           int k, int E, const int32_t* slot_table, const void* slot_pool,
+                           const moe_size_class_desc* d, void* out, void* ws, size_t ws_bytes,
+                           uint32_t* err_word, int path, hipStream_t stream);
+size_t moe_forward_workspace_size(int T, int k, int E, const moe_size_class_desc* d);
+
+/*
+ * Enqueue the copy of one expert row (d->slot_bytes bytes at `src`) into slot
+ * `slot` of `slot_pool` on `copy_stream`, then record `done` (may be NULL) on it.
+ * src_kind: MOE_SRC_HOST (pinned host memory) or MOE_SRC_DEVICE.  The copy is
+ * asynchronous; the slot must not be read until `done` has completed (wait on it
+ * from the compute stream).  Source: [RFC] "How the prototype works", Reads
+ * bullet (one contiguous read and one non-blocking host-to-device copy per
+ * expert); [HF-PR] host-tier commit message.
+ */
+int moe_cache_install(void* slot_pool, const moe_size_class_desc* d, int64_t slot,
+                      const void* src, int src_kind, hipStream_t copy_stream, hipEvent_t done);
+
+/*
+ * Host-side bounded expert cache: size classes, one LRU per class, per-layer
+ * expert -> slot tables.  Source: [RFC] "How the prototype works", Cache bullet
+ * (preallocated pool of slots, LRU, per-layer expert -> slot table on the host);
+ * [CLASS] PR description and constructor (slots of a class are contiguous, slot
+ * byte offsets are running sums, empty slots sit at the LRU's back and are taken
+ * first; each class has its own LRU and budget never moves between classes).
+ *
+ * moe_cache_create: classes[n_classes] (n_slots of each is that class's budget);
+ *   layer_class[n_layers] maps each layer to its class; E experts per layer.
+ *   Returns NULL on bad arguments (see moe_last_error).
+ * moe_cache_acquire: make (layer, expert) resident.  Hit -> *slot, *needs_fill=0,
+ *   entry moved to the LRU front.  Miss -> takes the LRU-back slot of the layer's
+ *   class that is not pinned and not in flight, evicts its owner (its table entry
+ *   becomes -1), *needs_fill = 1, and the entry is reserved (in flight) until
+ *   moe_cache_fill_done / moe_cache_poll completes it.  MOE_E_NO_SLOT when every
+ *   slot of the class is reserved or pinned.  An entry already in flight returns
+ *   MOE_E_BUSY with *slot set and *needs_fill = 0.
+ * moe_cache_fill_done: attach the event recorded after the install; the entry
+ *   stays reserved until the event completes (checked by moe_cache_poll, and
+ *   before every eviction).  ev == NULL marks the fill complete at once.
+ * moe_cache_pin / moe_cache_unpin: keep (layer, expert) from eviction while a
+ *   pass that reads it is queued (counted).
+ * moe_cache_table: copy layer's expert -> slot table (int32 [E], -1 = absent)
+ *   into host memory `table`.
+ * moe_cache_stats: hits, misses, evictions since creation (any may be NULL).
+ */
+typedef struct moe_cache moe_cache;
+moe_cache* moe_cache_create(const moe_size_class_desc* classes, int n_classes,
+                            const int32_t* layer_class, int n_layers, int E);
+void moe_cache_destroy(moe_cache* c);
+int  moe_cache_acquire(moe_cache* c, int layer, int expert, int64_t* slot, int* needs_fill);
+int  moe_cache_fill_done(moe_cache* c, int layer, int expert, hipEvent_t ev);
+int  moe_cache_poll(moe_cache* c);
+int  moe_cache_pin(moe_cache* c, int layer, int expert);
+int  moe_cache_unpin(moe_cache* c, int layer, int expert);
+int  moe_cache_table(const moe_cache* c, int layer, int32_t* table);
+int  moe_cache_lookup(const moe_cache* c, int layer, int expert, int64_t* slot);
+int  moe_cache_stats(const moe_cache* c, int64_t* hits, int64_t* misses, int64_t* evictions);
+int  moe_cache_class_of(const moe_cache* c, int layer);
+
+/* Thread-local message for the last failing call on this thread. */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

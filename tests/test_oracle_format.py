@@ -1,0 +1,116 @@
+"""Pins of the oracle's slot-format decoder and layout against hand-derived
+fixtures (tests/golden/pack_units.txt, tests/golden/layout.txt), the test
+quantizer's own arrays, and exact closed forms.
+
+The pages give the format only as group-wise affine quantization with one
+contiguous row per expert ("RFC: stream MoE experts from disk in
+from_pretrained", How the prototype works, Quantized experts); the bit order
+and block order are this build's reading, written in include/moe.h.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from quantized_routed_expert_softmax_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _units():
+    rows = []
+    with open(os.path.join(GOLDEN, "pack_units.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            b, codes, words = [c.strip() for c in line.split("|")]
+            rows.append((int(b), [int(v) for v in codes.split()], [int(v, 16) for v in words.split()]))
+    return rows
+
+
+@pytest.mark.parametrize("case", _units())
+def test_pack_unit_golden(case):
+    bits, codes, words = case
+    assert len(codes) == 32 and len(words) == bits
+    unit = np.array(words, dtype="<u4").view(np.uint8)
+    assert [oracle.code(unit, bits, i) for i in range(32)] == codes
+    # the generator's packer writes the same bytes
+    packed = synth.pack_codes(np.array([codes], dtype=np.uint8), bits)
+    assert packed.reshape(-1).tolist() == unit.tolist()
+
+
+@pytest.mark.parametrize("bits", [3, 4, 6, 8])
+def test_pack_round_trip(bits):
+    rng = synth.rng_for(40, bits)
+    q = rng.integers(0, 1 << bits, size=(3, 256), dtype=np.uint8)
+    packed = synth.pack_codes(q, bits)
+    for r in range(3):
+        got = [oracle.code(packed[r], bits, c) for c in range(256)]
+        assert got == q[r].tolist()
+
+
+def _layouts():
+    rows = []
+    with open(os.path.join(GOLDEN, "layout.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            a, b = line.split("|")
+            rows.append(([int(v) for v in a.split()], [int(v) for v in b.split()]))
+    return rows
+
+
+@pytest.mark.parametrize("case", _layouts())
+def test_layout_golden(case):
+    (H, I, bg, bd), offs = case
+    assert oracle.layout(H, I, bg, bd).tolist() == offs
+    lay = synth.Layout(H, I, bg, bd)
+    assert [lay.off_gu_codes, lay.off_gu_sb, lay.off_d_codes, lay.off_d_sb, lay.slot_bytes] == offs
+
+
+@pytest.mark.parametrize("bg,bd", [(4, 4), (3, 3), (8, 8), (4, 6), (6, 3)])
+def test_dequant_equals_scale_code_plus_bias(bg, bd):
+    """The oracle's decoded weights equal s*q + z computed in fp64 from the
+    quantizer's arrays (exact: s*q + z of fp16 values is exact in fp64)."""
+    H, I = 128, 64
+    rng = synth.rng_for(41, bg, bd)
+    e, w_gu, w_d = synth.gaussian_expert(rng, H, I, bg, bd)
+    lay = synth.Layout(H, I, bg, bd)
+    row = synth.expert_row(lay, e)
+    for which, (q, s, z) in enumerate([(e.gu_q, e.gu_s, e.gu_z), (e.d_q, e.d_s, e.d_z)]):
+        ref = q.astype(np.float64) * np.repeat(s.astype(np.float64), 64, axis=1) \
+            + np.repeat(z.astype(np.float64), 64, axis=1)
+        got = oracle.dequant(row, H, I, bg, bd, which)
+        assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("bits", [3, 4, 6, 8])
+def test_dequant_within_quantization_error(bits):
+    """|w_hat - w| <= s/2 plus the fp16 rounding of scale and bias (bounded by
+    (2^b - 1) * |s16 - s| + |z16 - z|, taken loosely as 2^-10 of the group's
+    range per term) for the test quantizer."""
+    H, I = 128, 64
+    rng = synth.rng_for(42, bits)
+    e, w_gu, w_d = synth.gaussian_expert(rng, H, I, bits, bits)
+    row = synth.expert_row(synth.Layout(H, I, bits, bits), e)
+    got = oracle.dequant(row, H, I, bits, bits, 0)
+    g = w_gu.astype(np.float64).reshape(2 * I, H // 64, 64)
+    rngp = (g.max(axis=2) - g.min(axis=2))
+    s = e.gu_s.astype(np.float64)
+    bound = np.repeat(s / 2 + 2 * 2.0 ** -10 * rngp + 1e-7, 64, axis=1)
+    assert np.all(np.abs(got - w_gu) <= bound)
+
+
+def test_integer_closed_form():
+    """Scale 1, bias 0: the decoded weights are the codes exactly."""
+    H, I, b = 64, 64, 8
+    rng = synth.rng_for(43)
+    q_gu = rng.integers(0, 256, size=(2 * I, H), dtype=np.uint8)
+    q_d = rng.integers(0, 256, size=(H, I), dtype=np.uint8)
+    one = np.ones((2 * I, 1), np.float16)
+    e = synth.ExpertQ(q_gu, one, np.zeros_like(one), q_d, np.ones((H, 1), np.float16),
+                      np.zeros((H, 1), np.float16))
+    row = synth.expert_row(synth.Layout(H, I, b, b), e)
+    assert np.array_equal(oracle.dequant(row, H, I, b, b, 0), q_gu.astype(np.float64))
+    assert np.array_equal(oracle.dequant(row, H, I, b, b, 1), q_d.astype(np.float64))
