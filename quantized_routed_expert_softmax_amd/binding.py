@@ -1,0 +1,319 @@
+"""Thin ctypes binding of libmoe.so (include/moe.h).
+
+Argument marshalling only: shapes, dtypes and devices of torch tensors are
+checked, raw device pointers and the current HIP stream are passed on, and a
+non-zero status becomes MoeError.  Every step of the layer runs in the HIP
+kernels of libmoe.so; there is no fallback.  PyTorch only provides device
+memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
+
+MOE_OK = 0
+MOE_E_INVALID = -1
+MOE_E_UNSUPPORTED = -2
+MOE_E_NOT_RESIDENT = -3
+MOE_E_NO_SLOT = -4
+MOE_E_HIP = -5
+MOE_E_BUSY = -6
+MOE_E_WORKSPACE = -7
+
+MOE_ERRW_NOT_RESIDENT = 0x1
+MOE_ERRW_BAD_SLOT = 0x2
+MOE_ERRW_NONFINITE = 0x4
+MOE_ERRW_BAD_ID = 0x8
+
+MOE_ROUTE_PLAIN = 0
+MOE_ROUTE_SUBST = 1
+MOE_PATH_AUTO = 0
+MOE_PATH_GEMV = 1
+MOE_PATH_MFMA = 2
+MOE_SRC_HOST = 0
+MOE_SRC_DEVICE = 1
+
+PASS_EXPERTS = 64
+
+_lock = threading.Lock()
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"moe error {code}: {msg}")
+        self.code = code
+
+
+class SizeClassDesc(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("I", ctypes.c_int32), ("bits_gu", ctypes.c_int32),
+                ("bits_d", ctypes.c_int32), ("group", ctypes.c_int32), ("align", ctypes.c_int32),
+                ("n_slots", ctypes.c_int64), ("off_gu_codes", ctypes.c_int64),
+                ("off_gu_sb", ctypes.c_int64), ("off_d_codes", ctypes.c_int64),
+                ("off_d_sb", ctypes.c_int64), ("slot_bytes", ctypes.c_int64)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so; raises if it has not been built (no silent fallback)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                                   "`python -m quantized_routed_expert_softmax_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            P, I32, I64, F32, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                    ctypes.c_size_t)
+            D = ctypes.POINTER(SizeClassDesc)
+            sig = {
+                "moe_size_class_init": (I32, [D, I32, I32, I32, I32, I32, I32, I64]),
+                "moe_route_topk": (I32, [P, I32, I32, I32, I32, F32, P, P, P, P, P]),
+                "moe_sort_by_expert": (I32, [P, I32, I32, I32, I32, P, P, P, P, SZ, P, P]),
+                "moe_sort_workspace_size": (SZ, [I32, I32, I32]),
+                "moe_pass_table_size": (I32, [I32, I32]),
+                "moe_experts_forward": (I32, [P, I32, P, P, I32, I32, P, P, D, P, P, SZ, P, P]),
+                "moe_experts_forward_ex": (I32, [P, I32, P, P, I32, I32, P, P, D, P, P, SZ, P, I32, P]),
+                "moe_forward_workspace_size": (SZ, [I32, I32, I32, D]),
+                "moe_cache_install": (I32, [P, D, I64, P, I32, P, P]),
+                "moe_cache_create": (P, [D, I32, P, I32, I32]),
+                "moe_cache_destroy": (None, [P]),
+                "moe_cache_acquire": (I32, [P, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(I32)]),
+                "moe_cache_fill_done": (I32, [P, I32, I32, P]),
+                "moe_cache_poll": (I32, [P]),
+                "moe_cache_pin": (I32, [P, I32, I32]),
+                "moe_cache_unpin": (I32, [P, I32, I32]),
+                "moe_cache_table": (I32, [P, I32, P]),
+                "moe_cache_lookup": (I32, [P, I32, I32, ctypes.POINTER(I64)]),
+                "moe_cache_stats": (I32, [P, ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I64)]),
+                "moe_cache_class_of": (I32, [P, I32]),
+                "moe_last_error": (ctypes.c_char_p, []),
+            }
+            for name, (res, args) in sig.items():
+                f = getattr(L, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/moe.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != MOE_OK:
+        raise MoeError(rc, moe_last_error())
+
+
+# --------------------------------------------------------------------------- #
+# tensor marshalling                                                           #
+# --------------------------------------------------------------------------- #
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, dtype, name, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _opt_ptr(t, dtype, name):
+    return None if t is None else _dev_ptr(t, dtype, name)
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def moe_size_class_init(H: int, I: int, bits_gu: int, bits_d: int, n_slots: int,
+                        group: int = 64, align: int = 256) -> SizeClassDesc:
+    d = SizeClassDesc()
+    _check(lib().moe_size_class_init(ctypes.byref(d), H, I, bits_gu, bits_d, group, align, n_slots))
+    return d
+
+
+def moe_route_topk(logits, k: int, mode: int = MOE_ROUTE_PLAIN, L: float = 0.0, slot_table=None,
+                   topk_ids=None, topk_w=None, err_word=None, stream=None):
+    """Softmax top-k routing (and cache-aware substitution in MOE_ROUTE_SUBST)."""
+    torch = _torch()
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib().moe_route_topk(_dev_ptr(logits, torch.float32, "logits", 2), T, E, k, mode, L,
+                                _opt_ptr(slot_table, torch.int32, "slot_table"),
+                                _dev_ptr(topk_ids, torch.int32, "topk_ids"),
+                                _dev_ptr(topk_w, torch.float32, "topk_w"),
+                                _opt_ptr(err_word, torch.int32, "err_word"), _stream(stream)))
+    return topk_ids, topk_w
+
+
+def moe_pass_table_size(E: int, pass_experts: int = PASS_EXPERTS) -> int:
+    return lib().moe_pass_table_size(E, pass_experts)
+
+
+def moe_sort_workspace_size(T: int, k: int, E: int) -> int:
+    return lib().moe_sort_workspace_size(T, k, E)
+
+
+def moe_sort_by_expert(topk_ids, E: int, pass_experts: int = PASS_EXPERTS, err_word=None, ws=None,
+                       stream=None):
+    """Stable sort of (token, j) pairs by expert; returns (offsets, sorted_pairs, pass_table)."""
+    torch = _torch()
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_pairs = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    pass_table = torch.empty(moe_pass_table_size(E, pass_experts), dtype=torch.int32, device=dev)
+    need = moe_sort_workspace_size(T, k, E)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(lib().moe_sort_by_expert(_dev_ptr(topk_ids, torch.int32, "topk_ids", 2), T, k, E,
+                                    pass_experts, _dev_ptr(offsets, None, "offsets"),
+                                    _dev_ptr(sorted_pairs, None, "sorted_pairs"),
+                                    _dev_ptr(pass_table, None, "pass_table"),
+                                    _dev_ptr(ws, torch.uint8, "ws"), ws.numel(),
+                                    _opt_ptr(err_word, torch.int32, "err_word"), _stream(stream)))
+    return offsets, sorted_pairs[:T * k], pass_table
+
+
+def moe_forward_workspace_size(T: int, k: int, E: int, desc: SizeClassDesc) -> int:
+    return lib().moe_forward_workspace_size(T, k, E, ctypes.byref(desc))
+
+
+def moe_experts_forward(x, topk_ids, topk_w, E: int, slot_table, slot_pool, desc: SizeClassDesc,
+                        out=None, ws=None, err_word=None, path: int = MOE_PATH_AUTO, stream=None):
+    """The routed experts of one layer: out = sum_j w_j * down(silu(gate x) * up x)."""
+    torch = _torch()
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    if H != desc.H:
+        raise ValueError(f"x has {H} columns, size class has H={desc.H}")
+    if slot_pool.numel() < desc.n_slots * desc.slot_bytes:
+        raise ValueError("slot_pool smaller than n_slots * slot_bytes")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(moe_forward_workspace_size(T, k, E, desc), 256), dtype=torch.uint8,
+                         device=x.device)
+    _check(lib().moe_experts_forward_ex(
+        _dev_ptr(x, torch.bfloat16, "x", 2), T, _dev_ptr(topk_ids, torch.int32, "topk_ids", 2),
+        _dev_ptr(topk_w, torch.float32, "topk_w", 2), k, E,
+        _dev_ptr(slot_table, torch.int32, "slot_table", 1), _dev_ptr(slot_pool, torch.uint8, "slot_pool"),
+        ctypes.byref(desc), _dev_ptr(out, torch.bfloat16, "out", 2), _dev_ptr(ws, torch.uint8, "ws"),
+        ws.numel(), _opt_ptr(err_word, torch.int32, "err_word"), path, _stream(stream)))
+    return out
+
+
+def moe_cache_install(slot_pool, desc: SizeClassDesc, slot: int, src, stream=None, event=None):
+    """Async copy of one expert row into `slot`; src is a pinned host or device uint8 tensor."""
+    torch = _torch()
+    if src.numel() < desc.slot_bytes or src.dtype != torch.uint8 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous uint8 tensor of at least slot_bytes")
+    if src.device.type == "cuda":
+        kind = MOE_SRC_DEVICE
+    else:
+        if not src.is_pinned():
+            raise ValueError("host source must be pinned memory")
+        kind = MOE_SRC_HOST
+    ev = None if event is None else ctypes.c_void_p(event.cuda_event)
+    _check(lib().moe_cache_install(_dev_ptr(slot_pool, torch.uint8, "slot_pool"), ctypes.byref(desc),
+                                   slot, ctypes.c_void_p(src.data_ptr()), kind, _stream(stream), ev))
+
+
+# --------------------------------------------------------------------------- #
+# host cache                                                                   #
+# --------------------------------------------------------------------------- #
+def moe_cache_create(classes: list[SizeClassDesc], layer_class: list[int], E: int) -> int:
+    arr = (SizeClassDesc * len(classes))(*classes)
+    lc = (ctypes.c_int32 * len(layer_class))(*layer_class)
+    h = lib().moe_cache_create(arr, len(classes), lc, len(layer_class), E)
+    if not h:
+        raise MoeError(MOE_E_INVALID, moe_last_error())
+    return h
+
+
+def moe_cache_destroy(c: int):
+    lib().moe_cache_destroy(c)
+
+
+def moe_cache_acquire(c: int, layer: int, expert: int) -> tuple[int, int, int]:
+    """Returns (status, slot, needs_fill); status is MOE_OK or MOE_E_BUSY, other
+    codes raise."""
+    slot = ctypes.c_int64(-1)
+    nf = ctypes.c_int32(0)
+    rc = lib().moe_cache_acquire(c, layer, expert, ctypes.byref(slot), ctypes.byref(nf))
+    if rc not in (MOE_OK, MOE_E_BUSY):
+        _check(rc)
+    return rc, slot.value, nf.value
+
+
+def moe_cache_fill_done(c: int, layer: int, expert: int, event=None):
+    ev = None if event is None else ctypes.c_void_p(event.cuda_event)
+    _check(lib().moe_cache_fill_done(c, layer, expert, ev))
+
+
+def moe_cache_poll(c: int) -> int:
+    rc = lib().moe_cache_poll(c)
+    if rc < 0:
+        _check(rc)
+    return rc
+
+
+def moe_cache_pin(c: int, layer: int, expert: int):
+    _check(lib().moe_cache_pin(c, layer, expert))
+
+
+def moe_cache_unpin(c: int, layer: int, expert: int):
+    _check(lib().moe_cache_unpin(c, layer, expert))
+
+
+def moe_cache_table(c: int, layer: int, E: int):
+    import numpy as np
+    t = np.empty(E, dtype=np.int32)
+    _check(lib().moe_cache_table(c, layer, t.ctypes.data_as(ctypes.c_void_p)))
+    return t
+
+
+def moe_cache_lookup(c: int, layer: int, expert: int) -> int:
+    s = ctypes.c_int64(-1)
+    _check(lib().moe_cache_lookup(c, layer, expert, ctypes.byref(s)))
+    return s.value
+
+
+def moe_cache_stats(c: int) -> tuple[int, int, int]:
+    h, m, e = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().moe_cache_stats(c, ctypes.byref(h), ctypes.byref(m), ctypes.byref(e)))
+    return h.value, m.value, e.value
+
+
+def moe_cache_class_of(c: int, layer: int) -> int:
+    return lib().moe_cache_class_of(c, layer)

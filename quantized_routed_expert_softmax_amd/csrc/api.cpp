@@ -1,0 +1,288 @@
+// api.cpp — the C-ABI of include/moe.h: argument checks, workspace carving and
+// kernel launches.  No entry point allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what)
+{
+    return fail(MOE_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool bits_ok(int b) { return b == 3 || b == 4 || b == 6 || b == 8; }
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int kPassExperts = 64;  // experts per pass of the sorted prefill
+
+int check_desc(const moe_size_class_desc* d)
+{
+    if (!d) return fail(MOE_E_INVALID, "size class descriptor is NULL");
+    moe_size_class_desc ref;
+    if (moe_size_class_init(&ref, d->H, d->I, d->bits_gu, d->bits_d, d->group, d->align, d->n_slots) != MOE_OK)
+        return MOE_E_INVALID;
+    if (ref.off_gu_codes != d->off_gu_codes || ref.off_gu_sb != d->off_gu_sb ||
+        ref.off_d_codes != d->off_d_codes || ref.off_d_sb != d->off_d_sb ||
+        ref.slot_bytes != d->slot_bytes)
+        return fail(MOE_E_INVALID, "size class descriptor offsets do not match its shape");
+    return MOE_OK;
+}
+
+moe::ClassView view_of(const moe_size_class_desc* d)
+{
+    moe::ClassView c;
+    c.H = d->H;
+    c.I = d->I;
+    c.bits_gu = d->bits_gu;
+    c.bits_d = d->bits_d;
+    c.n_slots = d->n_slots;
+    c.slot_bytes = d->slot_bytes;
+    c.off_gu_codes = d->off_gu_codes;
+    c.off_gu_sb = d->off_gu_sb;
+    c.off_d_codes = d->off_d_codes;
+    c.off_d_sb = d->off_d_sb;
+    return c;
+}
+
+struct FwdLayout {
+    size_t offsets, sorted, pass, sort_ws, hbuf, xp, ybuf, total;
+};
+
+FwdLayout fwd_layout(int T, int k, int E, const moe_size_class_desc* d)
+{
+    FwdLayout L;
+    const size_t n = (size_t)T * k;
+    size_t o = 0;
+    L.offsets = o;
+    o = align_up(o + sizeof(int32_t) * (E + 1), 256);
+    L.sorted = o;
+    o = align_up(o + sizeof(int32_t) * n, 256);
+    L.pass = o;
+    o = align_up(o + sizeof(int32_t) * (size_t)moe_pass_table_size(E, kPassExperts), 256);
+    L.sort_ws = o;
+    o = align_up(o + moe::sort_ws_bytes(T, k, E), 256);
+    L.hbuf = o;
+    o = align_up(o + sizeof(uint16_t) * n * (size_t)d->I, 256);
+    L.xp = o;
+    o = align_up(o + sizeof(uint16_t) * (size_t)T * d->H, 256);
+    L.ybuf = o;
+    o = align_up(o + sizeof(float) * n * (size_t)d->H, 256);
+    L.total = o;
+    return L;
+}
+
+}  // namespace
+
+int moe::set_error(int code, const char* msg)
+{
+    g_last_error = msg;
+    return code;
+}
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_size_class_init(moe_size_class_desc* d, int H, int I, int bits_gu, int bits_d, int group,
+                        int align, int64_t n_slots)
+{
+    if (!d) return fail(MOE_E_INVALID, "descriptor is NULL");
+    if (group != 64) return fail(MOE_E_INVALID, "group must be 64 (got %d)", group);
+    if (align != 256) return fail(MOE_E_INVALID, "align must be 256 (got %d)", align);
+    if (H <= 0 || I <= 0 || H % 64 || I % 64)
+        return fail(MOE_E_INVALID, "H and I must be positive multiples of 64 (H=%d I=%d)", H, I);
+    if (!bits_ok(bits_gu) || !bits_ok(bits_d))
+        return fail(MOE_E_INVALID, "bits must be 3, 4, 6 or 8 (gate_up %d, down %d)", bits_gu, bits_d);
+    if (n_slots < 0) return fail(MOE_E_INVALID, "n_slots < 0");
+    const int64_t gu_codes = (int64_t)2 * I * H * bits_gu / 8;
+    const int64_t gu_sb = (int64_t)2 * I * (H / 64) * 4;
+    const int64_t d_codes = (int64_t)H * I * bits_d / 8;
+    const int64_t d_sb = (int64_t)H * (I / 64) * 4;
+    d->H = H;
+    d->I = I;
+    d->bits_gu = bits_gu;
+    d->bits_d = bits_d;
+    d->group = group;
+    d->align = align;
+    d->n_slots = n_slots;
+    d->off_gu_codes = 0;
+    d->off_gu_sb = (int64_t)align_up((size_t)gu_codes, align);
+    d->off_d_codes = (int64_t)align_up((size_t)(d->off_gu_sb + gu_sb), align);
+    d->off_d_sb = (int64_t)align_up((size_t)(d->off_d_codes + d_codes), align);
+    d->slot_bytes = (int64_t)align_up((size_t)(d->off_d_sb + d_sb), align);
+    return MOE_OK;
+}
+
+int moe_route_topk(const float* logits, int T, int E, int k, int mode, float L,
+                   const int32_t* slot_table, int32_t* topk_ids, float* topk_w, uint32_t* err_word,
+                   hipStream_t stream)
+{
+    if (T < 0) return fail(MOE_E_INVALID, "T < 0");
+    if (E < 1 || E > 1024) return fail(MOE_E_INVALID, "E must be in [1, 1024] (got %d)", E);
+    if (k < 1 || k > E || k > 32) return fail(MOE_E_INVALID, "k must be in [1, min(E, 32)] (got %d)", k);
+    if (mode != MOE_ROUTE_PLAIN && mode != MOE_ROUTE_SUBST)
+        return fail(MOE_E_INVALID, "unknown routing mode %d", mode);
+    if (mode == MOE_ROUTE_SUBST) {
+        if (!slot_table) return fail(MOE_E_INVALID, "substitution needs the slot table");
+        if (!(L >= 0.0f) || !std::isfinite(L)) return fail(MOE_E_INVALID, "L must be finite and >= 0");
+    }
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_w) return fail(MOE_E_INVALID, "NULL buffer");
+    hipError_t e = moe::launch_route(logits, T, E, k, mode, L, slot_table, topk_ids, topk_w,
+                                     err_word, stream);
+    if (e != hipSuccess) return hip_fail(e, "route_topk launch");
+    return MOE_OK;
+}
+
+int moe_pass_table_size(int E, int pass_experts)
+{
+    if (E < 1 || pass_experts < 1) return 0;
+    return 2 + E + (E + pass_experts - 1) / pass_experts + 1;
+}
+
+size_t moe_sort_workspace_size(int T, int k, int E)
+{
+    if (T < 0 || k < 1 || E < 1) return 0;
+    return moe::sort_ws_bytes(T, k, E);
+}
+
+int moe_sort_by_expert(const int32_t* topk_ids, int T, int k, int E, int pass_experts,
+                       int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pass_table,
+                       void* ws, size_t ws_bytes, uint32_t* err_word, hipStream_t stream)
+{
+    if (T < 0) return fail(MOE_E_INVALID, "T < 0");
+    if (E < 1 || E > 1024) return fail(MOE_E_INVALID, "E must be in [1, 1024] (got %d)", E);
+    if (k < 1 || k > E || k > 32) return fail(MOE_E_INVALID, "k must be in [1, min(E, 32)] (got %d)", k);
+    if (pass_experts < 1) return fail(MOE_E_INVALID, "pass_experts must be >= 1");
+    if ((int64_t)T * k > (int64_t)1 << 26) return fail(MOE_E_INVALID, "T*k too large");
+    if (T == 0) return MOE_OK;
+    if (!topk_ids || !expert_offsets || !sorted_pairs || !pass_table)
+        return fail(MOE_E_INVALID, "NULL buffer");
+    const size_t need = moe::sort_ws_bytes(T, k, E);
+    if (ws_bytes < need || (need && !ws))
+        return fail(MOE_E_WORKSPACE, "sort workspace %zu bytes < %zu", ws_bytes, need);
+    hipError_t e = moe::launch_sort(topk_ids, T, k, E, pass_experts, expert_offsets, sorted_pairs,
+                                    pass_table, ws, err_word, stream);
+    if (e != hipSuccess) return hip_fail(e, "sort launch");
+    return MOE_OK;
+}
+
+size_t moe_forward_workspace_size(int T, int k, int E, const moe_size_class_desc* d)
+{
+    if (T < 0 || k < 1 || E < 1 || !d || d->H <= 0 || d->I <= 0) return 0;
+    return fwd_layout(T, k, E, d).total;
+}
+
+int moe_experts_forward_ex(const void* x, int T, const int32_t* topk_ids, const float* topk_w,
+                           int k, int E, const int32_t* slot_table, const void* slot_pool,
+                           const moe_size_class_desc* d, void* out, void* ws, size_t ws_bytes,
+                           uint32_t* err_word, int path, hipStream_t stream)
+{
+    if (int rc = check_desc(d)) return rc;
+    if (T < 0) return fail(MOE_E_INVALID, "T < 0");
+    if (E < 1 || E > 1024) return fail(MOE_E_INVALID, "E must be in [1, 1024] (got %d)", E);
+    if (k < 1 || k > E || k > 32) return fail(MOE_E_INVALID, "k must be in [1, min(E, 32)] (got %d)", k);
+    if (path != MOE_PATH_AUTO && path != MOE_PATH_GEMV && path != MOE_PATH_MFMA)
+        return fail(MOE_E_INVALID, "unknown path %d", path);
+    if ((int64_t)T * k > (int64_t)1 << 26) return fail(MOE_E_INVALID, "T*k too large");
+    if (T == 0) return MOE_OK;
+    if (!x || !topk_ids || !topk_w || !slot_table || !slot_pool || !out)
+        return fail(MOE_E_INVALID, "NULL buffer");
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(slot_pool, 256) || !aligned(ws, 256))
+        return fail(MOE_E_INVALID, "x/out need 16-byte, slot_pool/ws 256-byte alignment");
+    const FwdLayout L = fwd_layout(T, k, E, d);
+    if (ws_bytes < L.total) return fail(MOE_E_WORKSPACE, "forward workspace %zu bytes < %zu", ws_bytes, L.total);
+
+    const moe::ClassView c = view_of(d);
+    const bool gemv_ok = moe::gemv_supported(T, k, c);
+    if (path == MOE_PATH_GEMV && !gemv_ok)
+        return fail(MOE_E_UNSUPPORTED, "GEMV path supports T <= 64 and H/32, I/32 with an odd part <= 4");
+    if (path == MOE_PATH_AUTO) path = (gemv_ok && (int64_t)T * k <= 128) ? MOE_PATH_GEMV : MOE_PATH_MFMA;
+
+    char* w = (char*)ws;
+    int32_t* offsets = (int32_t*)(w + L.offsets);
+    int32_t* sorted = (int32_t*)(w + L.sorted);
+    int32_t* pass = (int32_t*)(w + L.pass);
+    uint16_t* hbuf = (uint16_t*)(w + L.hbuf);
+    hipError_t e = moe::launch_sort(topk_ids, T, k, E, kPassExperts, offsets, sorted, pass,
+                                    w + L.sort_ws, err_word, stream);
+    if (e != hipSuccess) return hip_fail(e, "sort launch");
+    moe::SortView sv{offsets, sorted, pass};
+    const uint8_t* pool = (const uint8_t*)slot_pool;
+    if (path == MOE_PATH_GEMV) {
+        e = moe::launch_gemv_gateup((const uint16_t*)x, T, k, E, sv, slot_table, pool, c, hbuf,
+                                    err_word, stream);
+        if (e != hipSuccess) return hip_fail(e, "gemv gate/up launch");
+        e = moe::launch_gemv_down(T, k, E, sv, topk_w, slot_table, pool, c, hbuf, (uint16_t*)out,
+                                  err_word, stream);
+        if (e != hipSuccess) return hip_fail(e, "gemv down launch");
+        return MOE_OK;
+    }
+    uint16_t* xp = (uint16_t*)(w + L.xp);
+    float* ybuf = (float*)(w + L.ybuf);
+    e = moe::launch_permute_x((const uint16_t*)x, T, c.H, xp, stream);
+    if (e != hipSuccess) return hip_fail(e, "permute launch");
+    e = moe::launch_mfma_gateup(xp, T, k, E, sv, slot_table, pool, c, hbuf, err_word, stream);
+    if (e != hipSuccess) return hip_fail(e, "mfma gate/up launch");
+    e = moe::launch_mfma_down(T, k, E, sv, slot_table, pool, c, hbuf, ybuf, err_word, stream);
+    if (e != hipSuccess) return hip_fail(e, "mfma down launch");
+    e = moe::launch_combine(ybuf, topk_w, T, k, c.H, (uint16_t*)out, stream);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    return MOE_OK;
+}
+
+int moe_experts_forward(const void* x, int T, const int32_t* topk_ids, const float* topk_w, int k,
+                        int E, const int32_t* slot_table, const void* slot_pool,
+                        const moe_size_class_desc* d, void* out, void* ws, size_t ws_bytes,
+                        uint32_t* err_word, hipStream_t stream)
+{
+    return moe_experts_forward_ex(x, T, topk_ids, topk_w, k, E, slot_table, slot_pool, d, out, ws,
+                                  ws_bytes, err_word, MOE_PATH_AUTO, stream);
+}
+
+int moe_cache_install(void* slot_pool, const moe_size_class_desc* d, int64_t slot, const void* src,
+                      int src_kind, hipStream_t copy_stream, hipEvent_t done)
+{
+    if (int rc = check_desc(d)) return rc;
+    if (!slot_pool || !src) return fail(MOE_E_INVALID, "NULL buffer");
+    if (slot < 0 || slot >= d->n_slots)
+        return fail(MOE_E_INVALID, "slot %lld outside [0, %lld)", (long long)slot, (long long)d->n_slots);
+    hipMemcpyKind kind;
+    if (src_kind == MOE_SRC_HOST) kind = hipMemcpyHostToDevice;
+    else if (src_kind == MOE_SRC_DEVICE) kind = hipMemcpyDeviceToDevice;
+    else return fail(MOE_E_INVALID, "unknown source kind %d", src_kind);
+    char* dst = (char*)slot_pool + (size_t)slot * (size_t)d->slot_bytes;
+    hipError_t e = hipMemcpyAsync(dst, src, (size_t)d->slot_bytes, kind, copy_stream);
+    if (e != hipSuccess) return hip_fail(e, "install copy");
+    if (done) {
+        e = hipEventRecord(done, copy_stream);
+        if (e != hipSuccess) return hip_fail(e, "install event");
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"

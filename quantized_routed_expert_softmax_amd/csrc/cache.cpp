@@ -1,0 +1,241 @@
+// cache.cpp — host side of the bounded expert cache: size classes, one LRU per
+// class, per-layer expert -> slot tables, reservation of slots whose fill is in
+// flight.
+//
+// Sources: "RFC: stream MoE experts from disk in from_pretrained", How the
+// prototype works, Cache (one preallocated pool of expert slots, LRU, per-layer
+// expert -> slot table kept on the host) and Reads (misses filled by one
+// non-blocking host-to-device copy per expert); "POC: Experts offload", host-tier
+// commit message (rows stay reserved until the copy that reads them has run);
+// "moe: expert slots in size classes", PR description and the ExpertCache
+// constructor in its review (layers grouped by bytes per expert; each group has
+// its own slots and LRU; slots of a class are contiguous; empty slots sit at the
+// LRU's back and are taken first; budget never moves between classes).
+//
+// All operations are O(1) (list splice + table lookup) and guarded by one mutex:
+// fills may be reported from I/O threads.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <list>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+struct CacheSlot {
+    int32_t layer = -1;
+    int32_t expert = -1;
+    int32_t pins = 0;
+    bool inflight = false;
+    hipEvent_t ev = nullptr;
+    std::list<int64_t>::iterator it;
+};
+
+struct CacheClass {
+    moe_size_class_desc desc;
+    std::vector<CacheSlot> slots;
+    std::list<int64_t> lru;  // front = most recently used, back = next victim
+};
+
+struct moe_cache {
+    std::vector<CacheClass> classes;
+    std::vector<int32_t> layer_class;
+    int E = 0;
+    std::vector<std::vector<int64_t>> table;  // [layer][expert] -> slot, -1 absent
+    int64_t hits = 0, misses = 0, evictions = 0;
+    mutable std::mutex mu;
+};
+
+namespace {
+
+int cache_fail(int code, const char* msg) { return moe::set_error(code, msg); }
+
+// A slot whose fill event has completed is no longer in flight.
+void poll_slot(CacheSlot& s)
+{
+    if (s.inflight && s.ev) {
+        if (hipEventQuery(s.ev) == hipSuccess) {
+            s.inflight = false;
+            s.ev = nullptr;
+        }
+    }
+}
+
+bool layer_ok(const moe_cache* c, int layer, int expert)
+{
+    return c && layer >= 0 && layer < (int)c->layer_class.size() && expert >= 0 && expert < c->E;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_cache* moe_cache_create(const moe_size_class_desc* classes, int n_classes,
+                            const int32_t* layer_class, int n_layers, int E)
+{
+    if (!classes || n_classes < 1 || !layer_class || n_layers < 1 || E < 1) {
+        cache_fail(MOE_E_INVALID, "moe_cache_create: bad arguments");
+        return nullptr;
+    }
+    for (int l = 0; l < n_layers; ++l)
+        if (layer_class[l] < 0 || layer_class[l] >= n_classes) {
+            cache_fail(MOE_E_INVALID, "moe_cache_create: layer class out of range");
+            return nullptr;
+        }
+    moe_cache* c = new (std::nothrow) moe_cache;
+    if (!c) return nullptr;
+    c->E = E;
+    c->layer_class.assign(layer_class, layer_class + n_layers);
+    c->table.assign(n_layers, std::vector<int64_t>(E, -1));
+    c->classes.resize(n_classes);
+    for (int ci = 0; ci < n_classes; ++ci) {
+        CacheClass& k = c->classes[ci];
+        k.desc = classes[ci];
+        if (k.desc.n_slots < 0) {
+            delete c;
+            cache_fail(MOE_E_INVALID, "moe_cache_create: negative slot count");
+            return nullptr;
+        }
+        k.slots.resize((size_t)k.desc.n_slots);
+        for (int64_t s = 0; s < k.desc.n_slots; ++s) {
+            k.lru.push_back(s);  // empty slots at the back: taken first
+            k.slots[(size_t)s].it = std::prev(k.lru.end());
+        }
+    }
+    return c;
+}
+
+void moe_cache_destroy(moe_cache* c) { delete c; }
+
+int moe_cache_class_of(const moe_cache* c, int layer)
+{
+    if (!c || layer < 0 || layer >= (int)c->layer_class.size()) return -1;
+    return c->layer_class[layer];
+}
+
+int moe_cache_acquire(moe_cache* c, int layer, int expert, int64_t* slot, int* needs_fill)
+{
+    if (!layer_ok(c, layer, expert) || !slot || !needs_fill)
+        return cache_fail(MOE_E_INVALID, "moe_cache_acquire: bad arguments");
+    std::lock_guard<std::mutex> lock(c->mu);
+    CacheClass& k = c->classes[c->layer_class[layer]];
+    *needs_fill = 0;
+    int64_t s = c->table[layer][expert];
+    if (s >= 0) {
+        CacheSlot& cs = k.slots[(size_t)s];
+        poll_slot(cs);
+        *slot = s;
+        k.lru.splice(k.lru.begin(), k.lru, cs.it);
+        if (cs.inflight) return MOE_E_BUSY;
+        ++c->hits;
+        return MOE_OK;
+    }
+    // miss: the least recently used slot that is neither pinned nor in flight
+    for (auto it = k.lru.rbegin(); it != k.lru.rend(); ++it) {
+        CacheSlot& cs = k.slots[(size_t)*it];
+        poll_slot(cs);
+        if (cs.pins > 0 || cs.inflight) continue;
+        const int64_t v = *it;
+        if (cs.layer >= 0) {
+            c->table[cs.layer][cs.expert] = -1;
+            ++c->evictions;
+        }
+        cs.layer = layer;
+        cs.expert = expert;
+        cs.inflight = true;
+        cs.ev = nullptr;
+        c->table[layer][expert] = v;
+        k.lru.splice(k.lru.begin(), k.lru, cs.it);
+        ++c->misses;
+        *slot = v;
+        *needs_fill = 1;
+        return MOE_OK;
+    }
+    *slot = -1;
+    return cache_fail(MOE_E_NO_SLOT, "moe_cache_acquire: every slot of the class is pinned or in flight");
+}
+
+int moe_cache_fill_done(moe_cache* c, int layer, int expert, hipEvent_t ev)
+{
+    if (!layer_ok(c, layer, expert)) return cache_fail(MOE_E_INVALID, "moe_cache_fill_done: bad arguments");
+    std::lock_guard<std::mutex> lock(c->mu);
+    const int64_t s = c->table[layer][expert];
+    if (s < 0) return cache_fail(MOE_E_NOT_RESIDENT, "moe_cache_fill_done: entry not resident");
+    CacheSlot& cs = c->classes[c->layer_class[layer]].slots[(size_t)s];
+    if (!cs.inflight) return cache_fail(MOE_E_INVALID, "moe_cache_fill_done: no fill in flight");
+    if (ev) {
+        cs.ev = ev;
+        poll_slot(cs);
+    } else {
+        cs.inflight = false;
+        cs.ev = nullptr;
+    }
+    return MOE_OK;
+}
+
+int moe_cache_poll(moe_cache* c)
+{
+    if (!c) return cache_fail(MOE_E_INVALID, "moe_cache_poll: NULL cache");
+    std::lock_guard<std::mutex> lock(c->mu);
+    int still = 0;
+    for (auto& k : c->classes)
+        for (auto& cs : k.slots) {
+            poll_slot(cs);
+            still += cs.inflight ? 1 : 0;
+        }
+    return still;
+}
+
+int moe_cache_pin(moe_cache* c, int layer, int expert)
+{
+    if (!layer_ok(c, layer, expert)) return cache_fail(MOE_E_INVALID, "moe_cache_pin: bad arguments");
+    std::lock_guard<std::mutex> lock(c->mu);
+    const int64_t s = c->table[layer][expert];
+    if (s < 0) return cache_fail(MOE_E_NOT_RESIDENT, "moe_cache_pin: entry not resident");
+    ++c->classes[c->layer_class[layer]].slots[(size_t)s].pins;
+    return MOE_OK;
+}
+
+int moe_cache_unpin(moe_cache* c, int layer, int expert)
+{
+    if (!layer_ok(c, layer, expert)) return cache_fail(MOE_E_INVALID, "moe_cache_unpin: bad arguments");
+    std::lock_guard<std::mutex> lock(c->mu);
+    const int64_t s = c->table[layer][expert];
+    if (s < 0) return cache_fail(MOE_E_NOT_RESIDENT, "moe_cache_unpin: entry not resident");
+    CacheSlot& cs = c->classes[c->layer_class[layer]].slots[(size_t)s];
+    if (cs.pins <= 0) return cache_fail(MOE_E_INVALID, "moe_cache_unpin: not pinned");
+    --cs.pins;
+    return MOE_OK;
+}
+
+int moe_cache_table(const moe_cache* c, int layer, int32_t* table)
+{
+    if (!c || !table || layer < 0 || layer >= (int)c->layer_class.size())
+        return cache_fail(MOE_E_INVALID, "moe_cache_table: bad arguments");
+    std::lock_guard<std::mutex> lock(c->mu);
+    for (int e = 0; e < c->E; ++e) table[e] = (int32_t)c->table[layer][e];
+    return MOE_OK;
+}
+
+int moe_cache_lookup(const moe_cache* c, int layer, int expert, int64_t* slot)
+{
+    if (!layer_ok(c, layer, expert) || !slot) return cache_fail(MOE_E_INVALID, "moe_cache_lookup: bad arguments");
+    std::lock_guard<std::mutex> lock(c->mu);
+    *slot = c->table[layer][expert];
+    return MOE_OK;
+}
+
+int moe_cache_stats(const moe_cache* c, int64_t* hits, int64_t* misses, int64_t* evictions)
+{
+    if (!c) return cache_fail(MOE_E_INVALID, "moe_cache_stats: NULL cache");
+    std::lock_guard<std::mutex> lock(c->mu);
+    if (hits) *hits = c->hits;
+    if (misses) *misses = c->misses;
+    if (evictions) *evictions = c->evictions;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,349 @@
+// mfma.hip — prefill path of the routed-expert layer on gfx950: a grouped
+// dequantizing GEMM on bf16 matrix cores (v_mfma_f32_16x16x32_bf16).
+//
+// Sources: "RFC: stream MoE experts from disk in from_pretrained", How the
+// prototype works, Prefill (a long prompt routes to nearly every expert; they
+// run through the sorted gather quantized matmul in groups of 64) and Quantized
+// experts (group-wise affine format); "POC: Experts offload", commit messages
+// (sorted prefill, 64 experts at a time).
+//
+// Work split: a workgroup owns (hit expert, 64 output columns); each of its 4
+// waves owns 16 columns and loops over the expert's rows (its sorted pairs) in
+// M-tiles of 16, up to 4 M-tiles per sweep of K.  Weights are read once per
+// sweep straight from the slot pool into registers: lane (column n, lane group
+// g) reads the few dwords holding its 8 codes of the current 32-wide K step and
+// turns them into 4 bf16 pairs (128 + c, the P16 pairing) without LDS.  The
+// activations were laid out in the same P16 order, so one 16-byte load per lane
+// is the A operand.
+//
+// The affine map is applied per group of 64 inputs after the matrix core has
+// summed codes against activations:
+//     sum_{i in g} x_i (s c_i + z) = s * [sum x (128 + c)] + (z - 128 s) * [sum x]
+// Both brackets are MFMA results (the second against a B operand of ones), so
+// the codes never need a scale multiply or a float conversion.
+//
+// gate/up: SwiGLU in registers (a wave holds gate column n and up column I + n
+// in identical accumulator layouts), h written as bf16 in P16 order.
+// down: y per (pair, output) in fp32 to a workspace; a combine kernel adds the
+// k contributions of each token in j order (deterministic).
+#include "../../include/moe.h"
+#include "moe_dev.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+__device__ __forceinline__ f32x4_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// The 4 P16 pairs (codes 4g+r and 4g+r+16, r = 0..3) of lane group g in the
+// unit starting at dword pointer `unit`.
+template <int B>
+__device__ __forceinline__ u32x4_t lane_pairs(const uint32_t* __restrict__ unit, int g)
+{
+    u32x4_t r;
+    if constexpr (B == 8) {
+        const uint32_t lo = unit[g], hi = unit[4 + g];
+        const float a0 = ubyte_f32<0>(lo), b0 = ubyte_f32<0>(hi);
+        const float a1 = ubyte_f32<1>(lo), b1 = ubyte_f32<1>(hi);
+        const float a2 = ubyte_f32<2>(lo), b2 = ubyte_f32<2>(hi);
+        const float a3 = ubyte_f32<3>(lo), b3 = ubyte_f32<3>(hi);
+        r.x = __builtin_amdgcn_perm(__float_as_uint(b0), __float_as_uint(a0), 0x07060302u);
+        r.y = __builtin_amdgcn_perm(__float_as_uint(b1), __float_as_uint(a1), 0x07060302u);
+        r.z = __builtin_amdgcn_perm(__float_as_uint(b2), __float_as_uint(a2), 0x07060302u);
+        r.w = __builtin_amdgcn_perm(__float_as_uint(b3), __float_as_uint(a3), 0x07060302u);
+    } else {
+        const int ol = 4 * g * B;              // first low code bit
+        const int oh = ol + 16 * B - 16;       // window whose bit 16 is the first high code bit
+        const int dl = ol >> 5, sl = ol & 31;
+        const int dh = oh >> 5, sh = oh & 31;
+        const uint64_t lo64 = (uint64_t)unit[dl] | ((uint64_t)unit[dl + 1] << 32);
+        const uint64_t hi64 = (uint64_t)unit[dh] | ((uint64_t)unit[dh + 1] << 32);
+        constexpr int S = Code<B>::per_t;  // 5 (B=3), 4 (B=4), 2 (B=6)
+        constexpr uint32_t M2 = Code<B>::mask2;
+        uint32_t p[4];
+#pragma unroll
+        for (int q = 0; q < 4; q += S) {
+            const uint32_t wl = (uint32_t)(lo64 >> (sl + q * B));
+            const uint32_t wh = (uint32_t)(hi64 >> (sh + q * B));
+            const uint32_t t = (wl & 0xFFFFu) | (wh & 0xFFFF0000u);
+#pragma unroll
+            for (int m = 0; m < S; ++m)
+                if (q + m < 4) p[q + m] = ((t >> (B * m)) & M2) | MOE_MAGIC_PAIR;
+        }
+        r.x = p[0];
+        r.y = p[1];
+        r.z = p[2];
+        r.w = p[3];
+    }
+    return r;
+}
+
+constexpr int kMaxMT = 4;  // M-tiles (of 16 rows) per K sweep
+
+template <int B>
+__global__ __launch_bounds__(256) void mfma_gateup_kernel(
+    const uint16_t* __restrict__ xp, int H, int I, int k, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table,
+    const int32_t* __restrict__ table, const uint8_t* __restrict__ pool, int64_t n_slots,
+    int64_t slot_bytes, int64_t off_codes, int64_t off_sb, uint16_t* __restrict__ hbuf,
+    uint32_t* __restrict__ err)
+{
+    const int hit = blockIdx.y;
+    if (hit >= pass_table[0]) return;
+    const int e = pass_table[2 + hit];
+    const int32_t slot = table[e];
+    if (slot < 0 || slot >= n_slots) {
+        if (threadIdx.x == 0 && err) atomicOr(err, slot < 0 ? MOE_ERRW_NOT_RESIDENT : MOE_ERRW_BAD_SLOT);
+        return;
+    }
+    const int base = offsets[e], cnt = offsets[e + 1] - base;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int n = blockIdx.x * 64 + wave * 16 + c16;  // gate column; up column I + n
+
+    const uint8_t* rowb = pool + (size_t)slot * (size_t)slot_bytes;
+    const size_t row_dw = (size_t)H * B / 32;
+    const uint32_t* gc = (const uint32_t*)(rowb + off_codes) + (size_t)n * row_dw;
+    const uint32_t* uc = (const uint32_t*)(rowb + off_codes) + (size_t)(I + n) * row_dw;
+    const uint32_t* gsb = (const uint32_t*)(rowb + off_sb) + (size_t)n * (H / 64);
+    const uint32_t* usb = (const uint32_t*)(rowb + off_sb) + (size_t)(I + n) * (H / 64);
+    constexpr float off = Code<B>::offset;
+    const u32x4_t ones = {MOE_ONES_PAIR, MOE_ONES_PAIR, MOE_ONES_PAIR, MOE_ONES_PAIR};
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+
+    for (int m0 = 0; m0 < cnt; m0 += 16 * kMaxMT) {
+        const int nmt = min(kMaxMT, (cnt - m0 + 15) >> 4);
+        const u32x4_t* arow[kMaxMT];
+#pragma unroll
+        for (int mt = 0; mt < kMaxMT; ++mt) {
+            int r = m0 + mt * 16 + c16;
+            r = r < cnt ? r : cnt - 1;
+            const int t = sorted_pairs[base + r] / k;
+            arow[mt] = (const u32x4_t*)(xp + (size_t)t * H);
+        }
+        f32x4_t accg[kMaxMT], accu[kMaxMT];
+#pragma unroll
+        for (int mt = 0; mt < kMaxMT; ++mt) accg[mt] = accu[mt] = zero;
+
+        for (int G = 0; G < H / 64; ++G) {
+            const u32x4_t bg0 = lane_pairs<B>(gc + (2 * G) * B, g);
+            const u32x4_t bg1 = lane_pairs<B>(gc + (2 * G + 1) * B, g);
+            const u32x4_t bu0 = lane_pairs<B>(uc + (2 * G) * B, g);
+            const u32x4_t bu1 = lane_pairs<B>(uc + (2 * G + 1) * B, g);
+            const uint32_t g2 = gsb[G], u2 = usb[G];
+            const float sg = half_bits_to_f32(g2 & 0xFFFFu);
+            const float zg = __builtin_fmaf(-off, sg, half_bits_to_f32(g2 >> 16));
+            const float su = half_bits_to_f32(u2 & 0xFFFFu);
+            const float zu = __builtin_fmaf(-off, su, half_bits_to_f32(u2 >> 16));
+#pragma unroll
+            for (int mt = 0; mt < kMaxMT; ++mt) {
+                if (mt < nmt) {
+                    const u32x4_t a0 = arow[mt][(2 * G) * 4 + g];
+                    const u32x4_t a1 = arow[mt][(2 * G + 1) * 4 + g];
+                    f32x4_t tg = mfma(a0, bg0, zero);
+                    tg = mfma(a1, bg1, tg);
+                    f32x4_t tu = mfma(a0, bu0, zero);
+                    tu = mfma(a1, bu1, tu);
+                    f32x4_t tx = mfma(a0, ones, zero);
+                    tx = mfma(a1, ones, tx);
+                    accg[mt] += sg * tg + zg * tx;
+                    accu[mt] += su * tu + zu * tx;
+                }
+            }
+        }
+        const int pos = (n & ~31) | p16_pos(n & 31);
+#pragma unroll
+        for (int mt = 0; mt < kMaxMT; ++mt) {
+            if (mt < nmt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = m0 + mt * 16 + 4 * g + i;
+                    if (r < cnt)
+                        hbuf[(size_t)(base + r) * I + pos] = f32_to_bf16(silu_mul(accg[mt][i], accu[mt][i]));
+                }
+            }
+        }
+    }
+}
+
+template <int B>
+__global__ __launch_bounds__(256) void mfma_down_kernel(
+    int H, int I, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
+    const int32_t* __restrict__ pass_table, const int32_t* __restrict__ table,
+    const uint8_t* __restrict__ pool, int64_t n_slots, int64_t slot_bytes, int64_t off_codes,
+    int64_t off_sb, const uint16_t* __restrict__ hbuf, float* __restrict__ ybuf,
+    uint32_t* __restrict__ err)
+{
+    const int hit = blockIdx.y;
+    if (hit >= pass_table[0]) return;
+    const int e = pass_table[2 + hit];
+    const int32_t slot = table[e];
+    if (slot < 0 || slot >= n_slots) {
+        if (threadIdx.x == 0 && err) atomicOr(err, slot < 0 ? MOE_ERRW_NOT_RESIDENT : MOE_ERRW_BAD_SLOT);
+        return;
+    }
+    const int base = offsets[e], cnt = offsets[e + 1] - base;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int n = blockIdx.x * 64 + wave * 16 + c16;  // output row of the down matrix
+
+    const uint8_t* rowb = pool + (size_t)slot * (size_t)slot_bytes;
+    const size_t row_dw = (size_t)I * B / 32;
+    const uint32_t* dc = (const uint32_t*)(rowb + off_codes) + (size_t)n * row_dw;
+    const uint32_t* dsb = (const uint32_t*)(rowb + off_sb) + (size_t)n * (I / 64);
+    constexpr float off = Code<B>::offset;
+    const u32x4_t ones = {MOE_ONES_PAIR, MOE_ONES_PAIR, MOE_ONES_PAIR, MOE_ONES_PAIR};
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+
+    for (int m0 = 0; m0 < cnt; m0 += 16 * kMaxMT) {
+        const int nmt = min(kMaxMT, (cnt - m0 + 15) >> 4);
+        const u32x4_t* arow[kMaxMT];
+#pragma unroll
+        for (int mt = 0; mt < kMaxMT; ++mt) {
+            int r = m0 + mt * 16 + c16;
+            r = r < cnt ? r : cnt - 1;
+            arow[mt] = (const u32x4_t*)(hbuf + (size_t)(base + r) * I);
+        }
+        f32x4_t acc[kMaxMT];
+#pragma unroll
+        for (int mt = 0; mt < kMaxMT; ++mt) acc[mt] = zero;
+
+        for (int G = 0; G < I / 64; ++G) {
+            const u32x4_t b0 = lane_pairs<B>(dc + (2 * G) * B, g);
+            const u32x4_t b1 = lane_pairs<B>(dc + (2 * G + 1) * B, g);
+            const uint32_t s2 = dsb[G];
+            const float s = half_bits_to_f32(s2 & 0xFFFFu);
+            const float z = __builtin_fmaf(-off, s, half_bits_to_f32(s2 >> 16));
+#pragma unroll
+            for (int mt = 0; mt < kMaxMT; ++mt) {
+                if (mt < nmt) {
+                    const u32x4_t a0 = arow[mt][(2 * G) * 4 + g];
+                    const u32x4_t a1 = arow[mt][(2 * G + 1) * 4 + g];
+                    f32x4_t ty = mfma(a0, b0, zero);
+                    ty = mfma(a1, b1, ty);
+                    f32x4_t tx = mfma(a0, ones, zero);
+                    tx = mfma(a1, ones, tx);
+                    acc[mt] += s * ty + z * tx;
+                }
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < kMaxMT; ++mt) {
+            if (mt < nmt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = m0 + mt * 16 + 4 * g + i;
+                    if (r < cnt) ybuf[(size_t)sorted_pairs[base + r] * H + n] = acc[mt][i];
+                }
+            }
+        }
+    }
+}
+
+// x [T, H] bf16 -> P16 layout: within each 32-chunk, position 2i+h holds input i+16h.
+__global__ __launch_bounds__(256) void permute_x_kernel(const uint16_t* __restrict__ x, int64_t n_dw,
+                                                        uint32_t* __restrict__ xp)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // output dword
+    if (q >= n_dw) return;
+    const int64_t chunk = q >> 4;
+    const int i = (int)(q & 15);
+    const uint16_t* src = x + chunk * 32;
+    xp[q] = (uint32_t)src[i] | ((uint32_t)src[i + 16] << 16);
+}
+
+// out[t, n] = bf16( sum_j w[t, j] * y[t*k + j, n] ), j ascending.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf,
+                                                      const float* __restrict__ w, int T, int k,
+                                                      int H, uint16_t* __restrict__ out)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 4 outputs per thread
+    const int64_t per_t = H / 4;
+    if (q >= (int64_t)T * per_t) return;
+    const int t = (int)(q / per_t);
+    const int n4 = (int)(q - (int64_t)t * per_t) * 4;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int j = 0; j < k; ++j) {
+        const float wj = w[(size_t)t * k + j];
+        const float4 y = *(const float4*)(ybuf + ((size_t)t * k + j) * H + n4);
+        a0 += wj * y.x;
+        a1 += wj * y.y;
+        a2 += wj * y.z;
+        a3 += wj * y.w;
+    }
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
+    o.y = (uint32_t)f32_to_bf16(a2) | ((uint32_t)f32_to_bf16(a3) << 16);
+    *(uint2*)(out + (size_t)t * H + n4) = o;
+}
+
+}  // namespace
+
+hipError_t launch_permute_x(const uint16_t* x, int T, int H, uint16_t* xp, hipStream_t s)
+{
+    const int64_t n_dw = (int64_t)T * H / 2;
+    const int64_t blocks = (n_dw + 255) / 256;
+    hipLaunchKernelGGL(permute_x_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n_dw,
+                       (uint32_t*)xp);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const SortView& sv,
+                              const int32_t* table, const uint8_t* pool, const ClassView& c,
+                              uint16_t* hbuf, uint32_t* err, hipStream_t s)
+{
+    const int max_hit = (int64_t)T * k < E ? T * k : E;
+    dim3 grid(c.I / 64, max_hit);
+#define MOE_MG(BB)                                                                                 \
+    hipLaunchKernelGGL((mfma_gateup_kernel<BB>), grid, dim3(256), 0, s, xp, c.H, c.I, k,           \
+                       sv.offsets, sv.sorted_pairs, sv.pass_table, table, pool, c.n_slots,         \
+                       c.slot_bytes, c.off_gu_codes, c.off_gu_sb, hbuf, err)
+    switch (c.bits_gu) {
+    case 3: MOE_MG(3); break;
+    case 4: MOE_MG(4); break;
+    case 6: MOE_MG(6); break;
+    case 8: MOE_MG(8); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef MOE_MG
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, const int32_t* table,
+                            const uint8_t* pool, const ClassView& c, const uint16_t* hbuf,
+                            float* ybuf, uint32_t* err, hipStream_t s)
+{
+    const int max_hit = (int64_t)T * k < E ? T * k : E;
+    dim3 grid(c.H / 64, max_hit);
+#define MOE_MD(BB)                                                                                 \
+    hipLaunchKernelGGL((mfma_down_kernel<BB>), grid, dim3(256), 0, s, c.H, c.I, sv.offsets,        \
+                       sv.sorted_pairs, sv.pass_table, table, pool, c.n_slots, c.slot_bytes,       \
+                       c.off_d_codes, c.off_d_sb, hbuf, ybuf, err)
+    switch (c.bits_d) {
+    case 3: MOE_MD(3); break;
+    case 4: MOE_MD(4); break;
+    case 6: MOE_MD(6); break;
+    case 8: MOE_MD(8); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef MOE_MD
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* ybuf, const float* topk_w, int T, int k, int H,
+                          uint16_t* out, hipStream_t s)
+{
+    const int64_t n = (int64_t)T * (H / 4);
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ybuf, topk_w, T, k,
+                       H, out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,132 @@
+// moe_dev.h — device helpers shared by the gfx950 kernels of the routed-expert
+// MoE layer: bf16 pair arithmetic, code extraction from the slot format's pack
+// units, wave reductions.
+//
+// Slot format (one expert row; the pages only say "group-wise affine, one
+// contiguous row per expert" — "RFC: stream MoE experts from disk in
+// from_pretrained", How the prototype works): codes are a little-endian bit
+// stream in pack units of 32 values held in B uint32 words; scale and bias are
+// one fp16 pair per group of 64 inputs.
+//
+// Pairing used by every kernel ("P16"): the 32 codes of a unit are consumed as
+// 16 pairs (c_i, c_{i+16}), i = 0..15.  A pair is packed into one register as
+// two bf16 values 128 + c (bf16 bits 0x4300 | c, exact for c < 128), or for
+// 8-bit codes as two bf16 values c (exact for c < 256).  Activations are laid
+// out to match: within every 32-wide chunk, position 2i+h holds input i+16h.
+// A bf16 dot2 then accumulates sum x*(off + c) exactly per product, and the
+// affine map is applied per group afterwards:
+//     sum_g s_g * sum x*c + z_g * sum x  =  s_g * acc + (z_g - off*s_g) * X_g.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+#define MOE_MAGIC_PAIR 0x43004300u  // two bf16 128.0
+#define MOE_ONES_PAIR 0x3F803F80u   // two bf16 1.0
+
+namespace moe {
+
+template <int B>
+struct Code {
+    static constexpr uint32_t mask = (1u << B) - 1u;
+    static constexpr uint32_t mask2 = mask * 0x10001u;
+    static constexpr float offset = (B == 8) ? 0.0f : 128.0f;  // bf16 value of code 0
+    static constexpr int per_t = 16 / B;                          // pairs from one window pair
+};
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    __bf16 b = (__bf16)f;  // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ float half_bits_to_f32(uint32_t h16)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+
+// 32-bit window of a unit's bit stream starting at compile-time bit `o`.
+template <int B>
+__device__ __forceinline__ uint32_t win(const uint32_t (&w)[B], int o)
+{
+    const int wi = o >> 5, sh = o & 31;
+    if (sh == 0) return w[wi];
+    if (wi + 1 >= B) return w[wi] >> sh;
+    return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh);
+}
+
+// Pair i of a unit with its low code at bit 0 and high code at bit 16
+// (other bits hold neighbouring codes; callers mask).
+template <int B>
+__device__ __forceinline__ uint32_t pair_window(const uint32_t (&w)[B], int i)
+{
+    const uint32_t lo = win<B>(w, B * i);
+    const uint32_t hi = win<B>(w, B * i + 16 * B - 16);
+    return (lo & 0xFFFFu) | (hi & 0xFFFF0000u);
+}
+
+// Float of byte N of t (the compiler emits v_cvt_f32_ubyteN).
+template <int N>
+__device__ __forceinline__ float ubyte_f32(uint32_t t)
+{
+    return (float)((t >> (8 * N)) & 0xFFu);
+}
+
+// Two bf16 values of the codes held at bits 0 and 16 of t (8-bit codes).
+__device__ __forceinline__ uint32_t bytes02_to_bf16pair(uint32_t t)
+{
+    const float f0 = ubyte_f32<0>(t);
+    const float f1 = ubyte_f32<2>(t);
+    return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+}
+
+// All 16 P16 pairs of one unit, as bf16 pairs of (offset + code).
+template <int B>
+__device__ __forceinline__ void unit_pairs(const uint32_t (&w)[B], uint32_t (&pr)[16])
+{
+    constexpr int S = Code<B>::per_t;
+#pragma unroll
+    for (int i = 0; i < 16; i += S) {
+        const uint32_t t = pair_window<B>(w, i);
+#pragma unroll
+        for (int m = 0; m < S; ++m) {
+            if (i + m < 16) {
+                const uint32_t tm = t >> (B * m);
+                if constexpr (B == 8)
+                    pr[i + m] = bytes02_to_bf16pair(tm);
+                else
+                    pr[i + m] = (tm & Code<B>::mask2) | MOE_MAGIC_PAIR;
+            }
+        }
+    }
+}
+
+// Sum over lanes within aligned segments of `width` lanes (power of two <= 64);
+// every lane of a segment gets the segment's sum.  Fixed butterfly order.
+__device__ __forceinline__ float seg_sum(float v, int width)
+{
+    for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    return g / (1.0f + __expf(-g)) * u;
+}
+
+// Position of input c (0..31) of a chunk in the P16 activation layout.
+__device__ __forceinline__ int p16_pos(int c) { return ((c & 15) << 1) | (c >> 4); }
+
+}  // namespace moe

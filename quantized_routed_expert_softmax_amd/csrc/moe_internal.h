@@ -1,0 +1,55 @@
+// moe_internal.h — launchers shared between the C-ABI layer and the kernel
+// translation units.  Host code only; every launcher enqueues on `s` and
+// returns hipGetLastError() of its launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Record `msg` as this thread's moe_last_error() text; returns `code`.
+int set_error(int code, const char* msg);
+
+struct ClassView {
+    int H, I, bits_gu, bits_d;
+    int64_t n_slots, slot_bytes;
+    int64_t off_gu_codes, off_gu_sb, off_d_codes, off_d_sb;
+};
+
+// Sorted-by-expert view of the routed pairs (all device pointers).
+struct SortView {
+    const int32_t* offsets;       // [E+1]
+    const int32_t* sorted_pairs;  // [n]
+    const int32_t* pass_table;    // [2 + E + n_pass_max + 1]
+};
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int mode, float L,
+                        const int32_t* table, int32_t* ids, float* w, uint32_t* err, hipStream_t s);
+
+size_t sort_ws_bytes(int T, int k, int E);
+hipError_t launch_sort(const int32_t* ids, int T, int k, int E, int P, int32_t* offsets,
+                       int32_t* sorted_pairs, int32_t* pass_table, void* ws, uint32_t* err,
+                       hipStream_t s);
+
+// Decode path: dequant-GEMV gate/up + SwiGLU, then down + weighted combine.
+hipError_t launch_gemv_gateup(const uint16_t* x, int T, int k, int E, const SortView& sv,
+                              const int32_t* table, const uint8_t* pool, const ClassView& c,
+                              uint16_t* hbuf, uint32_t* err, hipStream_t s);
+hipError_t launch_gemv_down(int T, int k, int E, const SortView& sv, const float* topk_w,
+                            const int32_t* table, const uint8_t* pool, const ClassView& c,
+                            const uint16_t* hbuf, uint16_t* out, uint32_t* err, hipStream_t s);
+bool gemv_supported(int T, int k, const ClassView& c);
+
+// Prefill path: P16-permuted x, MFMA gate/up + SwiGLU, MFMA down, combine.
+hipError_t launch_permute_x(const uint16_t* x, int T, int H, uint16_t* xp, hipStream_t s);
+hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const SortView& sv,
+                              const int32_t* table, const uint8_t* pool, const ClassView& c,
+                              uint16_t* hbuf, uint32_t* err, hipStream_t s);
+hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, const int32_t* table,
+                            const uint8_t* pool, const ClassView& c, const uint16_t* hbuf,
+                            float* ybuf, uint32_t* err, hipStream_t s);
+hipError_t launch_combine(const float* ybuf, const float* topk_w, int T, int k, int H,
+                          uint16_t* out, hipStream_t s);
+
+}  // namespace moe

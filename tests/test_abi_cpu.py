@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every function include/moe.h declares, and
+rejects bad arguments on the host (no GPU call is made by any check here)."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+from quantized_routed_expert_softmax_amd import binding as B
+from quantized_routed_expert_softmax_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_library_exports_every_header_function():
+    names = B.header_functions()
+    assert len(names) >= 20
+    L = ctypes.CDLL(B.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def _layouts():
+    rows = []
+    with open(os.path.join(GOLDEN, "layout.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            a, b = line.split("|")
+            rows.append(([int(v) for v in a.split()], [int(v) for v in b.split()]))
+    return rows
+
+
+@pytest.mark.parametrize("case", _layouts())
+def test_size_class_init_matches_golden_layout(case):
+    (H, I, bg, bd), offs = case
+    d = B.moe_size_class_init(H, I, bg, bd, 7)
+    assert [d.off_gu_codes, d.off_gu_sb, d.off_d_codes, d.off_d_sb, d.slot_bytes] == offs
+    assert (d.H, d.I, d.bits_gu, d.bits_d, d.group, d.align, d.n_slots) == (H, I, bg, bd, 64, 256, 7)
+
+
+@pytest.mark.parametrize("args", [(100, 64, 4, 4), (64, 96, 4, 4), (64, 64, 5, 4), (64, 64, 4, 2),
+                                  (0, 64, 4, 4), (64, 64, 4, 16)])
+def test_size_class_init_rejects(args):
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_size_class_init(*args, 4)
+    assert ei.value.code == B.MOE_E_INVALID
+    assert B.moe_last_error()
+
+
+def test_size_class_rejects_group_and_align():
+    for group, align in ((32, 256), (64, 128)):
+        with pytest.raises(B.MoeError):
+            B.moe_size_class_init(64, 64, 4, 4, 1, group=group, align=align)
+
+
+def test_route_argument_checks_on_host():
+    L = B.lib()
+    P = ctypes.c_void_p(0x1000)  # never dereferenced: the checks fail first
+    assert L.moe_route_topk(P, 4, 0, 1, 0, 0.0, None, P, P, None, None) == B.MOE_E_INVALID
+    assert L.moe_route_topk(P, 4, 2000, 1, 0, 0.0, None, P, P, None, None) == B.MOE_E_INVALID
+    assert L.moe_route_topk(P, 4, 8, 9, 0, 0.0, None, P, P, None, None) == B.MOE_E_INVALID
+    assert L.moe_route_topk(P, 4, 64, 33, 0, 0.0, None, P, P, None, None) == B.MOE_E_INVALID
+    assert L.moe_route_topk(P, 4, 8, 2, 7, 0.0, None, P, P, None, None) == B.MOE_E_INVALID
+    assert L.moe_route_topk(P, 4, 8, 2, 1, 0.1, None, P, P, None, None) == B.MOE_E_INVALID
+    assert L.moe_route_topk(P, 4, 8, 2, 1, -0.1, P, P, P, None, None) == B.MOE_E_INVALID
+    assert L.moe_route_topk(P, 4, 8, 2, 1, float("nan"), P, P, P, None, None) == B.MOE_E_INVALID
+    assert L.moe_route_topk(P, -1, 8, 2, 0, 0.0, None, P, P, None, None) == B.MOE_E_INVALID
+    assert "k must be" in B.moe_last_error() or "T < 0" in B.moe_last_error()
+    # T == 0 is a no-op that succeeds without touching the buffers
+    assert L.moe_route_topk(None, 0, 8, 2, 0, 0.0, None, None, None, None, None) == B.MOE_OK
+
+
+def test_sort_and_forward_argument_checks_on_host():
+    L = B.lib()
+    P = ctypes.c_void_p(0x1000)
+    assert L.moe_sort_by_expert(P, 4, 2, 0, 64, P, P, P, None, 0, None, None) == B.MOE_E_INVALID
+    assert L.moe_sort_by_expert(P, 4, 2, 8, 0, P, P, P, None, 0, None, None) == B.MOE_E_INVALID
+    # multi-tile sort needs workspace
+    need = B.moe_sort_workspace_size(1024, 10, 512)
+    assert need > 0
+    assert L.moe_sort_by_expert(P, 1024, 10, 512, 64, P, P, P, None, 0, None, None) == B.MOE_E_WORKSPACE
+    d = B.moe_size_class_init(256, 128, 4, 4, 8)
+    ws = B.moe_forward_workspace_size(16, 2, 8, d)
+    assert ws > 0 and ws % 256 == 0
+    A = ctypes.c_void_p(0x100000)  # 256-aligned fake address, never dereferenced
+    fwd = L.moe_experts_forward_ex
+    assert fwd(A, 16, A, A, 2, 8, A, A, ctypes.byref(d), A, A, ws - 1, None, 0, None) == B.MOE_E_WORKSPACE
+    assert fwd(A, 16, A, A, 9, 8, A, A, ctypes.byref(d), A, A, ws, None, 0, None) == B.MOE_E_INVALID
+    assert fwd(A, 16, A, A, 2, 8, A, A, ctypes.byref(d), A, A, ws, None, 9, None) == B.MOE_E_INVALID
+    bad = B.SizeClassDesc.from_buffer_copy(d)
+    bad.slot_bytes += 256
+    assert fwd(A, 16, A, A, 2, 8, A, A, ctypes.byref(bad), A, A, ws, None, 0, None) == B.MOE_E_INVALID
+    unaligned = ctypes.c_void_p(0x100008)
+    assert fwd(unaligned, 16, A, A, 2, 8, A, A, ctypes.byref(d), A, A, ws, None, 0, None) == B.MOE_E_INVALID
+    big = B.moe_size_class_init(4096, 1024, 8, 8, 1)
+    assert L.moe_experts_forward_ex(A, 100, A, A, 8, 256, A, A, ctypes.byref(big), A, A,
+                                    B.moe_forward_workspace_size(100, 8, 256, big), None,
+                                    B.MOE_PATH_GEMV, None) == B.MOE_E_UNSUPPORTED
+    assert fwd(None, 0, None, None, 2, 8, None, None, ctypes.byref(d), None, None, 0, None, 0, None) == B.MOE_OK
+
+
+def test_install_argument_checks_on_host():
+    L = B.lib()
+    d = B.moe_size_class_init(256, 128, 4, 4, 8)
+    A = ctypes.c_void_p(0x100000)
+    assert L.moe_cache_install(A, ctypes.byref(d), 8, A, 0, None, None) == B.MOE_E_INVALID
+    assert L.moe_cache_install(A, ctypes.byref(d), -1, A, 0, None, None) == B.MOE_E_INVALID
+    assert L.moe_cache_install(A, ctypes.byref(d), 0, A, 5, None, None) == B.MOE_E_INVALID
+    assert L.moe_cache_install(None, ctypes.byref(d), 0, A, 0, None, None) == B.MOE_E_INVALID
+
+
+def test_workspace_sizes_cover_prefill():
+    d = B.moe_size_class_init(2048, 512, 3, 3, 512)
+    ws = B.moe_forward_workspace_size(1024, 10, 512, d)
+    n = 1024 * 10
+    assert ws >= n * 2048 * 4 + n * 512 * 2 + 1024 * 2048 * 2
+    assert B.moe_pass_table_size(512, 64) == 2 + 512 + 8 + 1

@@ -1,0 +1,162 @@
+"""Host cache: size classes, one LRU per class, reservation of in-flight fills,
+pins.  Pure host code (fills are completed with a NULL event, so no GPU call).
+
+Sources: "RFC: stream MoE experts from disk in from_pretrained", How the
+prototype works (preallocated pool of slots, LRU, per-layer expert -> slot
+table); "POC: Experts offload", host-tier commit (rows stay reserved until the
+copy that reads them has run); "moe: expert slots in size classes", PR
+description and the ExpertCache constructor (own slots and LRU per class;
+empty slots at the LRU's back are taken first; budget never moves between
+classes).
+"""
+import numpy as np
+import pytest
+
+from quantized_routed_expert_softmax_amd import binding as B
+
+
+def make(n_a=4, n_b=2, layers=(0, 0, 1), E=8):
+    a = B.moe_size_class_init(256, 128, 4, 4, n_a)
+    b = B.moe_size_class_init(256, 128, 4, 6, n_b)
+    return B.moe_cache_create([a, b], list(layers), E)
+
+
+def fill(c, layer, expert):
+    rc, slot, nf = B.moe_cache_acquire(c, layer, expert)
+    assert rc == B.MOE_OK
+    if nf:
+        B.moe_cache_fill_done(c, layer, expert, None)
+    return slot, nf
+
+
+def test_empty_slots_taken_in_order_then_lru():
+    c = make()
+    try:
+        slots = [fill(c, 0, e)[0] for e in range(4)]
+        # slots are appended to the LRU in creation order and victims come off
+        # the back, so the empty slots are taken first, last-created first
+        assert slots == [3, 2, 1, 0]
+        assert fill(c, 0, 0) == (3, 0)           # hit, moves expert 0 to the front
+        s, nf = fill(c, 1, 5)                    # layer 1 shares class A: evicts LRU (expert 1)
+        assert nf == 1 and s == 2
+        assert B.moe_cache_lookup(c, 0, 1) == -1
+        assert B.moe_cache_lookup(c, 1, 5) == 2
+        h, m, ev = B.moe_cache_stats(c)
+        assert (h, m, ev) == (1, 5, 1)
+        t0 = B.moe_cache_table(c, 0, 8)
+        assert t0.tolist() == [3, -1, 1, 0, -1, -1, -1, -1]
+    finally:
+        B.moe_cache_destroy(c)
+
+
+def test_classes_never_evict_each_other():
+    c = make(n_a=2, n_b=2, layers=(0, 1), E=8)
+    try:
+        assert B.moe_cache_class_of(c, 0) == 0 and B.moe_cache_class_of(c, 1) == 1
+        fill(c, 1, 0)
+        fill(c, 1, 1)
+        for e in range(8):                      # churn class A hard
+            fill(c, 0, e)
+        assert B.moe_cache_table(c, 1, 8)[:2].tolist() == [1, 0]
+        fill(c, 1, 2)                            # class B evicts only within itself
+        assert B.moe_cache_table(c, 1, 8)[:3].tolist() == [-1, 0, 1]
+    finally:
+        B.moe_cache_destroy(c)
+
+
+def test_in_flight_slot_is_reserved():
+    c = make(n_a=2, layers=(0,), E=8)
+    try:
+        rc, s0, nf = B.moe_cache_acquire(c, 0, 0)
+        assert rc == B.MOE_OK and nf == 1
+        # a second acquire of an entry still in flight reports BUSY, same slot
+        rc, s, nf = B.moe_cache_acquire(c, 0, 0)
+        assert rc == B.MOE_E_BUSY and s == s0 and nf == 0
+        rc, s1, nf = B.moe_cache_acquire(c, 0, 1)
+        assert rc == B.MOE_OK and nf == 1
+        # both slots in flight: no victim
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_cache_acquire(c, 0, 2)
+        assert ei.value.code == B.MOE_E_NO_SLOT
+        assert B.moe_cache_poll(c) == 2
+        B.moe_cache_fill_done(c, 0, 0, None)
+        assert B.moe_cache_poll(c) == 1
+        rc, s2, nf = B.moe_cache_acquire(c, 0, 2)   # only the completed slot can go
+        assert rc == B.MOE_OK and s2 == s0 and nf == 1
+        assert B.moe_cache_lookup(c, 0, 0) == -1
+    finally:
+        B.moe_cache_destroy(c)
+
+
+def test_pinned_slot_is_not_evicted():
+    c = make(n_a=2, layers=(0,), E=8)
+    try:
+        s0, _ = fill(c, 0, 0)
+        s1, _ = fill(c, 0, 1)
+        B.moe_cache_pin(c, 0, 0)
+        fill(c, 0, 0)                      # touch 0: 1 is LRU anyway
+        B.moe_cache_pin(c, 0, 1)
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_cache_acquire(c, 0, 2)
+        assert ei.value.code == B.MOE_E_NO_SLOT
+        B.moe_cache_unpin(c, 0, 1)
+        s, nf = fill(c, 0, 2)
+        assert s == s1 and nf == 1
+        with pytest.raises(B.MoeError):
+            B.moe_cache_unpin(c, 0, 1)     # evicted: not resident any more
+        B.moe_cache_unpin(c, 0, 0)
+        with pytest.raises(B.MoeError):
+            B.moe_cache_unpin(c, 0, 0)     # not pinned
+    finally:
+        B.moe_cache_destroy(c)
+
+
+def test_lru_order_matches_a_reference_model():
+    """Random acquire sequence against a plain Python LRU of the same budget."""
+    rng = np.random.default_rng(7)
+    n, E, L = 5, 12, 2
+    c = make(n_a=n, layers=(0,) * L, E=E)
+    try:
+        order = []            # most recent first: (layer, expert)
+        owner = {}            # (layer, expert) -> slot
+        free = list(range(n))          # taken from the end: last-created first
+        for _ in range(400):
+            key = (int(rng.integers(L)), int(rng.integers(E)))
+            slot, nf = fill(c, *key)
+            if key in owner:
+                assert nf == 0 and slot == owner[key]
+                order.remove(key)
+            else:
+                assert nf == 1
+                if free:
+                    exp = free.pop()
+                else:
+                    victim = order.pop()
+                    exp = owner.pop(victim)
+                assert slot == exp
+                owner[key] = slot
+            order.insert(0, key)
+        for l in range(L):
+            t = B.moe_cache_table(c, l, E)
+            for e in range(E):
+                assert t[e] == owner.get((l, e), -1)
+    finally:
+        B.moe_cache_destroy(c)
+
+
+def test_bad_arguments():
+    a = B.moe_size_class_init(256, 128, 4, 4, 2)
+    with pytest.raises(B.MoeError):
+        B.moe_cache_create([a], [1], 8)
+    c = B.moe_cache_create([a], [0], 8)
+    try:
+        with pytest.raises(B.MoeError):
+            B.moe_cache_acquire(c, 1, 0)
+        with pytest.raises(B.MoeError):
+            B.moe_cache_acquire(c, 0, 8)
+        with pytest.raises(B.MoeError):
+            B.moe_cache_fill_done(c, 0, 3, None)
+        with pytest.raises(B.MoeError):
+            B.moe_cache_pin(c, 0, 3)
+    finally:
+        B.moe_cache_destroy(c)
