@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+Workload (the headline): decode of a 48-layer MoE with 512 experts per layer,
+hidden 2048, expert intermediate 512, top-10, 3-bit group-64 experts, batch 1,
+a 2048-slot pool per layer with a random expert -> slot table, router logits
+N(0,1) plus a per-expert Zipf(1.1) bias.  One step = one decode token through
+all 48 layers: per layer route (softmax, top-k, renormalise) and the experts
+forward (sort by expert, slot resolve, gate/up, SwiGLU, down, weighted
+combine); each layer's output is the next layer's input.  The step is captured
+once in a HIP graph and replayed.
+
+Also reported: 4K-token prefill (4 chunks of 1024 tokens through the same 48
+layers, every expert resident, MFMA path) and the CPU oracle on the host cores.
+
+Prints ONE JSON line.  Only one GPU is supported (--gpus 1).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--prefill-reps", type=int, default=3)
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-layers", type=int, default=12, help="oracle sample: decode layers")
+    p.add_argument("--eager", action="store_true", help="no HIP graph (launch-bound)")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class DecodeModel:
+    """48 layers of device state for the decode / prefill workloads."""
+
+    def __init__(self, torch, B, synth, wl):
+        self.torch, self.B, self.synth, self.wl = torch, B, synth, wl
+        dev = torch.device("cuda")
+        self.lay = synth.Layout(wl.H, wl.I, wl.bits_gu, wl.bits_d)
+        self.desc = B.moe_size_class_init(wl.H, wl.I, wl.bits_gu, wl.bits_d, wl.slots_per_layer)
+        self.tables_np, self.pools, self.tables = [], [], []
+        for l in range(wl.layers):
+            t = synth.slot_table(synth.rng_for(wl.seed, 4, l), wl.E, wl.slots_per_layer)
+            pool = torch.empty((wl.slots_per_layer, self.lay.slot_bytes), dtype=torch.uint8, device=dev)
+            synth.fill_pool_device(pool, self.lay, t, wl.seed, l)
+            self.tables_np.append(t)
+            self.tables.append(torch.from_numpy(t).to(dev))
+            self.pools.append(pool.view(-1))
+        torch.cuda.synchronize()
+
+
+def decode_inputs(torch, synth, wl):
+    lg = np.stack([synth.gen_logits(synth.rng_for(wl.seed, 3, l), 1, wl.E,
+                                    synth.zipf_bias(synth.rng_for(wl.seed, 2, l), wl.E, wl.zipf_s))
+                   for l in range(wl.layers)])
+    x0 = synth.gen_x(synth.rng_for(wl.seed, 1), 1, wl.H)
+    return lg, x0
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the routed-expert layer runs on a single "
+              f"device); --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import quantized_routed_expert_softmax_amd as moe
+    from quantized_routed_expert_softmax_amd import binding as B
+    from quantized_routed_expert_softmax_amd import synth
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    B.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda")
+    wl = synth.WORKLOADS["decode"]
+    t_setup = time.time()
+    model = DecodeModel(torch, B, synth, wl)
+    lg_np, x0_np = decode_inputs(torch, synth, wl)
+    logits = torch.from_numpy(lg_np).to(dev)                      # [L, 1, E]
+    x0 = torch.from_numpy(x0_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    xbuf = [torch.empty((1, wl.H), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    ids = torch.empty((wl.layers, 1, wl.k), dtype=torch.int32, device=dev)
+    w = torch.empty((wl.layers, 1, wl.k), dtype=torch.float32, device=dev)
+    ws = torch.zeros(B.moe_forward_workspace_size(1, wl.k, wl.E, model.desc), dtype=torch.uint8, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    log(f"setup {time.time() - t_setup:.1f}s")
+
+    def step(timing=None):
+        # per layer: router + experts (one fused launch at decode batch sizes)
+        x = x0
+        for l in range(wl.layers):
+            y = xbuf[l & 1]
+            if timing is not None:
+                timing[0][l].record()
+            B.moe_layer_forward(logits[l], x, model.tables[l], model.pools[l], model.desc, wl.k,
+                                topk_ids=ids[l], topk_w=w[l], out=y, ws=ws, err_word=err)
+            if timing is not None:
+                timing[1][l].record()
+            x = y
+        return x
+
+    # warm up eagerly (also required before graph capture)
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, f"device error word {int(err.item()):#x}"
+
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+
+    def run_step():
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        run_step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    assert int(err.item()) == 0, f"device error word {int(err.item()):#x}"
+    out_final = xbuf[(wl.layers - 1) & 1].float()
+    assert bool(torch.isfinite(out_final).all())
+
+    # --- per-launch duration of the experts forward, live, with HIP events ---
+    # A sleep kernel first lets the host queue all launches, so each event pair
+    # brackets GPU work only (no host launch gaps inside it).
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(wl.layers)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(wl.layers)]
+    fwd_ms = []
+    for _ in range(3):
+        torch.cuda._sleep(20_000_000)
+        step(timing=(starts, ends))
+        torch.cuda.synchronize()
+        fwd_ms += [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    fwd_ms_avg = float(np.mean(fwd_ms))
+    ids_np = ids.cpu().numpy()
+    distinct = [len(set(ids_np[l].reshape(-1).tolist())) for l in range(wl.layers)]
+    # algorithmic bytes of one launch: the distinct routed experts' rows, the
+    # router logits, x and out
+    bytes_per_launch = float(np.mean(distinct)) * model.lay.slot_bytes + wl.E * 4 + 2 * wl.H * 2
+    achieved_gbs = bytes_per_launch / (fwd_ms_avg * 1e-3) / 1e9
+    step_bytes = sum(distinct) * model.lay.slot_bytes
+    decode_gbs_step = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    result = {
+        "metric": "decode tok/s + HBM GB/s on quant expert bytes; 4K-prefill tok/s (MFMA util)",
+        "value": round(1000.0 / ms_per_step, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode: 48 layers x (hidden 2048, 512 experts, intermediate 512, "
+                               "top-10), 3-bit g64 experts, batch 1, 2048-slot pool per layer, "
+                               "Zipf(1.1)-biased router logits",
+                   "global_batch": 1, "layers": wl.layers, "graph": graph is not None,
+                   "wall_s_timed": round(wall, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_layer_kernel<3,3,1,1> (moe_layer_forward: route + sort + "
+                               "gate/up + SwiGLU + down + combine, one launch per layer)",
+                     "avg_launch_us": round(fwd_ms_avg * 1000.0, 3),
+                     "bytes_per_launch": int(bytes_per_launch)},
+        "decode_expert_bytes_per_token": int(step_bytes),
+        "decode_gbs_whole_step": round(decode_gbs_step, 1),
+    }
+
+    # ------------------------------- prefill ------------------------------- #
+    if not args.no_prefill:
+        pw = synth.WORKLOADS["prefill"]
+        T, chunks = pw.T, pw.chunks
+        plg = torch.empty((chunks, wl.layers, T, wl.E), dtype=torch.float32, device=dev)
+        for c in range(chunks):
+            for l in range(wl.layers):
+                plg[c, l] = torch.from_numpy(synth.gen_logits(synth.rng_for(pw.seed, 3, c, l), T, wl.E)).to(dev)
+        px = [torch.from_numpy(synth.gen_x(synth.rng_for(pw.seed, 1, c), T, wl.H).view(np.int16)).to(dev)
+              .view(torch.bfloat16) for c in range(chunks)]
+        pbuf = [torch.empty((T, wl.H), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        pids = torch.empty((T, wl.k), dtype=torch.int32, device=dev)
+        pw_ = torch.empty((T, wl.k), dtype=torch.float32, device=dev)
+        pws = torch.zeros(B.moe_forward_workspace_size(T, wl.k, wl.E, model.desc), dtype=torch.uint8,
+                          device=dev)
+        pstart = [torch.cuda.Event(enable_timing=True) for _ in range(wl.layers)]
+        pend = [torch.cuda.Event(enable_timing=True) for _ in range(wl.layers)]
+
+        def prefill(timing=False):
+            for c in range(chunks):
+                x = px[c]
+                for l in range(wl.layers):
+                    y = pbuf[l & 1]
+                    if timing and c == 0:
+                        pstart[l].record()
+                    B.moe_layer_forward(plg[c, l], x, model.tables[l], model.pools[l], model.desc, wl.k,
+                                        topk_ids=pids, topk_w=pw_, out=y, ws=pws, err_word=err)
+                    if timing and c == 0:
+                        pend[l].record()
+                    x = y
+
+        prefill()
+        torch.cuda.synchronize()
+        pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        pe0.record()
+        for _ in range(args.prefill_reps):
+            prefill()
+        pe1.record()
+        torch.cuda.synchronize()
+        p_ms = pe0.elapsed_time(pe1) / args.prefill_reps
+        torch.cuda._sleep(20_000_000)
+        prefill(timing=True)
+        torch.cuda.synchronize()
+        lc_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(pstart, pend)]))
+        assert int(err.item()) == 0, f"device error word {int(err.item()):#x}"
+        pairs = T * wl.k
+        flops = 2.0 * pairs * 3 * wl.H * wl.I
+        lc_bytes = wl.E * model.lay.slot_bytes
+        result["prefill"] = {
+            "workload": "4K prompt = 4 chunks x 1024 tokens, 48 layers, all 512 experts resident",
+            "tok_s": round(T * chunks / (p_ms * 1e-3), 1),
+            "ms_per_prompt": round(p_ms, 3),
+            "layer_chunk_us": round(lc_ms * 1000.0, 2),
+            "useful_tflops": round(flops / (lc_ms * 1e-3) / 1e12, 2),
+            "mfma_frac_of_bf16_peak": round(flops / (lc_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "hbm_gbs": round(lc_bytes / (lc_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(lc_bytes / (lc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+
+    # ----------------------------- CPU oracle ------------------------------ #
+    if not args.no_cpu:
+        import oracle
+        nl = min(args.cpu_layers, wl.layers)
+        x = x0_np.copy()
+        t_cpu = 0.0
+        for l in range(nl):
+            # the routed experts' rows, copied once from the device (not timed)
+            ids_l, w_l = oracle.route(lg_np[l], wl.k)
+            used = sorted(set(ids_l.reshape(-1).tolist()))
+            idx = torch.as_tensor([int(model.tables_np[l][e]) for e in used], device=dev)
+            rows = model.pools[l].view(wl.slots_per_layer, -1).index_select(0, idx).cpu().numpy()
+            table = np.full(wl.E, -1, np.int32)
+            table[used] = np.arange(len(used), dtype=np.int32)
+            t0 = time.perf_counter()
+            ids_l, w_l = oracle.route(lg_np[l], wl.k)
+            out = oracle.layer(x, ids_l, w_l, table, rows, wl.H, wl.I, wl.bits_gu, wl.bits_d, wl.E,
+                               threads=1)
+            t_cpu += time.perf_counter() - t0
+            x = synth.f32_to_bf16_bits(out.astype(np.float32))
+        per_layer = t_cpu / nl
+        result["cpu_baseline"] = {
+            "value": round(1.0 / (per_layer * wl.layers), 5),
+            "unit": "tok/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"{nl} of 48 decode layers of one token (route + fp64 layer), scaled to 48 "
+                      f"layers; the oracle parallelises over tokens only, so batch 1 uses one core",
+            "seconds": round(t_cpu, 2),
+            "host_cores_available": len(os.sched_getaffinity(0)),
+        }
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -107,6 +107,7 @@ extern "C" {
 #define MOE_ERRW_BAD_SLOT      0x2u /* slot_table[e] >= n_slots                 */
 #define MOE_ERRW_NONFINITE     0x4u /* a router logit is NaN or infinite        */
 #define MOE_ERRW_BAD_ID        0x8u /* a top-k id outside [0, E)                */
+#define MOE_ERRW_TIMEOUT      0x10u /* the fused decode kernel's grid barrier gave up */
 
 /* ---- routing modes ------------------------------------------------------- */
 #define MOE_ROUTE_PLAIN  0
@@ -116,6 +117,14 @@ extern "C" {
 #define MOE_PATH_AUTO  0 /* GEMV for few pairs per expert, MFMA otherwise       */
 #define MOE_PATH_GEMV  1 /* dequant-GEMV kernels (decode)                       */
 #define MOE_PATH_MFMA  2 /* dequant + bf16 MFMA grouped GEMM (prefill)          */
+#define MOE_PATH_GEMV3 3 /* GEMV as three launches (sort, gate/up, down)        */
+
+/* ---- workspace --------------------------------------------------------------
+ * The first MOE_WS_BARRIER_BYTES of a forward workspace hold the grid barrier of
+ * the fused decode kernel (a generation word and one arrival flag per
+ * workgroup).  They must be zero before the first call on that workspace; every
+ * call leaves them consistent for the next one.                               */
+#define MOE_WS_BARRIER_BYTES 8192
 
 /* ---- cache install sources ----------------------------------------------- */
 #define MOE_SRC_HOST    0 /* pinned host memory (hipHostMalloc)                 */
@@ -203,9 +212,16 @@ int    moe_pass_table_size(int E, int pass_experts);
  *   slot_table device int32 [E]: slot of each expert, -1 if not resident.
  *   slot_pool  device bytes [d->n_slots * d->slot_bytes].
  *   out        device bf16 [T, H] (overwritten; round to nearest even).
- *   ws         device scratch of moe_forward_workspace_size(...) bytes.
- *   err_word   MOE_ERRW_NOT_RESIDENT / MOE_ERRW_BAD_SLOT / MOE_ERRW_BAD_ID.
- * `path` selects the kernels (MOE_PATH_*); moe_experts_forward uses AUTO.
+ *   ws         device scratch of moe_forward_workspace_size(...) bytes, 256-byte
+ *              aligned; its first MOE_WS_BARRIER_BYTES must be zero before the
+ *              first call that uses it (the generation word at bytes 0..3 then
+ *              counts the fused calls).  Calls that share one ws must not overlap
+ *              in time (same stream, or ordered by events).
+ *   err_word   MOE_ERRW_NOT_RESIDENT / MOE_ERRW_BAD_SLOT / MOE_ERRW_BAD_ID /
+ *              MOE_ERRW_TIMEOUT.
+ * `path` selects the kernels (MOE_PATH_*); moe_experts_forward uses AUTO: the
+ * fused one-launch decode kernel when T*k <= 64 and the shape has a compiled
+ * variant, the GEMV kernels for other small batches, MFMA otherwise.
  * Sources: [HF-PR] PR description (experts run through gather_qmm on the cache);
  * [RFC] "How the prototype works" (Cache, Prefill and Quantized experts bullets).
  */
@@ -218,6 +234,24 @@ int moe_experts_forward_ex(const void* x, int T, const int32_t* topk_ids, const 
                            const moe_size_class_desc* d, void* out, void* ws, size_t ws_bytes,
                            uint32_t* err_word, int path, hipStream_t stream);
 size_t moe_forward_workspace_size(int T, int k, int E, const moe_size_class_desc* d);
+
+/*
+ * Router and routed experts of one layer: moe_route_topk followed by
+ * moe_experts_forward, with the same arguments and the same results (ids and
+ * weights bit-identical, outputs identical to MOE_PATH_GEMV).  For decode-sized
+ * batches (T*k <= 64) both run in ONE launch: every workgroup routes the tokens
+ * itself, so the layer needs no host round trip and no second kernel; the
+ * routing is also written to topk_ids / topk_w.  Larger batches fall back to the
+ * two calls.  Same workspace rules as moe_experts_forward.
+ * Sources: "POC: Experts offload", commit messages (queued GPU work must not idle
+ * between a layer's sub-steps); "RFC: stream MoE experts from disk in
+ * from_pretrained", How the prototype works (with every expert resident, layers
+ * never synchronise with the host).
+ */
+int moe_layer_forward(const float* logits, int T, int E, int k, int mode, float L, const void* x,
+                      const int32_t* slot_table, const void* slot_pool, const moe_size_class_desc* d,
+                      int32_t* topk_ids, float* topk_w, void* out, void* ws, size_t ws_bytes,
+                      uint32_t* err_word, hipStream_t stream);
 
 /*
  * Enqueue the copy of one expert row (d->slot_bytes bytes at `src`) into slot

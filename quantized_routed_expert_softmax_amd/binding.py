@@ -30,12 +30,14 @@ MOE_ERRW_NOT_RESIDENT = 0x1
 MOE_ERRW_BAD_SLOT = 0x2
 MOE_ERRW_NONFINITE = 0x4
 MOE_ERRW_BAD_ID = 0x8
+MOE_ERRW_TIMEOUT = 0x10
 
 MOE_ROUTE_PLAIN = 0
 MOE_ROUTE_SUBST = 1
 MOE_PATH_AUTO = 0
 MOE_PATH_GEMV = 1
 MOE_PATH_MFMA = 2
+MOE_PATH_GEMV3 = 3
 MOE_SRC_HOST = 0
 MOE_SRC_DEVICE = 1
 
@@ -64,6 +66,10 @@ def lib() -> ctypes.CDLL:
     global _lib
     with _lock:
         if _lib is None:
+            try:  # one HIP runtime per process: let torch load its own first
+                import torch  # noqa: F401
+            except ImportError:
+                pass
             if not os.path.exists(LIB_PATH):
                 raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                    "`python -m quantized_routed_expert_softmax_amd.build`")
@@ -80,6 +86,7 @@ def lib() -> ctypes.CDLL:
                 "moe_experts_forward": (I32, [P, I32, P, P, I32, I32, P, P, D, P, P, SZ, P, P]),
                 "moe_experts_forward_ex": (I32, [P, I32, P, P, I32, I32, P, P, D, P, P, SZ, P, I32, P]),
                 "moe_forward_workspace_size": (SZ, [I32, I32, I32, D]),
+                "moe_layer_forward": (I32, [P, I32, I32, I32, I32, F32, P, P, P, D, P, P, P, P, SZ, P, P]),
                 "moe_cache_install": (I32, [P, D, I64, P, I32, P, P]),
                 "moe_cache_create": (P, [D, I32, P, I32, I32]),
                 "moe_cache_destroy": (None, [P]),
@@ -221,8 +228,8 @@ def moe_experts_forward(x, topk_ids, topk_w, E: int, slot_table, slot_pool, desc
         raise ValueError("slot_pool smaller than n_slots * slot_bytes")
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
-    if ws is None:
-        ws = torch.empty(max(moe_forward_workspace_size(T, k, E, desc), 256), dtype=torch.uint8,
+    if ws is None:  # zero-filled: the first 256 bytes must start at zero
+        ws = torch.zeros(max(moe_forward_workspace_size(T, k, E, desc), 256), dtype=torch.uint8,
                          device=x.device)
     _check(lib().moe_experts_forward_ex(
         _dev_ptr(x, torch.bfloat16, "x", 2), T, _dev_ptr(topk_ids, torch.int32, "topk_ids", 2),
@@ -231,6 +238,37 @@ def moe_experts_forward(x, topk_ids, topk_w, E: int, slot_table, slot_pool, desc
         ctypes.byref(desc), _dev_ptr(out, torch.bfloat16, "out", 2), _dev_ptr(ws, torch.uint8, "ws"),
         ws.numel(), _opt_ptr(err_word, torch.int32, "err_word"), path, _stream(stream)))
     return out
+
+
+def moe_layer_forward(logits, x, slot_table, slot_pool, desc: SizeClassDesc, k: int,
+                      mode: int = MOE_ROUTE_PLAIN, L: float = 0.0, topk_ids=None, topk_w=None, out=None,
+                      ws=None, err_word=None, stream=None):
+    """Router + routed experts of one layer (one launch for decode-sized batches).
+    Returns (out, topk_ids, topk_w)."""
+    torch = _torch()
+    T, E = logits.shape
+    H = x.shape[1]
+    if H != desc.H:
+        raise ValueError(f"x has {H} columns, size class has H={desc.H}")
+    if slot_pool.numel() < desc.n_slots * desc.slot_bytes:
+        raise ValueError("slot_pool smaller than n_slots * slot_bytes")
+    dev = x.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if ws is None:
+        ws = torch.zeros(max(moe_forward_workspace_size(T, k, E, desc), 256), dtype=torch.uint8, device=dev)
+    _check(lib().moe_layer_forward(
+        _dev_ptr(logits, torch.float32, "logits", 2), T, E, k, mode, L, _dev_ptr(x, torch.bfloat16, "x", 2),
+        _dev_ptr(slot_table, torch.int32, "slot_table", 1), _dev_ptr(slot_pool, torch.uint8, "slot_pool"),
+        ctypes.byref(desc), _dev_ptr(topk_ids, torch.int32, "topk_ids", 2),
+        _dev_ptr(topk_w, torch.float32, "topk_w", 2), _dev_ptr(out, torch.bfloat16, "out", 2),
+        _dev_ptr(ws, torch.uint8, "ws"), ws.numel(), _opt_ptr(err_word, torch.int32, "err_word"),
+        _stream(stream)))
+    return out, topk_ids, topk_w
 
 
 def moe_cache_install(slot_pool, desc: SizeClassDesc, slot: int, src, stream=None, event=None):

@@ -68,8 +68,11 @@ moe::ClassView view_of(const moe_size_class_desc* d)
     return c;
 }
 
+// Forward workspace.  The first MOE_WS_BARRIER_BYTES hold the fused decode
+// kernel's grid barrier (generation word + one arrival flag per workgroup):
+// zero before the first call on a workspace, kept consistent by every call.
 struct FwdLayout {
-    size_t offsets, sorted, pass, sort_ws, hbuf, xp, ybuf, total;
+    size_t bar, offsets, sorted, pass, sort_ws, hbuf, xp, ybuf, total;
 };
 
 FwdLayout fwd_layout(int T, int k, int E, const moe_size_class_desc* d)
@@ -77,6 +80,8 @@ FwdLayout fwd_layout(int T, int k, int E, const moe_size_class_desc* d)
     FwdLayout L;
     const size_t n = (size_t)T * k;
     size_t o = 0;
+    L.bar = o;
+    o += MOE_WS_BARRIER_BYTES;
     L.offsets = o;
     o = align_up(o + sizeof(int32_t) * (E + 1), 256);
     L.sorted = o;
@@ -206,7 +211,7 @@ int moe_experts_forward_ex(const void* x, int T, const int32_t* topk_ids, const 
     if (T < 0) return fail(MOE_E_INVALID, "T < 0");
     if (E < 1 || E > 1024) return fail(MOE_E_INVALID, "E must be in [1, 1024] (got %d)", E);
     if (k < 1 || k > E || k > 32) return fail(MOE_E_INVALID, "k must be in [1, min(E, 32)] (got %d)", k);
-    if (path != MOE_PATH_AUTO && path != MOE_PATH_GEMV && path != MOE_PATH_MFMA)
+    if (path != MOE_PATH_AUTO && path != MOE_PATH_GEMV && path != MOE_PATH_MFMA && path != MOE_PATH_GEMV3)
         return fail(MOE_E_INVALID, "unknown path %d", path);
     if ((int64_t)T * k > (int64_t)1 << 26) return fail(MOE_E_INVALID, "T*k too large");
     if (T == 0) return MOE_OK;
@@ -219,7 +224,7 @@ int moe_experts_forward_ex(const void* x, int T, const int32_t* topk_ids, const 
 
     const moe::ClassView c = view_of(d);
     const bool gemv_ok = moe::gemv_supported(T, k, c);
-    if (path == MOE_PATH_GEMV && !gemv_ok)
+    if ((path == MOE_PATH_GEMV || path == MOE_PATH_GEMV3) && !gemv_ok)
         return fail(MOE_E_UNSUPPORTED, "GEMV path supports T <= 64 and H/32, I/32 with an odd part <= 4");
     if (path == MOE_PATH_AUTO) path = (gemv_ok && (int64_t)T * k <= 128) ? MOE_PATH_GEMV : MOE_PATH_MFMA;
 
@@ -228,12 +233,20 @@ int moe_experts_forward_ex(const void* x, int T, const int32_t* topk_ids, const 
     int32_t* sorted = (int32_t*)(w + L.sorted);
     int32_t* pass = (int32_t*)(w + L.pass);
     uint16_t* hbuf = (uint16_t*)(w + L.hbuf);
-    hipError_t e = moe::launch_sort(topk_ids, T, k, E, kPassExperts, offsets, sorted, pass,
+    const uint8_t* pool = (const uint8_t*)slot_pool;
+    hipError_t e;
+    if (path == MOE_PATH_GEMV && moe::decode_fused_supported(T, k, E, c)) {
+        e = moe::launch_decode_fused(nullptr, MOE_ROUTE_PLAIN, 0.0f, topk_ids, topk_w, nullptr,
+                                     nullptr, T, E, k, (const uint16_t*)x, slot_table, pool, c,
+                                     (uint16_t*)out, hbuf, (uint32_t*)(w + L.bar), err_word, stream);
+        if (e != hipSuccess) return hip_fail(e, "fused decode launch");
+        return MOE_OK;
+    }
+    e = moe::launch_sort(topk_ids, T, k, E, kPassExperts, offsets, sorted, pass,
                                     w + L.sort_ws, err_word, stream);
     if (e != hipSuccess) return hip_fail(e, "sort launch");
     moe::SortView sv{offsets, sorted, pass};
-    const uint8_t* pool = (const uint8_t*)slot_pool;
-    if (path == MOE_PATH_GEMV) {
+    if (path == MOE_PATH_GEMV || path == MOE_PATH_GEMV3) {
         e = moe::launch_gemv_gateup((const uint16_t*)x, T, k, E, sv, slot_table, pool, c, hbuf,
                                     err_word, stream);
         if (e != hipSuccess) return hip_fail(e, "gemv gate/up launch");
@@ -253,6 +266,43 @@ int moe_experts_forward_ex(const void* x, int T, const int32_t* topk_ids, const 
     e = moe::launch_combine(ybuf, topk_w, T, k, c.H, (uint16_t*)out, stream);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return MOE_OK;
+}
+
+int moe_layer_forward(const float* logits, int T, int E, int k, int mode, float L, const void* x,
+                      const int32_t* slot_table, const void* slot_pool, const moe_size_class_desc* d,
+                      int32_t* topk_ids, float* topk_w, void* out, void* ws, size_t ws_bytes,
+                      uint32_t* err_word, hipStream_t stream)
+{
+    if (int rc = check_desc(d)) return rc;
+    if (T < 0) return fail(MOE_E_INVALID, "T < 0");
+    if (E < 1 || E > 1024) return fail(MOE_E_INVALID, "E must be in [1, 1024] (got %d)", E);
+    if (k < 1 || k > E || k > 32) return fail(MOE_E_INVALID, "k must be in [1, min(E, 32)] (got %d)", k);
+    if (mode != MOE_ROUTE_PLAIN && mode != MOE_ROUTE_SUBST)
+        return fail(MOE_E_INVALID, "unknown routing mode %d", mode);
+    if (mode == MOE_ROUTE_SUBST && (!(L >= 0.0f) || !std::isfinite(L)))
+        return fail(MOE_E_INVALID, "L must be finite and >= 0");
+    if ((int64_t)T * k > (int64_t)1 << 26) return fail(MOE_E_INVALID, "T*k too large");
+    if (T == 0) return MOE_OK;
+    if (!logits || !x || !slot_table || !slot_pool || !out || !topk_ids || !topk_w)
+        return fail(MOE_E_INVALID, "NULL buffer");
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(slot_pool, 256) || !aligned(ws, 256))
+        return fail(MOE_E_INVALID, "x/out need 16-byte, slot_pool/ws 256-byte alignment");
+    const FwdLayout Lw = fwd_layout(T, k, E, d);
+    if (ws_bytes < Lw.total) return fail(MOE_E_WORKSPACE, "forward workspace %zu bytes < %zu", ws_bytes, Lw.total);
+    const moe::ClassView c = view_of(d);
+    if (moe::decode_fused_supported(T, k, E, c)) {
+        char* w = (char*)ws;
+        hipError_t e = moe::launch_decode_fused(logits, mode, L, nullptr, nullptr, topk_ids, topk_w, T, E,
+                                                k, (const uint16_t*)x, slot_table, (const uint8_t*)slot_pool,
+                                                c, (uint16_t*)out, (uint16_t*)(w + Lw.hbuf),
+                                                (uint32_t*)(w + Lw.bar), err_word, stream);
+        if (e != hipSuccess) return hip_fail(e, "fused decode launch");
+        return MOE_OK;
+    }
+    if (int rc = moe_route_topk(logits, T, E, k, mode, L, slot_table, topk_ids, topk_w, err_word, stream))
+        return rc;
+    return moe_experts_forward_ex(x, T, topk_ids, topk_w, k, E, slot_table, slot_pool, d, out, ws,
+                                  ws_bytes, err_word, MOE_PATH_AUTO, stream);
 }
 
 int moe_experts_forward(const void* x, int T, const int32_t* topk_ids, const float* topk_w, int k,

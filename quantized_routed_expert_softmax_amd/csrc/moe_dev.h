@@ -113,12 +113,53 @@ __device__ __forceinline__ void unit_pairs(const uint32_t (&w)[B], uint32_t (&pr
     }
 }
 
-// Sum over lanes within aligned segments of `width` lanes (power of two <= 64);
-// every lane of a segment gets the segment's sum.  Fixed butterfly order.
+// DPP lane moves within rows of 16 (gfx9 encodings): 0xB1 quad xor 1, 0x4E quad
+// xor 2, 0x141 half-row mirror (lane i <-> 7-i), 0x140 row mirror (i <-> 15-i).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
+                                                      0xF, 0xF, false));
+}
+
+// v + (the same register of lane i ^ 16), resp. i ^ 32, via the gfx950 swaps.
+__device__ __forceinline__ float xor16_add(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_add(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over aligned segments of W lanes (W a power of two <= 64); every lane of a
+// segment gets the same sum (each step adds a lane to its partner, and the
+// partner adds the same two values).  DPP and lane swaps, no LDS traffic.
+template <int W>
+__device__ __forceinline__ float seg_sum_w(float v)
+{
+    if constexpr (W >= 2) v += dpp_move<0xB1>(v);
+    if constexpr (W >= 4) v += dpp_move<0x4E>(v);
+    if constexpr (W >= 8) v += dpp_move<0x141>(v);
+    if constexpr (W >= 16) v += dpp_move<0x140>(v);
+    if constexpr (W >= 32) v = xor16_add(v);
+    if constexpr (W >= 64) v = xor32_add(v);
+    return v;
+}
+
 __device__ __forceinline__ float seg_sum(float v, int width)
 {
-    for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    switch (width) {
+    case 1: return v;
+    case 2: return seg_sum_w<2>(v);
+    case 4: return seg_sum_w<4>(v);
+    case 8: return seg_sum_w<8>(v);
+    case 16: return seg_sum_w<16>(v);
+    case 32: return seg_sum_w<32>(v);
+    default: return seg_sum_w<64>(v);
+    }
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u)

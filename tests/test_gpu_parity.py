@@ -203,7 +203,7 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("path", [B.MOE_PATH_GEMV, B.MOE_PATH_MFMA])
+@pytest.mark.parametrize("path", [B.MOE_PATH_GEMV, B.MOE_PATH_GEMV3, B.MOE_PATH_MFMA])
 @pytest.mark.parametrize("shape", SMALL)
 def test_forward_small(shape, path):
     T, H, E, I, k, bg, bd = shape
@@ -227,7 +227,7 @@ def test_forward_many_rows_per_expert_mfma():
     check_close(out, ref, "skewed")
 
 
-@pytest.mark.parametrize("path", [B.MOE_PATH_GEMV, B.MOE_PATH_MFMA])
+@pytest.mark.parametrize("path", [B.MOE_PATH_GEMV, B.MOE_PATH_GEMV3, B.MOE_PATH_MFMA])
 def test_forward_deterministic_and_placement_free(path):
     pr = synth.tiny_problem()
     ids, w = oracle.route(pr.logits, pr.k)
@@ -257,7 +257,7 @@ def test_forward_paths_agree():
 def test_forward_error_words():
     pr = synth.tiny_problem()
     ids, w = oracle.route(pr.logits, pr.k)
-    for path in (B.MOE_PATH_GEMV, B.MOE_PATH_MFMA):
+    for path in (B.MOE_PATH_GEMV, B.MOE_PATH_GEMV3, B.MOE_PATH_MFMA):
         table = pr.table.copy()
         table[ids[0, 0]] = -1
         _, ew = run_forward(pr, ids, w, path, table=table)
@@ -322,11 +322,21 @@ def test_forward_decode_layer_full_size(layer):
     ids, w = B.moe_route_topk(to_dev(lg), wl.k)
     ids_o, w_o = oracle.route(lg, wl.k)
     assert np.array_equal(ids.cpu().numpy(), ids_o)
-    for path in (B.MOE_PATH_AUTO, B.MOE_PATH_MFMA):
+    ref = oracle_on_rows(x, ids_o, w_o, table, pool, lay, wl.E, [0])
+    for path in (B.MOE_PATH_AUTO, B.MOE_PATH_GEMV3, B.MOE_PATH_MFMA):
         out, ew = forward_dev(dev_bf16(x), ids, w, wl.E, to_dev(table), pool, lay, path)
         assert ew == 0
-        ref = oracle_on_rows(x, ids_o, w_o, table, pool, lay, wl.E, [0])
         check_close(out, ref, f"decode layer {layer} path {path}")
+    # router + experts in one launch
+    desc = B.moe_size_class_init(lay.H, lay.I, lay.bits_gu, lay.bits_d, pool.shape[0])
+    ew = err_word()
+    out, ids2, w2 = B.moe_layer_forward(to_dev(lg), dev_bf16(x), to_dev(table), pool.view(-1), desc,
+                                        wl.k, err_word=ew)
+    _torch().cuda.synchronize()
+    assert int(ew.item()) == 0
+    assert np.array_equal(ids2.cpu().numpy(), ids_o)
+    assert np.array_equal(w2.cpu().numpy().view(np.uint32), w_o.view(np.uint32))
+    check_close(out, ref, f"decode layer {layer} moe_layer_forward")
 
 
 def test_forward_prefill_chunk_full_size():
@@ -369,11 +379,11 @@ def test_forward_mixed_classes_full_size(T, layer):
     ids, w = B.moe_route_topk(to_dev(lg), wl.k)
     ids_o, w_o = oracle.route(lg, wl.k)
     assert np.array_equal(ids.cpu().numpy(), ids_o)
-    for path in (B.MOE_PATH_AUTO, B.MOE_PATH_MFMA):
+    tokens = list(range(T))
+    ref = oracle_on_rows(x, ids_o, w_o, table, pool, lay, wl.E, tokens)
+    for path in (B.MOE_PATH_AUTO, B.MOE_PATH_GEMV3, B.MOE_PATH_MFMA):
         out, ew = forward_dev(dev_bf16(x), ids, w, wl.E, to_dev(table), pool, lay, path)
         assert ew == 0
-        tokens = list(range(T))
-        ref = oracle_on_rows(x, ids_o, w_o, table, pool, lay, wl.E, tokens)
         check_close(out, ref, f"mixed layer {layer} T {T} path {path}")
 
 
@@ -430,6 +440,10 @@ def test_int8_substitution_with_installs_full_size():
         table1 = B.moe_cache_table(cache, 0, E)
         assert np.all(table1[ids_o.reshape(-1)] >= 0)
         x = synth.gen_x(synth.rng_for(wl.seed, 1), T, wl.H)
+        # oracle: canonical placement (expert e in row e of the host tier)
+        tokens = [0, 7, 19, 31]
+        ref = oracle.layer(x, ids_o, w_o, np.arange(E, dtype=np.int32), host.numpy(), lay.H,
+                           lay.I, 8, 8, E, tokens=np.asarray(tokens, np.int32), threads=THREADS)
         for path in (B.MOE_PATH_AUTO, B.MOE_PATH_GEMV):
             ew = err_word()
             out = B.moe_experts_forward(dev_bf16(x), ids, w, E, to_dev(table1), pool.view(-1), desc,
@@ -437,10 +451,89 @@ def test_int8_substitution_with_installs_full_size():
             torch.cuda.synchronize()
             assert int(ew.item()) == 0
             assert B.moe_cache_poll(cache) == 0
-            # oracle: canonical placement (expert e in row e of the host tier)
-            tokens = [0, 7, 19, 31]
-            ref = oracle.layer(x, ids_o, w_o, np.arange(E, dtype=np.int32), host.numpy(), lay.H,
-                               lay.I, 8, 8, E, tokens=np.asarray(tokens, np.int32), threads=THREADS)
             check_close(out[tokens], ref, f"int8 subst path {path}")
     finally:
         B.moe_cache_destroy(cache)
+
+
+# --------------------------------------------------------------------------- #
+# router + experts in one launch                                               #
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("shape", [
+    (1, 256, 8, 128, 2, 4, 4, 0),
+    (8, 128, 16, 64, 8, 4, 6, 1),     # 64 pairs: the largest fused batch
+    (3, 512, 16, 256, 4, 3, 3, 1),
+    (2, 256, 10, 64, 5, 8, 8, 0),
+    (9, 128, 16, 64, 8, 3, 3, 0),     # 72 pairs: falls back to two calls
+])
+def test_layer_forward_matches_route_plus_forward(shape):
+    torch = _torch()
+    T, H, E, I, k, bg, bd, subst = shape
+    pr = synth.make_problem(400 + T + H, T, H, E, I, k, bg, bd, n_slots=E + 2,
+                            resident=None)
+    mode = B.MOE_ROUTE_SUBST if subst else B.MOE_ROUTE_PLAIN
+    ids_o, w_o = oracle.route(pr.logits, k, mode=mode, L=0.15, slot_table=pr.table)
+    desc = B.moe_size_class_init(H, I, bg, bd, pr.pool.shape[0])
+    ew = err_word()
+    out, ids, w = B.moe_layer_forward(to_dev(pr.logits), dev_bf16(pr.x), to_dev(pr.table),
+                                      to_dev(pr.pool.reshape(-1)), desc, k, mode=mode, L=0.15,
+                                      err_word=ew)
+    torch.cuda.synchronize()
+    assert int(ew.item()) == 0
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), w_o.view(np.uint32))
+    ref = oracle.layer(pr.x, ids_o, w_o, pr.table, pr.pool, H, I, bg, bd, E, threads=THREADS)
+    check_close(out, ref, f"layer_forward {shape}")
+    # identical to the two-call form on the fused kernel
+    out2, _ = run_forward(pr, ids_o, w_o, B.MOE_PATH_GEMV)
+    assert np.array_equal(out.view(torch.int16).cpu().numpy(), out2.view(torch.int16).cpu().numpy())
+
+
+def test_fused_decode_repeated_calls_and_graph_replay():
+    """The fused kernel's grid barrier lives in the workspace: a generation word
+    (bytes 0..3) that counts calls and one arrival flag per workgroup (from byte
+    256) that holds the generation of its last arrival.  Many calls on one
+    workspace, eager and replayed from a HIP graph, give the same bits and never
+    time out."""
+    torch = _torch()
+    pr = synth.make_problem(77, 4, 256, 16, 128, 4, 3, 3)
+    desc = B.moe_size_class_init(256, 128, 3, 3, pr.pool.shape[0])
+    lg, x = to_dev(pr.logits), dev_bf16(pr.x)
+    table, pool = to_dev(pr.table), to_dev(pr.pool.reshape(-1))
+    ws = torch.zeros(B.moe_forward_workspace_size(4, 4, 16, desc), dtype=torch.uint8, device="cuda")
+    ew = err_word()
+    outs = []
+    for _ in range(30):
+        out, _, _ = B.moe_layer_forward(lg, x, table, pool, desc, 4, ws=ws, err_word=ew)
+        outs.append(out.view(torch.int16).clone())
+    torch.cuda.synchronize()
+    assert int(ew.item()) == 0
+    assert all(torch.equal(outs[0], o) for o in outs)
+    gen = ws[:8192].view(torch.int32)
+    assert int(gen[0].item()) == 30
+    assert int(gen[1:64].count_nonzero().item()) == 0
+    flags = gen[64:]
+    n_wg = int((flags != 0).sum().item())
+    assert n_wg >= 1 and bool((flags[:n_wg] == 30).all()) and int(flags[n_wg:].count_nonzero().item()) == 0
+    out_g = torch.empty_like(out)
+    ids_g = torch.empty((4, 4), dtype=torch.int32, device="cuda")
+    w_g = torch.empty((4, 4), dtype=torch.float32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(3):
+                B.moe_layer_forward(lg, x, table, pool, desc, 4, topk_ids=ids_g, topk_w=w_g, out=out_g,
+                                    ws=ws, err_word=ew)
+    torch.cuda.current_stream().wait_stream(s)
+    for r in range(5):
+        out_g.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), outs[0]), f"replay {r}"
+        # eager work between replays
+        B.moe_layer_forward(lg, x, table, pool, desc, 4, ws=ws, err_word=ew)
+        torch.cuda.synchronize()
+    assert int(ew.item()) == 0
+    assert int(ws[:4].view(torch.int32).item()) == 30 + 5 * 3 + 5
