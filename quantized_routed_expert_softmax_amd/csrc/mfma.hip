@@ -26,6 +26,8 @@
 // in identical accumulator layouts), h written as bf16 in P16 order.
 // down: y per (pair, output) in fp32 to a workspace; a combine kernel adds the
 // k contributions of each token in j order (deterministic).
+#include <utility>
+
 #include "../../include/moe.h"
 #include "moe_dev.h"
 #include "moe_internal.h"
@@ -34,6 +36,18 @@ namespace moe {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+// Calls f(std::integral_constant<int, i>) for i = 0..N-1 (indices known at compile time).
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>)
+{
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ f32x4_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c)
 {
@@ -84,102 +98,50 @@ __device__ __forceinline__ u32x4_t lane_pairs(const uint32_t* __restrict__ unit,
     return r;
 }
 
-constexpr int kMaxMT = 4;  // M-tiles (of 16 rows) per K sweep
+constexpr int kMT = 4;            // M-tiles (of 16 rows) per sweep of K
+constexpr int kKC = 128;          // K per pipeline stage
+constexpr int kUPC = kKC / 32;    // pack units per stage
+constexpr int kGPC = kKC / 64;    // groups per stage
+constexpr int kAROW = kKC + 8;    // bf16 per staged activation row (padding: conflict-free reads)
 
+// One pipeline stage in LDS: raw codes and scale/bias of the workgroup's NB*64
+// weight rows for kKC inputs, and kKC activations of up to kMT*16 rows.
+template <int B, int NB>
+struct Stage {
+    uint32_t codes[NB * 64][kUPC * B];
+    uint32_t sb[NB * 64][kGPC];
+    uint16_t a[kMT * 16][kAROW];
+};
+
+// The 4 P16 pairs of lane group g from the dwords of one unit held in LDS
+// (same bit arithmetic as lane_pairs, reading LDS instead of global memory).
 template <int B>
-__global__ __launch_bounds__(256) void mfma_gateup_kernel(
-    const uint16_t* __restrict__ xp, int H, int I, int k, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table,
-    const int32_t* __restrict__ table, const uint8_t* __restrict__ pool, int64_t n_slots,
-    int64_t slot_bytes, int64_t off_codes, int64_t off_sb, uint16_t* __restrict__ hbuf,
-    uint32_t* __restrict__ err)
+__device__ __forceinline__ u32x4_t lds_pairs(const uint32_t* __restrict__ unit, int g)
 {
-    const int hit = blockIdx.y;
-    if (hit >= pass_table[0]) return;
-    const int e = pass_table[2 + hit];
-    const int32_t slot = table[e];
-    if (slot < 0 || slot >= n_slots) {
-        if (threadIdx.x == 0 && err) atomicOr(err, slot < 0 ? MOE_ERRW_NOT_RESIDENT : MOE_ERRW_BAD_SLOT);
-        return;
-    }
-    const int base = offsets[e], cnt = offsets[e + 1] - base;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, c16 = lane & 15;
-    const int n = blockIdx.x * 64 + wave * 16 + c16;  // gate column; up column I + n
-
-    const uint8_t* rowb = pool + (size_t)slot * (size_t)slot_bytes;
-    const size_t row_dw = (size_t)H * B / 32;
-    const uint32_t* gc = (const uint32_t*)(rowb + off_codes) + (size_t)n * row_dw;
-    const uint32_t* uc = (const uint32_t*)(rowb + off_codes) + (size_t)(I + n) * row_dw;
-    const uint32_t* gsb = (const uint32_t*)(rowb + off_sb) + (size_t)n * (H / 64);
-    const uint32_t* usb = (const uint32_t*)(rowb + off_sb) + (size_t)(I + n) * (H / 64);
-    constexpr float off = Code<B>::offset;
-    const u32x4_t ones = {MOE_ONES_PAIR, MOE_ONES_PAIR, MOE_ONES_PAIR, MOE_ONES_PAIR};
-    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-
-    for (int m0 = 0; m0 < cnt; m0 += 16 * kMaxMT) {
-        const int nmt = min(kMaxMT, (cnt - m0 + 15) >> 4);
-        const u32x4_t* arow[kMaxMT];
-#pragma unroll
-        for (int mt = 0; mt < kMaxMT; ++mt) {
-            int r = m0 + mt * 16 + c16;
-            r = r < cnt ? r : cnt - 1;
-            const int t = sorted_pairs[base + r] / k;
-            arow[mt] = (const u32x4_t*)(xp + (size_t)t * H);
-        }
-        f32x4_t accg[kMaxMT], accu[kMaxMT];
-#pragma unroll
-        for (int mt = 0; mt < kMaxMT; ++mt) accg[mt] = accu[mt] = zero;
-
-        for (int G = 0; G < H / 64; ++G) {
-            const u32x4_t bg0 = lane_pairs<B>(gc + (2 * G) * B, g);
-            const u32x4_t bg1 = lane_pairs<B>(gc + (2 * G + 1) * B, g);
-            const u32x4_t bu0 = lane_pairs<B>(uc + (2 * G) * B, g);
-            const u32x4_t bu1 = lane_pairs<B>(uc + (2 * G + 1) * B, g);
-            const uint32_t g2 = gsb[G], u2 = usb[G];
-            const float sg = half_bits_to_f32(g2 & 0xFFFFu);
-            const float zg = __builtin_fmaf(-off, sg, half_bits_to_f32(g2 >> 16));
-            const float su = half_bits_to_f32(u2 & 0xFFFFu);
-            const float zu = __builtin_fmaf(-off, su, half_bits_to_f32(u2 >> 16));
-#pragma unroll
-            for (int mt = 0; mt < kMaxMT; ++mt) {
-                if (mt < nmt) {
-                    const u32x4_t a0 = arow[mt][(2 * G) * 4 + g];
-                    const u32x4_t a1 = arow[mt][(2 * G + 1) * 4 + g];
-                    f32x4_t tg = mfma(a0, bg0, zero);
-                    tg = mfma(a1, bg1, tg);
-                    f32x4_t tu = mfma(a0, bu0, zero);
-                    tu = mfma(a1, bu1, tu);
-                    f32x4_t tx = mfma(a0, ones, zero);
-                    tx = mfma(a1, ones, tx);
-                    accg[mt] += sg * tg + zg * tx;
-                    accu[mt] += su * tu + zu * tx;
-                }
-            }
-        }
-        const int pos = (n & ~31) | p16_pos(n & 31);
-#pragma unroll
-        for (int mt = 0; mt < kMaxMT; ++mt) {
-            if (mt < nmt) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = m0 + mt * 16 + 4 * g + i;
-                    if (r < cnt)
-                        hbuf[(size_t)(base + r) * I + pos] = f32_to_bf16(silu_mul(accg[mt][i], accu[mt][i]));
-                }
-            }
-        }
+    if constexpr (B == 8) {
+        return lane_pairs<8>(unit, g);
+    } else {
+        return lane_pairs<B>(unit, g);
     }
 }
 
-template <int B>
-__global__ __launch_bounds__(256) void mfma_down_kernel(
-    int H, int I, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted_pairs,
-    const int32_t* __restrict__ pass_table, const int32_t* __restrict__ table,
-    const uint8_t* __restrict__ pool, int64_t n_slots, int64_t slot_bytes, int64_t off_codes,
-    int64_t off_sb, const uint16_t* __restrict__ hbuf, float* __restrict__ ybuf,
-    uint32_t* __restrict__ err)
+// Grouped dequantizing GEMM for one hit expert and 64 output columns per
+// workgroup (16 per wave), pipelined through LDS in stages of kKC inputs.
+//   GU = true : gate/up.  Weight rows: gate n0..n0+63 and up I+n0..; A = P16 x
+//               rows of the expert's pairs (via sorted_pairs); epilogue SwiGLU
+//               -> h (bf16, P16) at the pair's sorted position.
+//   GU = false: down.  Weight rows n0..n0+63 of the down matrix; A = h rows;
+//               epilogue y (fp32) at [pair id][n].
+template <int B, bool GU>
+__global__ __launch_bounds__(256, 2) void mfma_grouped_kernel(
+    const uint16_t* __restrict__ act, int H, int I, int k, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table,
+    const int32_t* __restrict__ table, const uint8_t* __restrict__ pool, int64_t n_slots,
+    int64_t slot_bytes, int64_t off_codes, int64_t off_sb, uint16_t* __restrict__ hbuf,
+    float* __restrict__ ybuf, uint32_t* __restrict__ err)
 {
+    constexpr int NB = GU ? 2 : 1;
+    __shared__ Stage<B, NB> st[2];
     const int hit = blockIdx.y;
     if (hit >= pass_table[0]) return;
     const int e = pass_table[2 + hit];
@@ -189,61 +151,165 @@ __global__ __launch_bounds__(256) void mfma_down_kernel(
         return;
     }
     const int base = offsets[e], cnt = offsets[e + 1] - base;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    const int n = blockIdx.x * 64 + wave * 16 + c16;  // output row of the down matrix
+    const int K = GU ? H : I;            // reduction length
+    const int n0 = blockIdx.x * 64;      // first output column of the workgroup
+    const int n = n0 + wave * 16 + c16;  // this lane's column
+    const int NC = K / kKC;              // stages per sweep (K is a multiple of 64)
+    const bool tail = (K % kKC) != 0;    // a last half stage of 64 inputs
+    const int n_stages = NC + (tail ? 1 : 0);
 
     const uint8_t* rowb = pool + (size_t)slot * (size_t)slot_bytes;
-    const size_t row_dw = (size_t)I * B / 32;
-    const uint32_t* dc = (const uint32_t*)(rowb + off_codes) + (size_t)n * row_dw;
-    const uint32_t* dsb = (const uint32_t*)(rowb + off_sb) + (size_t)n * (I / 64);
+    const size_t row_dw = (size_t)K * B / 32;
+    const uint32_t* codes = (const uint32_t*)(rowb + off_codes);
+    const uint32_t* sbg = (const uint32_t*)(rowb + off_sb);
     constexpr float off = Code<B>::offset;
     const u32x4_t ones = {MOE_ONES_PAIR, MOE_ONES_PAIR, MOE_ONES_PAIR, MOE_ONES_PAIR};
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 
-    for (int m0 = 0; m0 < cnt; m0 += 16 * kMaxMT) {
-        const int nmt = min(kMaxMT, (cnt - m0 + 15) >> 4);
-        const u32x4_t* arow[kMaxMT];
-#pragma unroll
-        for (int mt = 0; mt < kMaxMT; ++mt) {
-            int r = m0 + mt * 16 + c16;
-            r = r < cnt ? r : cnt - 1;
-            arow[mt] = (const u32x4_t*)(hbuf + (size_t)(base + r) * I);
-        }
-        f32x4_t acc[kMaxMT];
-#pragma unroll
-        for (int mt = 0; mt < kMaxMT; ++mt) acc[mt] = zero;
+    // weight row (in the whole matrix) of the workgroup's local row r
+#define wrow(R) (GU ? ((R) < 64 ? n0 + (R) : I + n0 + ((R) - 64)) : n0 + (R))
 
-        for (int G = 0; G < I / 64; ++G) {
-            const u32x4_t b0 = lane_pairs<B>(dc + (2 * G) * B, g);
-            const u32x4_t b1 = lane_pairs<B>(dc + (2 * G + 1) * B, g);
-            const uint32_t s2 = dsb[G];
-            const float s = half_bits_to_f32(s2 & 0xFFFFu);
-            const float z = __builtin_fmaf(-off, s, half_bits_to_f32(s2 >> 16));
+    // staging assignment: B pieces (16 B), sb dwords, A pieces (16 B)
+    constexpr int BPIECES = NB * 64 * B;                 // per stage (B pieces of 16 B per row)
+    constexpr int BPT = (BPIECES + 255) / 256;
+    constexpr int SBN = NB * 64 * kGPC;                  // sb dwords per stage
+    constexpr int APT = kMT * 16 * (kKC / 8) / 256;      // A pieces per thread (= 4)
+
+    for (int m0 = 0; m0 < cnt; m0 += 16 * kMT) {
+        const int rows = min(16 * kMT, cnt - m0);
+        const int nmt = (rows + 15) >> 4;
+        // activation row pointers of this thread's A pieces (fixed for the sweep)
+        // rows past the expert's last pair re-read its last row (results discarded)
+        const uint16_t* arow[APT];
 #pragma unroll
-            for (int mt = 0; mt < kMaxMT; ++mt) {
-                if (mt < nmt) {
-                    const u32x4_t a0 = arow[mt][(2 * G) * 4 + g];
-                    const u32x4_t a1 = arow[mt][(2 * G + 1) * 4 + g];
-                    f32x4_t ty = mfma(a0, b0, zero);
-                    ty = mfma(a1, b1, ty);
-                    f32x4_t tx = mfma(a0, ones, zero);
-                    tx = mfma(a1, ones, tx);
-                    acc[mt] += s * ty + z * tx;
+        for (int i = 0; i < APT; ++i) {
+            const int q = tid + 256 * i;
+            int m = q / (kKC / 8);
+            m = m < rows ? m : rows - 1;
+            if (GU) arow[i] = act + (size_t)(sorted_pairs[base + m0 + m] / k) * H;
+            else arow[i] = act + (size_t)(base + m0 + m) * I;
+        }
+        u32x4_t rb[BPT];
+        uint32_t rs;
+        u32x4_t ra[APT];
+// every staging load is unconditional (indices clamped to valid data), so the
+// staging registers are never spilled and the loads stay in flight
+#define MOE_LOAD_STAGE(C)                                                                       \
+    {                                                                                           \
+        const int kin_ = (C) * kKC;                                                             \
+        const int units_ = (kin_ + kKC <= K) ? kUPC : (K - kin_) / 32;                          \
+        static_for<BPT>([&](auto I_) {                                                          \
+            constexpr int i = decltype(I_)::value;                                              \
+            int q = tid + 256 * i;                                                              \
+            q = q < BPIECES ? q : BPIECES - 1;                                                  \
+            const int r = q / B;                                                                \
+            int p = q - r * B;                                                                  \
+            p = p * 4 < units_ * B ? p : 0;                                                     \
+            rb[i] = *(const u32x4_t*)(codes + (size_t)wrow(r) * row_dw + (size_t)(kin_ / 32) * B + p * 4); \
+        });                                                                                     \
+        {                                                                                       \
+            const int qs = tid < SBN ? tid : SBN - 1;                                           \
+            const int r = qs / kGPC;                                                            \
+            int gg = qs - r * kGPC;                                                             \
+            gg = gg * 64 < units_ * 32 ? gg : 0;                                                \
+            rs = sbg[(size_t)wrow(r) * (K / 64) + kin_ / 64 + gg];                              \
+        }                                                                                       \
+        static_for<APT>([&](auto I_) {                                                          \
+            constexpr int i = decltype(I_)::value;                                              \
+            int p = (tid + 256 * i) % (kKC / 8);                                                \
+            p = p * 8 < units_ * 32 ? p : 0;                                                    \
+            ra[i] = *(const u32x4_t*)(arow[i] + kin_ + p * 8);                                  \
+        });                                                                                     \
+    }
+#define MOE_STORE_STAGE(BUF)                                                                    \
+    {                                                                                           \
+        Stage<B, NB>& S_ = st[(BUF)];                                                           \
+        static_for<BPT>([&](auto I_) {                                                          \
+            constexpr int i = decltype(I_)::value;                                              \
+            const int q = tid + 256 * i;                                                        \
+            if (q < BPIECES) {                                                                  \
+                const int r = q / B, p = q - r * B;                                             \
+                *(u32x4_t*)(&S_.codes[r][p * 4]) = rb[i];                                       \
+            }                                                                                   \
+        });                                                                                     \
+        if (tid < SBN) S_.sb[tid / kGPC][tid % kGPC] = rs;                                      \
+        static_for<APT>([&](auto I_) {                                                          \
+            constexpr int i = decltype(I_)::value;                                              \
+            const int q = tid + 256 * i;                                                        \
+            *(u32x4_t*)(&S_.a[q / (kKC / 8)][(q % (kKC / 8)) * 8]) = ra[i];                    \
+        });                                                                                     \
+    }
+
+        f32x4_t acc[NB][kMT];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mt = 0; mt < kMT; ++mt) acc[nb][mt] = zero;
+
+        MOE_LOAD_STAGE(0)
+        MOE_STORE_STAGE(0)
+        __syncthreads();
+        for (int c = 0; c < n_stages; ++c) {
+            if (c + 1 < n_stages) MOE_LOAD_STAGE(c + 1)
+            const Stage<B, NB>& S = st[c & 1];
+            const int kin = c * kKC;
+            const int groups = (kin + kKC <= K) ? kGPC : (K - kin) / 64;
+            for (int G2 = 0; G2 < groups; ++G2) {
+                u32x4_t bw[NB][2];
+                float sc[NB], zc[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int r = nb * 64 + wave * 16 + c16;
+                    bw[nb][0] = lds_pairs<B>(&S.codes[r][(2 * G2) * B], g);
+                    bw[nb][1] = lds_pairs<B>(&S.codes[r][(2 * G2 + 1) * B], g);
+                    const uint32_t s2 = S.sb[r][G2];
+                    sc[nb] = half_bits_to_f32(s2 & 0xFFFFu);
+                    zc[nb] = __builtin_fmaf(-off, sc[nb], half_bits_to_f32(s2 >> 16));
+                }
+#pragma unroll
+                for (int mt = 0; mt < kMT; ++mt) {
+                    if (mt < nmt) {
+                        const u32x4_t a0 = *(const u32x4_t*)(&S.a[mt * 16 + c16][(2 * G2) * 32 + 8 * g]);
+                        const u32x4_t a1 = *(const u32x4_t*)(&S.a[mt * 16 + c16][(2 * G2 + 1) * 32 + 8 * g]);
+                        f32x4_t tx = mfma(a0, ones, zero);
+                        tx = mfma(a1, ones, tx);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) {
+                            f32x4_t t = mfma(a0, bw[nb][0], zero);
+                            t = mfma(a1, bw[nb][1], t);
+                            acc[nb][mt] += sc[nb] * t + zc[nb] * tx;
+                        }
+                    }
                 }
             }
+            if (c + 1 < n_stages) MOE_STORE_STAGE((c + 1) & 1)
+            __syncthreads();
         }
+#undef MOE_LOAD_STAGE
+#undef MOE_STORE_STAGE
+
+        // epilogue
 #pragma unroll
-        for (int mt = 0; mt < kMaxMT; ++mt) {
+        for (int mt = 0; mt < kMT; ++mt) {
             if (mt < nmt) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = m0 + mt * 16 + 4 * g + i;
-                    if (r < cnt) ybuf[(size_t)sorted_pairs[base + r] * H + n] = acc[mt][i];
+                    if (r < cnt) {
+                        if constexpr (GU) {
+                            const int pos = (n & ~31) | p16_pos(n & 31);
+                            hbuf[(size_t)(base + r) * I + pos] = f32_to_bf16(silu_mul(acc[0][mt][i], acc[1][mt][i]));
+                        } else {
+                            ybuf[(size_t)sorted_pairs[base + r] * H + n] = acc[0][mt][i];
+                        }
+                    }
                 }
             }
         }
     }
+#undef wrow
 }
 
 // x [T, H] bf16 -> P16 layout: within each 32-chunk, position 2i+h holds input i+16h.
@@ -301,9 +367,9 @@ hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const Sor
     const int max_hit = (int64_t)T * k < E ? T * k : E;
     dim3 grid(c.I / 64, max_hit);
 #define MOE_MG(BB)                                                                                 \
-    hipLaunchKernelGGL((mfma_gateup_kernel<BB>), grid, dim3(256), 0, s, xp, c.H, c.I, k,           \
+    hipLaunchKernelGGL((mfma_grouped_kernel<BB, true>), grid, dim3(256), 0, s, xp, c.H, c.I, k,    \
                        sv.offsets, sv.sorted_pairs, sv.pass_table, table, pool, c.n_slots,         \
-                       c.slot_bytes, c.off_gu_codes, c.off_gu_sb, hbuf, err)
+                       c.slot_bytes, c.off_gu_codes, c.off_gu_sb, hbuf, nullptr, err)
     switch (c.bits_gu) {
     case 3: MOE_MG(3); break;
     case 4: MOE_MG(4); break;
@@ -322,9 +388,9 @@ hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, const int32
     const int max_hit = (int64_t)T * k < E ? T * k : E;
     dim3 grid(c.H / 64, max_hit);
 #define MOE_MD(BB)                                                                                 \
-    hipLaunchKernelGGL((mfma_down_kernel<BB>), grid, dim3(256), 0, s, c.H, c.I, sv.offsets,        \
-                       sv.sorted_pairs, sv.pass_table, table, pool, c.n_slots, c.slot_bytes,       \
-                       c.off_d_codes, c.off_d_sb, hbuf, ybuf, err)
+    hipLaunchKernelGGL((mfma_grouped_kernel<BB, false>), grid, dim3(256), 0, s, hbuf, c.H, c.I, k, \
+                       sv.offsets, sv.sorted_pairs, sv.pass_table, table, pool, c.n_slots,         \
+                       c.slot_bytes, c.off_d_codes, c.off_d_sb, nullptr, ybuf, err)
     switch (c.bits_d) {
     case 3: MOE_MD(3); break;
     case 4: MOE_MD(4); break;
