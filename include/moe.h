@@ -107,7 +107,7 @@ extern "C" {
 #define MOE_ERRW_BAD_SLOT      0x2u /* slot_table[e] >= n_slots                 */
 #define MOE_ERRW_NONFINITE     0x4u /* a router logit is NaN or infinite        */
 #define MOE_ERRW_BAD_ID        0x8u /* a top-k id outside [0, E)                */
-#define MOE_ERRW_TIMEOUT      0x10u /* the fused decode kernel's grid barrier gave up */
+#define MOE_ERRW_TIMEOUT      0x10u /* the fused decode kernel's h exchange gave up */
 
 /* ---- routing modes ------------------------------------------------------- */
 #define MOE_ROUTE_PLAIN  0
@@ -120,11 +120,16 @@ extern "C" {
 #define MOE_PATH_GEMV3 3 /* GEMV as three launches (sort, gate/up, down)        */
 
 /* ---- workspace --------------------------------------------------------------
- * The first MOE_WS_BARRIER_BYTES of a forward workspace hold the grid barrier of
- * the fused decode kernel (a generation word and one arrival flag per
- * workgroup).  They must be zero before the first call on that workspace; every
- * call leaves them consistent for the next one.                               */
-#define MOE_WS_BARRIER_BYTES 8192
+ * The first MOE_WS_RESERVED_BYTES of a forward workspace belong to the fused
+ * decode kernel's h exchange: MOE_WS_GEN_BYTES of call-tag counters (one per
+ * workgroup slot, from dword 64), then MOE_WS_XWORDS 64-bit words, each an h
+ * pair (two bf16) in its low half and the tag of the call that wrote it in its
+ * high half.  The prefix must be zero before the first call on a workspace and
+ * is written only by the library afterwards; every call leaves it consistent
+ * for the next one.  No other buffer of any path overlaps it.                 */
+#define MOE_WS_GEN_BYTES 8192
+#define MOE_WS_XWORDS 32768
+#define MOE_WS_RESERVED_BYTES (MOE_WS_GEN_BYTES + 8 * MOE_WS_XWORDS)
 
 /* ---- cache install sources ----------------------------------------------- */
 #define MOE_SRC_HOST    0 /* pinned host memory (hipHostMalloc)                 */
@@ -213,9 +218,9 @@ int    moe_pass_table_size(int E, int pass_experts);
  *   slot_pool  device bytes [d->n_slots * d->slot_bytes].
  *   out        device bf16 [T, H] (overwritten; round to nearest even).
  *   ws         device scratch of moe_forward_workspace_size(...) bytes, 256-byte
- *              aligned; its first MOE_WS_BARRIER_BYTES must be zero before the
- *              first call that uses it (the generation word at bytes 0..3 then
- *              counts the fused calls).  Calls that share one ws must not overlap
+ *              aligned; its first MOE_WS_RESERVED_BYTES must be zero before the
+ *              first call that uses it (the call-tag counters from byte 256 then
+ *              count the fused calls).  Calls that share one ws must not overlap
  *              in time (same stream, or ordered by events).
  *   err_word   MOE_ERRW_NOT_RESIDENT / MOE_ERRW_BAD_SLOT / MOE_ERRW_BAD_ID /
  *              MOE_ERRW_TIMEOUT.

@@ -68,11 +68,12 @@ moe::ClassView view_of(const moe_size_class_desc* d)
     return c;
 }
 
-// Forward workspace.  The first MOE_WS_BARRIER_BYTES hold the fused decode
-// kernel's grid barrier (generation word + one arrival flag per workgroup):
-// zero before the first call on a workspace, kept consistent by every call.
+// Forward workspace.  The first MOE_WS_RESERVED_BYTES hold the fused decode
+// kernel's h exchange (call-tag counters + tagged h words): zero before the
+// first call on a workspace, kept consistent by every call, overlapped by
+// nothing else.
 struct FwdLayout {
-    size_t bar, offsets, sorted, pass, sort_ws, hbuf, xp, ybuf, total;
+    size_t reserved, offsets, sorted, pass, sort_ws, hbuf, xp, ybuf, total;
 };
 
 FwdLayout fwd_layout(int T, int k, int E, const moe_size_class_desc* d)
@@ -80,8 +81,8 @@ FwdLayout fwd_layout(int T, int k, int E, const moe_size_class_desc* d)
     FwdLayout L;
     const size_t n = (size_t)T * k;
     size_t o = 0;
-    L.bar = o;
-    o += MOE_WS_BARRIER_BYTES;
+    L.reserved = o;
+    o += MOE_WS_RESERVED_BYTES;
     L.offsets = o;
     o = align_up(o + sizeof(int32_t) * (E + 1), 256);
     L.sorted = o;
@@ -238,7 +239,7 @@ int moe_experts_forward_ex(const void* x, int T, const int32_t* topk_ids, const 
     if (path == MOE_PATH_GEMV && moe::decode_fused_supported(T, k, E, c)) {
         e = moe::launch_decode_fused(nullptr, MOE_ROUTE_PLAIN, 0.0f, topk_ids, topk_w, nullptr,
                                      nullptr, T, E, k, (const uint16_t*)x, slot_table, pool, c,
-                                     (uint16_t*)out, hbuf, (uint32_t*)(w + L.bar), err_word, stream);
+                                     (uint16_t*)out, w + L.reserved, err_word, stream);
         if (e != hipSuccess) return hip_fail(e, "fused decode launch");
         return MOE_OK;
     }
@@ -294,8 +295,7 @@ int moe_layer_forward(const float* logits, int T, int E, int k, int mode, float 
         char* w = (char*)ws;
         hipError_t e = moe::launch_decode_fused(logits, mode, L, nullptr, nullptr, topk_ids, topk_w, T, E,
                                                 k, (const uint16_t*)x, slot_table, (const uint8_t*)slot_pool,
-                                                c, (uint16_t*)out, (uint16_t*)(w + Lw.hbuf),
-                                                (uint32_t*)(w + Lw.bar), err_word, stream);
+                                                c, (uint16_t*)out, w + Lw.reserved, err_word, stream);
         if (e != hipSuccess) return hip_fail(e, "fused decode launch");
         return MOE_OK;
     }

@@ -1,7 +1,7 @@
 // decode.hip — the whole routed-expert layer for decode-sized batches in ONE
 // persistent launch on gfx950: (route) -> sort by expert -> slot resolve ->
-// gate/up dequant-GEMV + SwiGLU -> grid barrier -> down dequant-GEMV ->
-// weighted combine.
+// gate/up dequant-GEMV + SwiGLU -> h exchange -> down dequant-GEMV -> weighted
+// combine.
 //
 // Sources: "POC: Experts offload", PR description and commit messages (quantized
 // experts through a gather quantized matmul on the device cache; the GPU should
@@ -14,27 +14,39 @@
 // Why one kernel: a decode layer moves ~14 MB (10 experts of 1.38 MB at 3 bits),
 // about 2 us of HBM time, while every extra launch and every dependent global
 // load costs ~1-5 us.  So each workgroup
-//   1. stages router logits, the token rows and nothing else, routes (one wave
+//   1. stages router logits, the token rows and the slot table, routes (one wave
 //      per token, identical arithmetic to the router kernel) and sorts the
 //      <= 64 (token, j) pairs by expert in LDS -- redundantly in every
 //      workgroup, which costs a few hundred cycles and saves a launch and a
 //      global round trip;
 //   2. looks up the hit experts' slots, then issues the loads of ALL its weight
-//      rows at once: the gate/up rows of phase 1 and the down rows of phase 2
-//      (the down weights do not depend on h, so they stream in while gate/up
-//      computes);
-//   3. phase 1: a wave owns gate row n and up row I+n of one hit expert; codes
-//      become bf16 pairs (128 + c) and bf16 dot2 sums them against the P16
-//      paired activations; per unit s*acc + (z - 128 s)*sum(x); h = silu(g)*u
-//      goes to the workspace in bf16;
-//   4. grid barrier (one atomic counter + generation word, bounded spin that
-//      reports MOE_ERRW_TIMEOUT instead of hanging);
-//   5. phase 2: h of all pairs is staged in LDS; wave w of a workgroup takes
-//      hits w, w+4, ... for the workgroup's output rows and accumulates w_j*y per
-//      token; the four waves' partial sums are added in wave order, so the
-//      result is bit-reproducible.
+//      rows at once (one vector load per pack unit): the gate/up rows of phase 1
+//      and the down rows of phase 2 (the down weights do not depend on h, so
+//      they stream in while gate/up computes);
+//   3. phase 1: a wave owns gate rows n, n+16 (one P16 pair) and the matching
+//      up rows of one hit expert (or, for short rows, several pairs side by
+//      side); codes become bf16 pairs (128 + c) and bf16 dot2 sums them against
+//      the P16 paired activations; per unit s*acc + (z - 128 s)*sum(x), with
+//      sum(x) per unit computed once; h = silu(g)*u in bf16;
+//   4. h exchange without a grid barrier: the wave publishes each h pair word
+//      as one 64-bit relaxed atomic store of (pair, call tag) into the reserved
+//      workspace region; readers poll each word until it carries this call's
+//      tag.  A word holds its own proof of freshness, so no fence, flag or
+//      central counter sits between the last producer and the consumers;
+//   5. phase 2: h of all pairs is in LDS; wave w of a workgroup takes hits w,
+//      w+8, ... for the workgroup's output rows and accumulates w_j*y per token;
+//      the waves' partial sums are added in wave order, so the result is
+//      bit-reproducible.
 // All workgroups are co-resident (grid <= compute units, occupancy checked on
-// the host), so the barrier always completes.
+// the host), so every polled word is eventually written; the poll is bounded
+// and reports MOE_ERRW_TIMEOUT instead of hanging.
+//
+// Call tags: each workgroup slot b < kMaxGrid has a counter in the reserved
+// region.  All counters are equal between calls; workgroup b reads counter b,
+// uses tag = counter + 1 (never 0, the value of a cleared region) and stores the
+// tag into counters b, b+G, b+2G, ... of the next call right away (no other
+// workgroup of this call reads them).  A word written by an earlier call carries
+// an older tag, so it is never taken for this call's value.
 #pragma clang fp contract(off)
 
 #include "../../include/moe.h"
@@ -49,7 +61,8 @@ constexpr int kMaxPairs = 64;
 constexpr int kMaxE = 1024;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxGrid = 1024;  // arrival flags in the workspace barrier region
+constexpr int kMaxGrid = 1024;  // call-tag counters in the reserved workspace region
+constexpr int kGenBase = 64;    // dword index of counter 0
 
 struct DecodeParams {
     const float* logits;  // routing in-kernel when not null
@@ -65,12 +78,13 @@ struct DecodeParams {
     const uint8_t* pool;
     int64_t n_slots, slot_bytes, off_gu_codes, off_gu_sb, off_d_codes, off_d_sb;
     uint16_t* out;
-    uint16_t* hbuf;
-    uint32_t* bar;
+    uint32_t* gen;     // call-tag counters (reserved workspace region)
+    uint64_t* xw;      // tagged h pair words (reserved workspace region)
     uint32_t* err;
     int lpr_gu, lpr_d;
-    int rows_per_wg;  // phase-2 output rows per workgroup (multiple of 64/lpr_d)
-    int act_dw;       // dwords of the activation region of dynamic LDS
+    int rows_per_wg;   // phase-2 output rows per workgroup (multiple of 64/lpr_d)
+    int xs1_dw, h2_dw, xs2_dw, part_dw;  // dword offsets in dynamic LDS (see lds_layout)
+    int nw_q, nw_r;    // (grid waves) / (phase-1 items per hit) and remainder
     unsigned spin_limit;
 };
 
@@ -85,40 +99,79 @@ struct RowLoad {
     uint32_t sb[UPL];
 };
 
-template <int B, int UPL>
-__device__ __forceinline__ void load_row(RowLoad<B, UPL>& r, const uint32_t* __restrict__ codes_row,
-                                         const uint32_t* __restrict__ sb_row, int seg, int lpr)
+typedef uint32_t u32x2a_t __attribute__((ext_vector_type(2), aligned(4)));
+typedef uint32_t u32x3a_t __attribute__((ext_vector_type(3), aligned(4)));
+typedef uint32_t u32x4a_t __attribute__((ext_vector_type(4), aligned(4)));
+
+// The B dwords of one pack unit with as few vector loads as the size allows.
+template <int B>
+__device__ __forceinline__ void load_unit(uint32_t (&w)[B], const uint32_t* __restrict__ p)
 {
-#pragma unroll
-    for (int j = 0; j < UPL; ++j) {
-        const int u = seg + lpr * j;
-#pragma unroll
-        for (int b = 0; b < B; ++b) r.w[j][b] = codes_row[u * B + b];
-        r.sb[j] = sb_row[u >> 1];
+    if constexpr (B == 3) {
+        const u32x3a_t v = *(const u32x3a_t*)p;
+        w[0] = v.x; w[1] = v.y; w[2] = v.z;
+    } else if constexpr (B == 4) {
+        const u32x4a_t v = *(const u32x4a_t*)p;
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else if constexpr (B == 6) {
+        const u32x4a_t v = *(const u32x4a_t*)p;
+        const u32x2a_t u = *(const u32x2a_t*)(p + 4);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w; w[4] = u.x; w[5] = u.y;
+    } else {
+        static_assert(B == 8, "bits");
+        const u32x4a_t v = *(const u32x4a_t*)p;
+        const u32x4a_t u = *(const u32x4a_t*)(p + 4);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        w[4] = u.x; w[5] = u.y; w[6] = u.z; w[7] = u.w;
     }
 }
 
+// One lane's units of a weight row: codes at byte offset `codes` and scale/bias
+// at byte offset `sb` from the slot base (32-bit offsets from a wave-uniform
+// base, so the loads take the scalar-base form).
+template <int B, int UPL>
+__device__ __forceinline__ void load_row(RowLoad<B, UPL>& r, const uint8_t* __restrict__ base,
+                                         uint32_t codes, uint32_t sb, int seg, int lpr)
+{
+#pragma unroll
+    for (int j = 0; j < UPL; ++j) {
+        const uint32_t u = (uint32_t)(seg + lpr * j);
+        load_unit<B>(r.w[j], (const uint32_t*)(base + (codes + u * (uint32_t)(4 * B))));
+        r.sb[j] = *(const uint32_t*)(base + (sb + (u >> 1) * 4u));
+    }
+}
+
+// Row of phase-1 index j of a hit: consecutive indices 2m, 2m+1 are the rows of
+// one P16 pair, n and n + 16 of a 32-row chunk.
+__device__ __forceinline__ int pair_row(int j) { return (j & ~31) | ((j >> 1) & 15) | ((j & 1) << 4); }
+
 // Dot of one row's lane share (UPL units) with activations read from LDS in the
-// transposed P16 layout act[j][u] (16 dwords per unit, U units per row).
+// transposed P16 layout act[i][u] (16 dwords per unit, U units per row); xs[u]
+// holds the activations' sum over unit u (bf16 dot2 against ones, i ascending).
 template <int B, int UPL>
 __device__ __forceinline__ float row_dot(const uint32_t (&cp)[UPL][16], const float (&s)[UPL],
                                          const float (&z)[UPL], const uint32_t* __restrict__ act,
-                                         int U, int seg, int lpr)
+                                         const float* __restrict__ xs, int U, int seg, int lpr)
 {
     float y = 0.0f;
 #pragma unroll
     for (int j = 0; j < UPL; ++j) {
         const int u = seg + lpr * j;
-        float X = 0.0f, a = 0.0f;
+        float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t xv = act[i * U + u];
-            X = dot2(xv, MOE_ONES_PAIR, X);
-            a = dot2(cp[j][i], xv, a);
-        }
-        y = __builtin_fmaf(s[j], a, __builtin_fmaf(z[j], X, y));
+        for (int i = 0; i < 16; ++i) a = dot2(cp[j][i], act[i * U + u], a);
+        y = __builtin_fmaf(s[j], a, __builtin_fmaf(z[j], xs[u], y));
     }
     return y;
+}
+
+// Sum over one unit of P16 activations (16 dwords at stride U), i ascending.
+__device__ __forceinline__ float unit_sum(const uint32_t* __restrict__ act, int U)
+{
+    float X = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) X = dot2(act[i * U], MOE_ONES_PAIR, X);
+    return X;
 }
 
 template <int B, int UPL>
@@ -137,15 +190,15 @@ __device__ __forceinline__ void unpack_row(const RowLoad<B, UPL>& r, uint32_t (&
 template <int BG, int BD, int UG, int UD>
 __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
 {
-    extern __shared__ uint32_t s_dyn[];  // activations (x then h), logits, then partials
+    extern __shared__ uint32_t s_dyn[];  // x, logits, x unit sums, h, h unit sums, partials
     __shared__ int32_t s_table[kMaxE];
     __shared__ int32_t s_ids[kMaxPairs];
     __shared__ float s_w[kMaxPairs];
+    __shared__ alignas(16) int32_t s_e[kMaxPairs];
     __shared__ int32_t s_sorted[kMaxPairs];
     __shared__ int32_t s_hit[kMaxPairs];
     __shared__ int32_t s_base[kMaxPairs + 1];
-    __shared__ int32_t s_slot[kMaxPairs];
-    __shared__ const uint8_t* s_rowb[kMaxPairs];  // slot row of each hit (null: skip)
+    __shared__ int32_t s_slot[kMaxPairs];  // slot of each hit (-1: not resident, skipped)
     __shared__ int32_t s_cnt[2];  // n_hit, n_valid
     __shared__ unsigned s_gen;
     __shared__ RouteScratch s_rsc[kWaves];
@@ -156,12 +209,15 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
     const int n = T * k;
     const bool wg0 = blockIdx.x == 0;
 
-    // ---- one round of loads: barrier generation, x, slot table, routing input ----
+    // ---- one round of loads: call tag, x, slot table, routing input ----
     // x goes to LDS as P16 pairs, transposed: dword (t, i, u) at t*H/2 + i*U + u
     const int Ug = H / 32;
     uint32_t* s_act = s_dyn;
     float* s_logit = (float*)(s_dyn + T * H / 2);
-    if (tid == 0) s_gen = __hip_atomic_load(&P.bar[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float* s_xs1 = (float*)(s_dyn + P.xs1_dw);  // [t][unit] sums of x
+    uint32_t* s_h2 = s_dyn + P.h2_dw;           // h of every valid pair, transposed P16
+    float* s_xs2 = (float*)(s_dyn + P.xs2_dw);  // [pos][unit] sums of h
+    if (tid == 0) s_gen = __hip_atomic_load(&P.gen[kGenBase + blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     {
         // all loads of this round are issued before any LDS store
         constexpr int R = 4;
@@ -219,6 +275,16 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
         }
     }
     __syncthreads();
+    unsigned tag = s_gen + 1u;
+    if (tag == 0u) tag = 1u;
+    // the next call's counters: b, b+G, ... (read by no other workgroup of this call)
+    for (int j = blockIdx.x + G * tid; j < kMaxGrid; j += G * kThreads)
+        __hip_atomic_store(&P.gen[kGenBase + j], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // per-unit sums of x (read by phase 1, after the sort's barrier)
+    for (int q = tid; q < T * Ug; q += kThreads) {
+        const int t = q / Ug, u = q - t * Ug;
+        s_xs1[q] = unit_sum(s_act + t * (H / 2) + u, Ug);
+    }
 
     // ---- routing from LDS (one wave per token), identical to the router kernel ----
     if (P.logits) {
@@ -235,6 +301,10 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
     }
 
     // ---- sort the pairs by expert (stable by pair id), hit list, slots ----
+    // Lane l holds pair l's expert e; lt = pairs with a smaller expert (bit mask),
+    // dup = earlier pairs with the same expert.  Sorted position = |lt| + dup;
+    // hit index = first occurrences among lt.  Experts are read back from LDS
+    // four at a time (broadcast reads); pairs past n hold the sentinel.
     if (wave == 0) {
         int e = 0x7fffffff;  // invalid pairs sort after every expert and are dropped
         if (lane < n) {
@@ -244,37 +314,30 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
                 e = 0x7fffffff;
             }
         }
+        s_e[lane] = e;
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         const bool valid = e != 0x7fffffff;
-        int pos = 0, dup = 0;
-        for (int q0 = 0; q0 < n; q0 += 8) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int q = q0 + r;
-                if (q < n) {
-                    const int eq = __builtin_amdgcn_readlane(e, q);
-                    pos += (eq < e) ? 1 : 0;
-                    dup += (eq == e && q < lane) ? 1 : 0;
-                }
-            }
+        uint64_t lt = 0;
+        int dup = 0;
+        for (int q = 0; q < n; q += 4) {
+            const int4 eq = *(const int4*)&s_e[q];
+            lt |= (uint64_t)(eq.x < e) << q;
+            lt |= (uint64_t)(eq.y < e) << (q + 1);
+            lt |= (uint64_t)(eq.z < e) << (q + 2);
+            lt |= (uint64_t)(eq.w < e) << (q + 3);
+            dup += (eq.x == e && q < lane) ? 1 : 0;
+            dup += (eq.y == e && q + 1 < lane) ? 1 : 0;
+            dup += (eq.z == e && q + 2 < lane) ? 1 : 0;
+            dup += (eq.w == e && q + 3 < lane) ? 1 : 0;
         }
         const bool first = valid && dup == 0;
-        pos += dup;  // stable: equal experts keep pair order
+        const int pos = __popcll(lt) + dup;  // stable: equal experts keep pair order
         const unsigned long long fm = __ballot(first);
         const unsigned long long vm = __ballot(valid);
-        // hit index = distinct valid experts below e (first occurrences with a smaller expert)
-        int hidx = 0;
-        for (int q0 = 0; q0 < n; q0 += 8) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int q = q0 + r;
-                if (q < n) {
-                    const int eq = __builtin_amdgcn_readlane(e, q);
-                    hidx += ((fm >> q) & 1ull) && eq < e ? 1 : 0;
-                }
-            }
-        }
         if (valid) s_sorted[pos] = lane;
         if (first) {
+            const int hidx = __popcll(fm & lt);
             s_hit[hidx] = e;
             s_base[hidx] = pos;
             int32_t slot = s_table[e];
@@ -283,7 +346,6 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
                 slot = -1;
             }
             s_slot[hidx] = slot;
-            s_rowb[hidx] = slot >= 0 ? P.pool + (size_t)slot * (size_t)P.slot_bytes : nullptr;
         }
         const int nh = __popcll(fm);
         if (lane == 0) {
@@ -297,28 +359,53 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
 
     // ---- weight loads: phase 1 rows first, then the phase-2 rows (they do not
     //      depend on h, so they stream in while phase 1 computes) ----
+    // A hit's rows are visited in P16 pair order (index j -> row pair_row(j)).  A
+    // phase-1 item is RW = max(rpp, 2) consecutive indices -- whole pairs -- so the
+    // wave that computes it publishes its h words itself.  Wave gw takes items
+    // gw, gw + NW, ...; (hit, item in hit) advance by (nw_q, nw_r) per step.
     const int lpr = P.lpr_gu, rpp = 64 / lpr;
     const int seg = lane & (lpr - 1), rloc = lane / lpr;
-    const int n_rg1 = (I + rpp - 1) / rpp;
-    const int n_items = n_hit * n_rg1;
+    const int RW = rpp > 1 ? rpp : 2;  // pair-order indices per item
+    const int nsub = rpp > 1 ? 1 : 2;  // rows per lane per item
+    const int n_ipr = I / RW;          // items per hit
+    const int n_items = n_hit * n_ipr;
     const int gw = blockIdx.x * kWaves + wave, NW = G * kWaves;
     const size_t g_row_dw = (size_t)H * BG / 32;
-    constexpr int D1 = (64 / (2 * UG * (BG + 1))) < 1 ? 1 : ((64 / (2 * UG * (BG + 1))) > 8 ? 8 : (64 / (2 * UG * (BG + 1))));
-    RowLoad<BG, UG> gr[D1], ur[D1];
+    constexpr int D1 = (64 / (4 * UG * (BG + 1))) < 1 ? 1 : ((64 / (4 * UG * (BG + 1))) > 8 ? 8 : (64 / (4 * UG * (BG + 1))));
+    RowLoad<BG, UG> gr[D1][2], ur[D1][2];
+    int ih[D1], iii[D1], islot[D1];
+    const uint32_t g_row_b = (uint32_t)(g_row_dw * 4), g_sb_b = (uint32_t)(H / 16);  // bytes per row
+    int h_next = gw / n_ipr, ii_next = gw - (gw / n_ipr) * n_ipr;  // item at it0
     auto issue_p1 = [&](int it0) {
+        int h = h_next, ii = ii_next;
 #pragma unroll
         for (int d = 0; d < D1; ++d) {
-            const int it = it0 + d * NW;
-            if (it < n_items) {
-                const int h = it / n_rg1, rg = it - h * n_rg1;
-                const int nr = rg * rpp + rloc;
-                const uint8_t* rowb = s_rowb[h];
-                if (rowb && nr < I) {
-                    const uint32_t* cb = (const uint32_t*)(rowb + P.off_gu_codes);
-                    const uint32_t* sbb = (const uint32_t*)(rowb + P.off_gu_sb);
-                    load_row<BG, UG>(gr[d], cb + (size_t)nr * g_row_dw, sbb + (size_t)nr * (H / 64), seg, lpr);
-                    load_row<BG, UG>(ur[d], cb + (size_t)(I + nr) * g_row_dw,
-                                     sbb + (size_t)(I + nr) * (H / 64), seg, lpr);
+            ih[d] = h;
+            iii[d] = ii;
+            h += P.nw_q;
+            ii += P.nw_r;
+            if (ii >= n_ipr) {
+                ii -= n_ipr;
+                ++h;
+            }
+        }
+        h_next = h;
+        ii_next = ii;
+#pragma unroll
+        for (int d = 0; d < D1; ++d)
+            islot[d] = __builtin_amdgcn_readfirstlane(s_slot[ih[d] < kMaxPairs ? ih[d] : kMaxPairs - 1]);
+#pragma unroll
+        for (int d = 0; d < D1; ++d) {
+            if (it0 + d * NW < n_items && islot[d] >= 0) {
+                const uint8_t* base = P.pool + (size_t)islot[d] * (size_t)P.slot_bytes;
+                const uint32_t oc = (uint32_t)P.off_gu_codes, os = (uint32_t)P.off_gu_sb;
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    if (sb < nsub) {
+                        const uint32_t nr = (uint32_t)pair_row(iii[d] * RW + sb * rpp + rloc);
+                        load_row<BG, UG>(gr[d][sb], base, oc + nr * g_row_b, os + nr * g_sb_b, seg, lpr);
+                        load_row<BG, UG>(ur[d][sb], base, oc + (nr + I) * g_row_b, os + (nr + I) * g_sb_b, seg, lpr);
+                    }
                 }
             }
         }
@@ -330,117 +417,130 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
     const int Ud = I / 32;
     const int row0 = blockIdx.x * P.rows_per_wg;
     const int n_rg = P.rows_per_wg / rpp_d;   // row groups of this workgroup
-    const size_t d_row_dw = (size_t)I * BD / 32;
+    const uint32_t d_row_b = (uint32_t)(I * BD / 8), d_sb_b = (uint32_t)(I / 16);  // bytes per row
     constexpr int D2 = (64 / (UD * (BD + 1))) < 1 ? 1 : ((64 / (UD * (BD + 1))) > 8 ? 8 : (64 / (UD * (BD + 1))));
     // items of this wave: (row group rg, hit h = wave + kWaves*q), rg-major
     const int hits_w = n_hit > wave ? (n_hit - wave + kWaves - 1) / kWaves : 0;
     const int n_items2 = n_rg * hits_w;
     RowLoad<BD, UD> pre[D2];
     auto issue_p2 = [&](RowLoad<BD, UD>* dst, int d0) {
+        int rg = 0, q = d0;
+        while (q >= hits_w && hits_w > 0) {
+            q -= hits_w;
+            ++rg;
+        }
+        int hh[D2], rr[D2], sl[D2];
 #pragma unroll
         for (int d = 0; d < D2; ++d) {
-            const int it = d0 + d;
-            if (it < n_items2) {
-                const int rg = it / hits_w, h = wave + kWaves * (it - rg * hits_w);
-                const int nrow = row0 + rg * rpp_d + rloc_d;
-                const uint8_t* rowb = s_rowb[h];
-                if (rowb && nrow < H)
-                    load_row<BD, UD>(dst[d], (const uint32_t*)(rowb + P.off_d_codes) + (size_t)nrow * d_row_dw,
-                                     (const uint32_t*)(rowb + P.off_d_sb) + (size_t)nrow * (I / 64), seg_d, lpr_d);
+            hh[d] = wave + kWaves * q;
+            rr[d] = rg;
+            if (++q == hits_w) {
+                q = 0;
+                ++rg;
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < D2; ++d)
+            sl[d] = __builtin_amdgcn_readfirstlane(s_slot[hh[d] < kMaxPairs ? hh[d] : kMaxPairs - 1]);
+#pragma unroll
+        for (int d = 0; d < D2; ++d) {
+            const int nrow = row0 + rr[d] * rpp_d + rloc_d;
+            if (d0 + d < n_items2 && sl[d] >= 0 && nrow < H) {
+                const uint8_t* base = P.pool + (size_t)sl[d] * (size_t)P.slot_bytes;
+                load_row<BD, UD>(dst[d], base, (uint32_t)P.off_d_codes + (uint32_t)nrow * d_row_b,
+                                 (uint32_t)P.off_d_sb + (uint32_t)nrow * d_sb_b, seg_d, lpr_d);
             }
         }
     };
     issue_p2(pre, 0);
 
-    // ---- phase 1: gate/up + SwiGLU ----
+    // ---- phase 1: gate/up + SwiGLU -> tagged h pair words ----
+    // Publisher of an item's pair words: lane 0 (rpp = 1: the lane holds both rows
+    // of the pair), else the first lane of each even row (its odd partner row
+    // sits lpr lanes up).  A hit that is not resident publishes zeros, so the
+    // readers of its words are not kept waiting.
+    const uint64_t tag_hi = (uint64_t)tag << 32;
+    const bool pub_lane = nsub == 2 ? lane == 0 : (seg == 0 && (rloc & 1) == 0);
     for (int it0 = gw; it0 < n_items;) {
 #pragma unroll
         for (int d = 0; d < D1; ++d) {
             const int it = it0 + d * NW;
             if (it >= n_items) continue;
-            const int h = it / n_rg1, rg = it - h * n_rg1;
-            const int nr = rg * rpp + rloc;
-            if (!s_rowb[h]) continue;  // uniform per wave
-            uint32_t gp[UG][16], up[UG][16];
-            float gs[UG], gz[UG], us[UG], uz[UG];
-            unpack_row<BG, UG>(gr[d], gp, gs, gz);
-            unpack_row<BG, UG>(ur[d], up, us, uz);
-            const int pend = s_base[h + 1];
-            for (int pos = s_base[h]; pos < pend; ++pos) {
+            const int h = ih[d];
+            const int pidx = nsub == 2 ? iii[d] : ((iii[d] * RW + rloc) >> 1);
+            const int pb = s_base[h], pe = s_base[h + 1];
+            if (islot[d] < 0) {  // uniform per wave
+                if (pub_lane)
+                    for (int pos = pb; pos < pe; ++pos)
+                        __hip_atomic_store(&P.xw[(size_t)pos * (I / 2) + pidx], tag_hi, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                continue;
+            }
+            uint32_t gp[2][UG][16], up[2][UG][16];
+            float gs[2][UG], gz[2][UG], us[2][UG], uz[2][UG];
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                if (sb < nsub) {
+                    unpack_row<BG, UG>(gr[d][sb], gp[sb], gs[sb], gz[sb]);
+                    unpack_row<BG, UG>(ur[d][sb], up[sb], us[sb], uz[sb]);
+                }
+            }
+            for (int pos = pb; pos < pe; ++pos) {
                 const int t = s_sorted[pos] / k;
                 const uint32_t* act = s_act + t * (H / 2);
-                float g = row_dot<BG, UG>(gp, gs, gz, act, Ug, seg, lpr);
-                float u = row_dot<BG, UG>(up, us, uz, act, Ug, seg, lpr);
-                g = seg_sum(g, lpr);
-                u = seg_sum(u, lpr);
-                if (seg == 0 && nr < I) {
-                    const int hp = (nr & ~31) | p16_pos(nr & 31);
-                    P.hbuf[(size_t)pos * I + hp] = f32_to_bf16(silu_mul(g, u));
+                const float* xs = s_xs1 + t * Ug;
+                uint32_t hb[2] = {0u, 0u};
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    if (sb < nsub) {
+                        float g = row_dot<BG, UG>(gp[sb], gs[sb], gz[sb], act, xs, Ug, seg, lpr);
+                        float u = row_dot<BG, UG>(up[sb], us[sb], uz[sb], act, xs, Ug, seg, lpr);
+                        g = seg_sum(g, lpr);
+                        u = seg_sum(u, lpr);
+                        hb[sb] = f32_to_bf16(silu_mul(g, u));
+                    }
                 }
+                if (nsub == 1) hb[1] = (uint32_t)__shfl_xor((int)hb[0], lpr, 64);
+                if (pub_lane)
+                    __hip_atomic_store(&P.xw[(size_t)pos * (I / 2) + pidx], tag_hi | hb[0] | (hb[1] << 16),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         it0 += NW * D1;
         if (it0 < n_items) issue_p1(it0);
     }
 
-    // ---- grid barrier: per-workgroup arrival flags, one poller, one release word ----
-    // Workspace words: bar[0] = generation, bar[64 + b] = arrival flag of
-    // workgroup b.  No read-modify-write: every word has one writer.
-    __syncthreads();
-    {
-        const unsigned target = s_gen + 1u;
-        uint32_t* flags = P.bar + 64;
-        if (tid == 0) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // h is visible device-wide
-            __hip_atomic_store(&flags[blockIdx.x], target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (wg0) {
-            if (wave == 0) {
-                unsigned spins = 0;
-                for (;;) {
-                    bool mine = true;
-                    for (int j = lane; j < G; j += 64)
-                        mine = mine && __hip_atomic_load(&flags[j], __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT) == target;
-                    if (__all(mine)) break;
-                    __builtin_amdgcn_s_sleep(1);
-                    if (++spins > P.spin_limit) {
-                        if (lane == 0) flag(P.err, MOE_ERRW_TIMEOUT);
-                        break;
-                    }
-                }
-                if (lane == 0) {
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                    __hip_atomic_store(&P.bar[0], target, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-        } else if (tid == 0) {
-            unsigned spins = 0;
-            while (__hip_atomic_load(&P.bar[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != target) {
-                __builtin_amdgcn_s_sleep(1);
-                if (++spins > P.spin_limit) {
-                    flag(P.err, MOE_ERRW_TIMEOUT);
-                    break;
-                }
-            }
-        }
-        __syncthreads();
-        if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        __syncthreads();
-    }
-
-    // ---- stage h of every valid pair (transposed P16: (pos, i, u) at pos*I/2 + i*Ud + u) ----
+    // ---- stage h of every valid pair (transposed P16: (pos, i, u) at pos*I/2 + i*Ud + u),
+    //      polling each tagged word until it carries this call's tag.  Consecutive
+    //      lanes poll consecutive words (one request per 64 bytes). ----
     const int n_valid = s_cnt[1];
     {
         constexpr int R = 8;
         const int nh = n_valid * (I / 2);
-        const uint32_t* hsrc = (const uint32_t*)P.hbuf;
         for (int q0 = tid; q0 < nh; q0 += kThreads * R) {
-            uint32_t hv[R];
+            uint64_t hv[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int q = q0 + kThreads * r;
-                hv[r] = hsrc[q < nh ? q : nh - 1];
+                hv[r] = q < nh ? __hip_atomic_load(&P.xw[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag_hi;
+            }
+            unsigned spins = 0;
+            for (;;) {
+                bool ready = true;
+#pragma unroll
+                for (int r = 0; r < R; ++r) ready = ready && (uint32_t)(hv[r] >> 32) == tag;
+                if (ready) break;
+                if (++spins > P.spin_limit) {
+                    flag(P.err, MOE_ERRW_TIMEOUT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int q = q0 + kThreads * r;
+                    if ((uint32_t)(hv[r] >> 32) != tag)
+                        hv[r] = __hip_atomic_load(&P.xw[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -448,35 +548,46 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
                 if (q < nh) {
                     const int pos = q / (I / 2);
                     const int rr = q - pos * (I / 2);
-                    s_act[pos * (I / 2) + (rr & 15) * Ud + (rr >> 4)] = hv[r];
+                    s_h2[pos * (I / 2) + (rr & 15) * Ud + (rr >> 4)] = (uint32_t)hv[r];
                 }
             }
         }
     }
-    float* s_part = (float*)(s_dyn + P.act_dw);  // [wave][row][t]
+    __syncthreads();
+    // per-unit sums of h (read by phase 2)
+    for (int c = tid; c < n_valid * Ud; c += kThreads) {
+        const int pos = c / Ud, u = c - pos * Ud;
+        s_xs2[c] = unit_sum(s_h2 + pos * (I / 2) + u, Ud);
+    }
+    float* s_part = (float*)(s_dyn + P.part_dw);  // [wave][row][t]
     for (int q = tid; q < kWaves * P.rows_per_wg * T; q += kThreads) s_part[q] = 0.0f;
     __syncthreads();
 
     // ---- phase 2: down + weighted combine ----
     float* part = s_part + wave * P.rows_per_wg * T;
+    int rg_c = 0, q_c = 0;  // (row group, hit slot) of item d0 + d
     for (int d0 = 0; d0 < n_items2; d0 += D2) {
         if (d0 > 0) issue_p2(pre, d0);
         RowLoad<BD, UD>* cur = pre;
 #pragma unroll
         for (int d = 0; d < D2; ++d) {
             const int it = d0 + d;
-            if (it >= n_items2) break;
-            const int rg = it / hits_w, h = wave + kWaves * (it - rg * hits_w);
+            const int rg = rg_c, h = wave + kWaves * q_c;
+            if (++q_c == hits_w) {
+                q_c = 0;
+                ++rg_c;
+            }
+            if (it >= n_items2) continue;
             const int lrow = rg * rpp_d + rloc_d;
             const int nrow = row0 + lrow;
-            if (!s_rowb[h]) continue;
+            if (s_slot[h] < 0) continue;
             uint32_t cp[UD][16];
             float s[UD], z[UD];
             unpack_row<BD, UD>(cur[d], cp, s, z);
             const int pend = s_base[h + 1];
             for (int pos = s_base[h]; pos < pend; ++pos) {
                 const int pair = s_sorted[pos];
-                float y = row_dot<BD, UD>(cp, s, z, s_act + pos * (I / 2), Ud, seg_d, lpr_d);
+                float y = row_dot<BD, UD>(cp, s, z, s_h2 + pos * (I / 2), s_xs2 + pos * Ud, Ud, seg_d, lpr_d);
                 y = seg_sum(y, lpr_d);
                 if (seg_d == 0 && nrow < H) {
                     const int t = pair / k;
@@ -567,15 +678,23 @@ DevInfo dev_info()
     return info;
 }
 
-int act_dwords(int T, int k, int E, int H, int I)
-{
-    const int a = T * H / 2 + T * E, b = T * k * I / 2;  // phase 1: x + logits; phase 2: h
-    return a > b ? a : b;
-}
+// Dynamic LDS layout (dwords): x (T*H/2), logits (T*E), x unit sums (T*H/32),
+// staged h (n*I/2), h unit sums (n*I/32), then the phase-2 partials.
+struct LdsLayout {
+    int xs1, h2, xs2, part;
+    size_t bytes;
+};
 
-size_t dyn_lds(int T, int k, int E, int H, int I, int rows_per_wg)
+LdsLayout lds_layout(int T, int k, int E, int H, int I, int rows_per_wg)
 {
-    return (size_t)4 * act_dwords(T, k, E, H, I) + sizeof(float) * (size_t)kWaves * rows_per_wg * T;
+    LdsLayout L;
+    const int n = T * k;
+    L.xs1 = T * H / 2 + T * E;
+    L.h2 = L.xs1 + T * (H / 32);
+    L.xs2 = L.h2 + n * (I / 2);
+    L.part = L.xs2 + n * (I / 32);
+    L.bytes = (size_t)4 * L.part + sizeof(float) * (size_t)kWaves * rows_per_wg * T;
+    return L;
 }
 
 }  // namespace
@@ -593,16 +712,18 @@ bool decode_fused_supported(int T, int k, int E, const ClassView& c)
     const int rpp_d = 64 / ld;
     const int n_rg = c.H / rpp_d;
     const int rows = ((n_rg + di.cus - 1) / di.cus) * rpp_d;
+    if ((size_t)n * (c.I / 2) > (size_t)MOE_WS_XWORDS) return false;  // tagged h words
+    if (c.slot_bytes >= ((int64_t)1 << 31)) return false;                // 32-bit offsets in a slot
     const size_t static_lds = sizeof(int32_t) * (kMaxE + 7 * kMaxPairs) + sizeof(void*) * kMaxPairs +
                               sizeof(RouteScratch) * kWaves + 64;
-    return dyn_lds(T, k, E, c.H, c.I, rows) + static_lds <= di.lds_per_block;
+    return lds_layout(T, k, E, c.H, c.I, rows).bytes + static_lds <= di.lds_per_block;
 }
 
 hipError_t launch_decode_fused(const float* logits, int mode, float L, const int32_t* ids_in,
                                const float* w_in, int32_t* ids_out, float* w_out, int T, int E,
                                int k, const uint16_t* x, const int32_t* table, const uint8_t* pool,
-                               const ClassView& c, uint16_t* out, uint16_t* hbuf, uint32_t* bar,
-                               uint32_t* err, hipStream_t s)
+                               const ClassView& c, uint16_t* out, void* reserved, uint32_t* err,
+                               hipStream_t s)
 {
     int lg, ug, ld, ud;
     lanes_of(c.H / 32, &lg, &ug);
@@ -618,7 +739,8 @@ hipError_t launch_decode_fused(const float* logits, int mode, float L, const int
     int G = n_rg < di.cus ? n_rg : di.cus;
     if (G > kMaxGrid) G = kMaxGrid;
     const int rows = ((n_rg + G - 1) / G) * rpp_d;
-    const size_t lds = dyn_lds(T, k, E, c.H, c.I, rows);
+    const LdsLayout LL = lds_layout(T, k, E, c.H, c.I, rows);
+    const size_t lds = LL.bytes;
     if (v->occ(lds) < 1) return hipErrorInvalidConfiguration;
     DecodeParams P;
     P.logits = logits;
@@ -643,13 +765,20 @@ hipError_t launch_decode_fused(const float* logits, int mode, float L, const int
     P.off_d_codes = c.off_d_codes;
     P.off_d_sb = c.off_d_sb;
     P.out = out;
-    P.hbuf = hbuf;
-    P.bar = bar;
+    P.gen = (uint32_t*)reserved;
+    P.xw = (uint64_t*)((uint8_t*)reserved + MOE_WS_GEN_BYTES);
     P.err = err;
     P.lpr_gu = lg;
     P.lpr_d = ld;
     P.rows_per_wg = rows;
-    P.act_dw = act_dwords(T, k, E, c.H, c.I);
+    P.xs1_dw = LL.xs1;
+    P.h2_dw = LL.h2;
+    P.xs2_dw = LL.xs2;
+    P.part_dw = LL.part;
+    const int rpp = 64 / lg;
+    const int n_ipr = c.I / (rpp > 1 ? rpp : 2);
+    P.nw_q = G * kWaves / n_ipr;
+    P.nw_r = G * kWaves % n_ipr;
     P.spin_limit = 1u << 20;
     return v->launch(P, G, lds, s);
 }

@@ -42,14 +42,14 @@ hipError_t launch_gemv_down(int T, int k, int E, const SortView& sv, const float
 bool gemv_supported(int T, int k, const ClassView& c);
 
 // Decode path fused into one persistent launch (routing optional: logits != null).
-// `bar` points at the workspace barrier region (MOE_WS_BARRIER_BYTES, zero before
-// the first call): generation word, then one arrival flag per workgroup.
+// `reserved` points at the workspace's reserved prefix (MOE_WS_RESERVED_BYTES,
+// zero before the first call): call-tag counters, then the tagged h words.
 bool decode_fused_supported(int T, int k, int E, const ClassView& c);
 hipError_t launch_decode_fused(const float* logits, int mode, float L, const int32_t* ids_in,
                                const float* w_in, int32_t* ids_out, float* w_out, int T, int E,
                                int k, const uint16_t* x, const int32_t* table, const uint8_t* pool,
-                               const ClassView& c, uint16_t* out, uint16_t* hbuf, uint32_t* bar,
-                               uint32_t* err, hipStream_t s);
+                               const ClassView& c, uint16_t* out, void* reserved, uint32_t* err,
+                               hipStream_t s);
 
 // Prefill path: P16-permuted x, MFMA gate/up + SwiGLU, MFMA down, combine.
 hipError_t launch_permute_x(const uint16_t* x, int T, int H, uint16_t* xp, hipStream_t s);

@@ -39,15 +39,111 @@ __device__ __forceinline__ float exp_contract(float x)
     return p * __uint_as_float((uint32_t)(ni + 127) << 23);
 }
 
+// Max / min over the wave, every lane gets the result: DPP moves within rows of
+// 16 (quad xor 1, quad xor 2, half-row mirror, row mirror), then the gfx950 row
+// swaps for lane i ^ 16 and i ^ 32 (each swap returns the lane's own value and
+// its partner's, in some order).  No LDS traffic.
 __device__ __forceinline__ float wave_max_f(float v)
 {
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+    v = fmaxf(v, dpp_move<0xB1>(v));
+    v = fmaxf(v, dpp_move<0x4E>(v));
+    v = fmaxf(v, dpp_move<0x141>(v));
+    v = fmaxf(v, dpp_move<0x140>(v));
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float wave_min_f(float v)
 {
-    for (int off = 32; off > 0; off >>= 1) v = fminf(v, __shfl_xor(v, off, 64));
-    return v;
+    v = fminf(v, dpp_move<0xB1>(v));
+    v = fminf(v, dpp_move<0x4E>(v));
+    v = fminf(v, dpp_move<0x141>(v));
+    v = fminf(v, dpp_move<0x140>(v));
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// The fixed halving tree of the routing contract over one partial per lane:
+// for off = 32, 16, ..., 1 lane l adds lane l + off; the result is lane 0's.
+// Only lanes below off need a correct partner at each level: the row swaps
+// bring lane l + 32 (l + 16) to lane l, DPP row shift left by n brings lane
+// l + n within a row of 16.  Float addition is commutative, so operand order
+// inside one add does not change the rounded sum.
+__device__ __forceinline__ float tree_sum_lane0(float S)
+{
+    S = xor32_add(S);
+    S = xor16_add(S);
+    S = S + dpp_move<0x108>(S);
+    S = S + dpp_move<0x104>(S);
+    S = S + dpp_move<0x102>(S);
+    S = S + dpp_move<0x101>(S);
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(S)));
+}
+
+// k-th largest (k = 1..64) of one value per lane: a bitonic network over the 64
+// lanes sorts descending (lane 0 = largest), then lane k-1 is read.  Partner of
+// lane l at distance s is lane l ^ s: quad DPP for s = 1, 2; two row shifts
+// and a select for s = 4; row rotate by 8 for s = 8; the row swaps for 16, 32.
+__device__ __forceinline__ float p4_partner(float v, int lane)
+{
+    const float up = dpp_move<0x114>(v);  // lane l - 4 (row shift right)
+    const float dn = dpp_move<0x104>(v);  // lane l + 4 (row shift left)
+    return (lane & 4) ? up : dn;
+}
+
+__device__ __forceinline__ float wave_kth_largest(float v, int k, int lane)
+{
+#define MOE_CX(PV, S, SIZE)                                                           \
+    {                                                                                 \
+        const float pv_ = (PV);                                                       \
+        const float mx_ = fmaxf(v, pv_), mn_ = fminf(v, pv_);                         \
+        const bool lo_ = (lane & (S)) == 0, dsc_ = (lane & (SIZE)) == 0;              \
+        v = (lo_ == dsc_) ? mx_ : mn_;                                                \
+    }
+// both moves run with the full wave (a DPP source lane must be active), then select
+#define MOE_P4(V) p4_partner(V, lane)
+#define MOE_SW16(SIZE)                                                                \
+    {                                                                                 \
+        auto r_ = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false); \
+        const float a_ = __uint_as_float(r_[0]), b_ = __uint_as_float(r_[1]);        \
+        const bool lo_ = (lane & 16) == 0, dsc_ = (lane & (SIZE)) == 0;               \
+        v = (lo_ == dsc_) ? fmaxf(a_, b_) : fminf(a_, b_);                            \
+    }
+#define MOE_SW32()                                                                    \
+    {                                                                                 \
+        auto r_ = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false); \
+        const float a_ = __uint_as_float(r_[0]), b_ = __uint_as_float(r_[1]);        \
+        v = (lane & 32) == 0 ? fmaxf(a_, b_) : fminf(a_, b_);                         \
+    }
+    MOE_CX(dpp_move<0xB1>(v), 1, 2)
+    MOE_CX(dpp_move<0x4E>(v), 2, 4)
+    MOE_CX(dpp_move<0xB1>(v), 1, 4)
+    MOE_CX(MOE_P4(v), 4, 8)
+    MOE_CX(dpp_move<0x4E>(v), 2, 8)
+    MOE_CX(dpp_move<0xB1>(v), 1, 8)
+    MOE_CX(dpp_move<0x128>(v), 8, 16)
+    MOE_CX(MOE_P4(v), 4, 16)
+    MOE_CX(dpp_move<0x4E>(v), 2, 16)
+    MOE_CX(dpp_move<0xB1>(v), 1, 16)
+    MOE_SW16(32)
+    MOE_CX(dpp_move<0x128>(v), 8, 32)
+    MOE_CX(MOE_P4(v), 4, 32)
+    MOE_CX(dpp_move<0x4E>(v), 2, 32)
+    MOE_CX(dpp_move<0xB1>(v), 1, 32)
+    MOE_SW32()
+    MOE_SW16(64)
+    MOE_CX(dpp_move<0x128>(v), 8, 64)
+    MOE_CX(MOE_P4(v), 4, 64)
+    MOE_CX(dpp_move<0x4E>(v), 2, 64)
+    MOE_CX(dpp_move<0xB1>(v), 1, 64)
+#undef MOE_CX
+#undef MOE_P4
+#undef MOE_SW16
+#undef MOE_SW32
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k - 1));
 }
 
 // DPP lane moves within rows of 16 (gfx9 encodings).
@@ -109,7 +205,7 @@ __device__ __forceinline__ void wave_first(float& k, int& i)
 // the winning lane drops its head.  The order is total (key desc, id asc), so
 // the result equals repeated argmax over all E experts.
 // Per-wave LDS scratch of route_token: candidates and the chosen k.
-struct RouteScratch {
+struct alignas(16) RouteScratch {
     float ck[64];
     int ci[64];
     float cp[64];
@@ -118,7 +214,7 @@ struct RouteScratch {
 };
 
 template <int MJ>
-__device__ __forceinline__ bool route_token_t(const float* __restrict__ lr, int E, int k, int mode,
+__device__ __attribute__((noinline)) bool route_token_t(const float* __restrict__ lr, int E, int k, int mode,
                                               float L, const int32_t* __restrict__ table, int lane,
                                               int32_t* ids, float* w, RouteScratch* sc)
 {
@@ -158,8 +254,7 @@ __device__ __forceinline__ bool route_token_t(const float* __restrict__ lr, int 
         v[j] = (i < E) ? exp_contract(v[j] - m) : 0.0f;
         S = S + v[j];
     }
-    for (int off = 32; off > 0; off >>= 1) S = S + __shfl_down(S, off, 64);
-    const float Z = __shfl(S, 0, 64);
+    const float Z = tree_sum_lane0(S);
 
     // probabilities and selection keys (invalid entries: key -inf, never chosen)
     float key[MJ];
@@ -209,17 +304,7 @@ __device__ __forceinline__ bool route_token_t(const float* __restrict__ lr, int 
                 hk = key[j];
                 hid = id[j];
             }
-        const uint32_t hu = hk >= 0.0f ? __float_as_uint(hk) : 0u;  // keys are >= 0
-        uint32_t prefix = 0;
-        int need = k;
-        for (int bit = 30; bit >= 0; --bit) {
-            const uint32_t msk = 0xFFFFFFFFu << bit;
-            const uint32_t want = prefix | (1u << bit);
-            const int cnt = __popcll(__ballot((hu & msk) == want));
-            if (cnt >= need) prefix = want;
-            else need -= cnt;
-        }
-        const float tau = __uint_as_float(prefix);
+        const float tau = wave_kth_largest(hk, k, lane);
         unsigned long long cm[MJ];
         int total = 0;
 #pragma unroll
@@ -249,11 +334,15 @@ __device__ __forceinline__ bool route_token_t(const float* __restrict__ lr, int 
                 mi = sc->ci[lane];
                 mp = sc->cp[lane];
             }
+            // rank = candidates ahead of this one; four per LDS read (broadcast)
             int rank = 0;
-            for (int q = 0; q < total; ++q) {
-                const float qk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mk), q));
-                const int qi = __builtin_amdgcn_readlane(mi, q);
-                rank += precedes(qk, qi, mk, mi) ? 1 : 0;
+            for (int q = 0; q < total; q += 4) {
+                const float4 qk = *(const float4*)&sc->ck[q];
+                const int4 qi = *(const int4*)&sc->ci[q];
+                rank += (precedes(qk.x, qi.x, mk, mi) ? 1 : 0);
+                rank += (q + 1 < total && precedes(qk.y, qi.y, mk, mi)) ? 1 : 0;
+                rank += (q + 2 < total && precedes(qk.z, qi.z, mk, mi)) ? 1 : 0;
+                rank += (q + 3 < total && precedes(qk.w, qi.w, mk, mi)) ? 1 : 0;
             }
             if (lane < total && rank < k) {
                 sc->sel_id[rank] = mi;
@@ -261,8 +350,20 @@ __device__ __forceinline__ bool route_token_t(const float* __restrict__ lr, int 
             }
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            // renormalise: the chosen probabilities summed left to right
+            float sp[32];
+#pragma unroll
+            for (int r = 0; r < 32; r += 4) {
+                const float4 q4 = *(const float4*)&sc->sel_p[r];
+                sp[r] = q4.x;
+                sp[r + 1] = q4.y;
+                sp[r + 2] = q4.z;
+                sp[r + 3] = q4.w;
+            }
             float s = 0.0f;
-            for (int r = 0; r < k; ++r) s = s + sc->sel_p[r];
+#pragma unroll
+            for (int r = 0; r < 32; ++r)
+                if (r < k) s = s + sp[r];
             if (lane < k) {
                 ids[lane] = sc->sel_id[lane];
                 w[lane] = __fdiv_rn(sc->sel_p[lane], s);
