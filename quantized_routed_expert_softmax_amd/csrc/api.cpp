@@ -291,7 +291,8 @@ int moe_layer_forward(const float* logits, int T, int E, int k, int mode, float 
     const FwdLayout Lw = fwd_layout(T, k, E, d);
     if (ws_bytes < Lw.total) return fail(MOE_E_WORKSPACE, "forward workspace %zu bytes < %zu", ws_bytes, Lw.total);
     const moe::ClassView c = view_of(d);
-    if (moe::decode_fused_supported(T, k, E, c)) {
+    // in-kernel routing covers E <= 512; larger E routes with the router kernel first
+    if (E <= 512 && moe::decode_fused_supported(T, k, E, c)) {
         char* w = (char*)ws;
         hipError_t e = moe::launch_decode_fused(logits, mode, L, nullptr, nullptr, topk_ids, topk_w, T, E,
                                                 k, (const uint16_t*)x, slot_table, (const uint8_t*)slot_pool,

@@ -145,32 +145,60 @@ __device__ __forceinline__ void load_row(RowLoad<B, UPL>& r, const uint8_t* __re
 // one P16 pair, n and n + 16 of a 32-row chunk.
 __device__ __forceinline__ int pair_row(int j) { return (j & ~31) | ((j >> 1) & 15) | ((j & 1) << 4); }
 
-// Dot of one row's lane share (UPL units) with activations read from LDS in the
-// transposed P16 layout act[i][u] (16 dwords per unit, U units per row); xs[u]
-// holds the activations' sum over unit u (bf16 dot2 against ones, i ascending).
-template <int B, int UPL>
-__device__ __forceinline__ float row_dot(const uint32_t (&cp)[UPL][16], const float (&s)[UPL],
-                                         const float (&z)[UPL], const uint32_t* __restrict__ act,
-                                         const float* __restrict__ xs, int U, int seg, int lpr)
+// LDS layout of a row of P16 activations: the 16 dwords of unit u are contiguous
+// (dwords 16u..16u+15), in four 16-byte chunks whose order is rotated by an XOR
+// with (u >> 2) & 3, so 16 lanes reading chunk c of units u..u+15 touch 64
+// distinct banks.  Dword i of unit u sits at swz(u, i).
+__device__ __forceinline__ int swz(int u, int i) { return 16 * u + ((((i >> 2) ^ (u >> 2)) & 3) << 2) + (i & 3); }
+
+// The 16 dwords of unit u, in order, with four 16-byte LDS reads.
+__device__ __forceinline__ void load_unit_act(const uint32_t* __restrict__ row, int u, uint32_t (&a)[16])
 {
+    const uint32_t* base = row + 16 * u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint4 v = *(const uint4*)(base + (((c ^ (u >> 2)) & 3) << 2));
+        a[4 * c] = v.x;
+        a[4 * c + 1] = v.y;
+        a[4 * c + 2] = v.z;
+        a[4 * c + 3] = v.w;
+    }
+}
+
+// Dot of one row's lane share (UPL units) with a row of activations in LDS
+// (layout swz); each unit is unpacked right before its dot product, so only
+// one unit's 16 pairs are live at a time.  xs[u] is the activations' sum over
+// unit u.  Per unit: s*acc + (z - off*s)*xs.
+template <int B, int UPL>
+__device__ __forceinline__ float row_dot_raw(const RowLoad<B, UPL>& r, const uint32_t* __restrict__ act,
+                                             const float* __restrict__ xs, int seg, int lpr)
+{
+    constexpr float off = Code<B>::offset;
     float y = 0.0f;
 #pragma unroll
     for (int j = 0; j < UPL; ++j) {
         const int u = seg + lpr * j;
-        float a = 0.0f;
+        uint32_t av[16], cp[16];
+        load_unit_act(act, u, av);
+        unit_pairs<B>(r.w[j], cp);
+        const float s = half_bits_to_f32(r.sb[j] & 0xFFFFu);
+        const float z = __builtin_fmaf(-off, s, half_bits_to_f32(r.sb[j] >> 16));
+        float acc = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) a = dot2(cp[j][i], act[i * U + u], a);
-        y = __builtin_fmaf(s[j], a, __builtin_fmaf(z[j], xs[u], y));
+        for (int i = 0; i < 16; ++i) acc = dot2(cp[i], av[i], acc);
+        y = __builtin_fmaf(s, acc, __builtin_fmaf(z, xs[u], y));
     }
     return y;
 }
 
-// Sum over one unit of P16 activations (16 dwords at stride U), i ascending.
-__device__ __forceinline__ float unit_sum(const uint32_t* __restrict__ act, int U)
+// Sum over unit u of a row of P16 activations (bf16 dot2 against ones, i ascending).
+__device__ __forceinline__ float unit_sum(const uint32_t* __restrict__ row, int u)
 {
+    uint32_t av[16];
+    load_unit_act(row, u, av);
     float X = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) X = dot2(act[i * U], MOE_ONES_PAIR, X);
+    for (int i = 0; i < 16; ++i) X = dot2(av[i], MOE_ONES_PAIR, X);
     return X;
 }
 
@@ -190,7 +218,7 @@ __device__ __forceinline__ void unpack_row(const RowLoad<B, UPL>& r, uint32_t (&
 template <int BG, int BD, int UG, int UD>
 __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
 {
-    extern __shared__ uint32_t s_dyn[];  // x, logits, x unit sums, h, h unit sums, partials
+    extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // x, logits, x unit sums, h, h unit sums, partials
     __shared__ int32_t s_table[kMaxE];
     __shared__ int32_t s_ids[kMaxPairs];
     __shared__ float s_w[kMaxPairs];
@@ -202,6 +230,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
     __shared__ int32_t s_cnt[2];  // n_hit, n_valid
     __shared__ unsigned s_gen;
     __shared__ RouteScratch s_rsc[kWaves];
+    __shared__ RouteWgScratch<kWaves> s_rwg;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = gridDim.x;
@@ -210,12 +239,12 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
     const bool wg0 = blockIdx.x == 0;
 
     // ---- one round of loads: call tag, x, slot table, routing input ----
-    // x goes to LDS as P16 pairs, transposed: dword (t, i, u) at t*H/2 + i*U + u
+    // x goes to LDS as P16 pairs, unit-contiguous (layout swz)
     const int Ug = H / 32;
     uint32_t* s_act = s_dyn;
     float* s_logit = (float*)(s_dyn + T * H / 2);
     float* s_xs1 = (float*)(s_dyn + P.xs1_dw);  // [t][unit] sums of x
-    uint32_t* s_h2 = s_dyn + P.h2_dw;           // h of every valid pair, transposed P16
+    uint32_t* s_h2 = s_dyn + P.h2_dw;           // h of every valid pair (P16, layout swz)
     float* s_xs2 = (float*)(s_dyn + P.xs2_dw);  // [pos][unit] sums of h
     if (tid == 0) s_gen = __hip_atomic_load(&P.gen[kGenBase + blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     {
@@ -240,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
                 if (q < nx) {
                     const int t = q / (H / 2);
                     const int rr = q - t * (H / 2);
-                    s_act[t * (H / 2) + (rr & 15) * Ug + (rr >> 4)] = lo[r] | (hi[r] << 16);
+                    s_act[t * (H / 2) + swz(rr >> 4, rr & 15)] = lo[r] | (hi[r] << 16);
                 }
             }
         }
@@ -283,15 +312,24 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
     // per-unit sums of x (read by phase 1, after the sort's barrier)
     for (int q = tid; q < T * Ug; q += kThreads) {
         const int t = q / Ug, u = q - t * Ug;
-        s_xs1[q] = unit_sum(s_act + t * (H / 2) + u, Ug);
+        s_xs1[q] = unit_sum(s_act + t * (H / 2), u);
     }
 
     // ---- routing from LDS (one wave per token), identical to the router kernel ----
+    // (few tokens: all waves route each token together; more: one wave per token)
     if (P.logits) {
-        for (int t = wave; t < T; t += kWaves) {
-            const bool ok = route_token(s_logit + t * E, E, k, P.mode, P.L, s_table, lane,
-                                        s_ids + t * k, s_w + t * k, &s_rsc[wave]);
-            if (!ok && wg0 && lane == 0) flag(P.err, MOE_ERRW_NONFINITE);
+        if (T <= 3 && E >= 64) {
+            for (int t = 0; t < T; ++t) {
+                const bool ok = route_token_wg<kWaves>(s_logit + t * E, E, k, P.mode, P.L, s_table,
+                                                       s_ids + t * k, s_w + t * k, &s_rsc[0], &s_rwg);
+                if (!ok && wg0 && tid == 0) flag(P.err, MOE_ERRW_NONFINITE);
+            }
+        } else {
+            for (int t = wave; t < T; t += kWaves) {
+                const bool ok = route_token_512(s_logit + t * E, E, k, P.mode, P.L, s_table, lane,
+                                                s_ids + t * k, s_w + t * k, &s_rsc[wave]);
+                if (!ok && wg0 && lane == 0) flag(P.err, MOE_ERRW_NONFINITE);
+            }
         }
         __syncthreads();
         if (wg0 && P.ids_out && tid < n) {
@@ -357,8 +395,8 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
     __syncthreads();
     const int n_hit = s_cnt[0];
 
-    // ---- weight loads: phase 1 rows first, then the phase-2 rows (they do not
-    //      depend on h, so they stream in while phase 1 computes) ----
+    // ---- weight loads: phase 1 rows now, the phase-2 rows once phase 1 is done
+    //      (they do not depend on h, so they stream in during the h exchange) ----
     // A hit's rows are visited in P16 pair order (index j -> row pair_row(j)).  A
     // phase-1 item is RW = max(rpp, 2) consecutive indices -- whole pairs -- so the
     // wave that computes it publishes its h words itself.  Wave gw takes items
@@ -419,32 +457,34 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
     const int n_rg = P.rows_per_wg / rpp_d;   // row groups of this workgroup
     const uint32_t d_row_b = (uint32_t)(I * BD / 8), d_sb_b = (uint32_t)(I / 16);  // bytes per row
     constexpr int D2 = (64 / (UD * (BD + 1))) < 1 ? 1 : ((64 / (UD * (BD + 1))) > 8 ? 8 : (64 / (UD * (BD + 1))));
-    // items of this wave: (row group rg, hit h = wave + kWaves*q), rg-major
-    const int hits_w = n_hit > wave ? (n_hit - wave + kWaves - 1) / kWaves : 0;
-    const int n_items2 = n_rg * hits_w;
+    // phase-2 items of the workgroup: (row group, hit), i = rg * n_hit + hit; wave w
+    // takes i = w, w + kWaves, ... (balanced to within one item per wave)
+    const int n_all2 = n_rg * n_hit;
+    const int n_items2 = n_all2 > wave ? (n_all2 - wave + kWaves - 1) / kWaves : 0;
     RowLoad<BD, UD> pre[D2];
+    int hh2[D2], rr2[D2];
+    int h2_next = n_hit > 0 ? wave % n_hit : 0, rg2_next = n_hit > 0 ? wave / n_hit : 0;
     auto issue_p2 = [&](RowLoad<BD, UD>* dst, int d0) {
-        int rg = 0, q = d0;
-        while (q >= hits_w && hits_w > 0) {
-            q -= hits_w;
-            ++rg;
-        }
-        int hh[D2], rr[D2], sl[D2];
+        int h = h2_next, rg = rg2_next;
 #pragma unroll
         for (int d = 0; d < D2; ++d) {
-            hh[d] = wave + kWaves * q;
-            rr[d] = rg;
-            if (++q == hits_w) {
-                q = 0;
+            hh2[d] = h;
+            rr2[d] = rg;
+            h += kWaves;
+            while (h >= n_hit && n_hit > 0) {
+                h -= n_hit;
                 ++rg;
             }
         }
+        h2_next = h;
+        rg2_next = rg;
+        int sl[D2];
 #pragma unroll
         for (int d = 0; d < D2; ++d)
-            sl[d] = __builtin_amdgcn_readfirstlane(s_slot[hh[d] < kMaxPairs ? hh[d] : kMaxPairs - 1]);
+            sl[d] = __builtin_amdgcn_readfirstlane(s_slot[hh2[d] < kMaxPairs ? hh2[d] : kMaxPairs - 1]);
 #pragma unroll
         for (int d = 0; d < D2; ++d) {
-            const int nrow = row0 + rr[d] * rpp_d + rloc_d;
+            const int nrow = row0 + rr2[d] * rpp_d + rloc_d;
             if (d0 + d < n_items2 && sl[d] >= 0 && nrow < H) {
                 const uint8_t* base = P.pool + (size_t)sl[d] * (size_t)P.slot_bytes;
                 load_row<BD, UD>(dst[d], base, (uint32_t)P.off_d_codes + (uint32_t)nrow * d_row_b,
@@ -452,7 +492,6 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
             }
         }
     };
-    issue_p2(pre, 0);
 
     // ---- phase 1: gate/up + SwiGLU -> tagged h pair words ----
     // Publisher of an item's pair words: lane 0 (rpp = 1: the lane holds both rows
@@ -476,15 +515,6 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
                                            __HIP_MEMORY_SCOPE_AGENT);
                 continue;
             }
-            uint32_t gp[2][UG][16], up[2][UG][16];
-            float gs[2][UG], gz[2][UG], us[2][UG], uz[2][UG];
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                if (sb < nsub) {
-                    unpack_row<BG, UG>(gr[d][sb], gp[sb], gs[sb], gz[sb]);
-                    unpack_row<BG, UG>(ur[d][sb], up[sb], us[sb], uz[sb]);
-                }
-            }
             for (int pos = pb; pos < pe; ++pos) {
                 const int t = s_sorted[pos] / k;
                 const uint32_t* act = s_act + t * (H / 2);
@@ -493,8 +523,8 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb) {
                     if (sb < nsub) {
-                        float g = row_dot<BG, UG>(gp[sb], gs[sb], gz[sb], act, xs, Ug, seg, lpr);
-                        float u = row_dot<BG, UG>(up[sb], us[sb], uz[sb], act, xs, Ug, seg, lpr);
+                        float g = row_dot_raw<BG, UG>(gr[d][sb], act, xs, seg, lpr);
+                        float u = row_dot_raw<BG, UG>(ur[d][sb], act, xs, seg, lpr);
                         g = seg_sum(g, lpr);
                         u = seg_sum(u, lpr);
                         hb[sb] = f32_to_bf16(silu_mul(g, u));
@@ -510,7 +540,10 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
         if (it0 < n_items) issue_p1(it0);
     }
 
-    // ---- stage h of every valid pair (transposed P16: (pos, i, u) at pos*I/2 + i*Ud + u),
+    // the phase-2 rows stream in while h is exchanged (they do not depend on h)
+    issue_p2(pre, 0);
+
+    // ---- stage h of every valid pair (P16, unit-contiguous: layout swz),
     //      polling each tagged word until it carries this call's tag.  Consecutive
     //      lanes poll consecutive words (one request per 64 bytes). ----
     const int n_valid = s_cnt[1];
@@ -548,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
                 if (q < nh) {
                     const int pos = q / (I / 2);
                     const int rr = q - pos * (I / 2);
-                    s_h2[pos * (I / 2) + (rr & 15) * Ud + (rr >> 4)] = (uint32_t)hv[r];
+                    s_h2[pos * (I / 2) + swz(rr >> 4, rr & 15)] = (uint32_t)hv[r];
                 }
             }
         }
@@ -557,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
     // per-unit sums of h (read by phase 2)
     for (int c = tid; c < n_valid * Ud; c += kThreads) {
         const int pos = c / Ud, u = c - pos * Ud;
-        s_xs2[c] = unit_sum(s_h2 + pos * (I / 2) + u, Ud);
+        s_xs2[c] = unit_sum(s_h2 + pos * (I / 2), u);
     }
     float* s_part = (float*)(s_dyn + P.part_dw);  // [wave][row][t]
     for (int q = tid; q < kWaves * P.rows_per_wg * T; q += kThreads) s_part[q] = 0.0f;
@@ -565,29 +598,21 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
 
     // ---- phase 2: down + weighted combine ----
     float* part = s_part + wave * P.rows_per_wg * T;
-    int rg_c = 0, q_c = 0;  // (row group, hit slot) of item d0 + d
     for (int d0 = 0; d0 < n_items2; d0 += D2) {
         if (d0 > 0) issue_p2(pre, d0);
         RowLoad<BD, UD>* cur = pre;
 #pragma unroll
         for (int d = 0; d < D2; ++d) {
             const int it = d0 + d;
-            const int rg = rg_c, h = wave + kWaves * q_c;
-            if (++q_c == hits_w) {
-                q_c = 0;
-                ++rg_c;
-            }
+            const int rg = rr2[d], h = hh2[d];
             if (it >= n_items2) continue;
             const int lrow = rg * rpp_d + rloc_d;
             const int nrow = row0 + lrow;
             if (s_slot[h] < 0) continue;
-            uint32_t cp[UD][16];
-            float s[UD], z[UD];
-            unpack_row<BD, UD>(cur[d], cp, s, z);
             const int pend = s_base[h + 1];
             for (int pos = s_base[h]; pos < pend; ++pos) {
                 const int pair = s_sorted[pos];
-                float y = row_dot<BD, UD>(cp, s, z, s_h2 + pos * (I / 2), s_xs2 + pos * Ud, Ud, seg_d, lpr_d);
+                float y = row_dot_raw<BD, UD>(cur[d], s_h2 + pos * (I / 2), s_xs2 + pos * Ud, seg_d, lpr_d);
                 y = seg_sum(y, lpr_d);
                 if (seg_d == 0 && nrow < H) {
                     const int t = pair / k;
@@ -689,10 +714,11 @@ LdsLayout lds_layout(int T, int k, int E, int H, int I, int rows_per_wg)
 {
     LdsLayout L;
     const int n = T * k;
-    L.xs1 = T * H / 2 + T * E;
-    L.h2 = L.xs1 + T * (H / 32);
-    L.xs2 = L.h2 + n * (I / 2);
-    L.part = L.xs2 + n * (I / 32);
+    auto up4 = [](int v) { return (v + 3) & ~3; };  // 16-byte aligned regions
+    L.xs1 = up4(T * H / 2 + T * E);
+    L.h2 = up4(L.xs1 + T * (H / 32));
+    L.xs2 = up4(L.h2 + n * (I / 2));
+    L.part = up4(L.xs2 + n * (I / 32));
     L.bytes = (size_t)4 * L.part + sizeof(float) * (size_t)kWaves * rows_per_wg * T;
     return L;
 }
@@ -714,8 +740,8 @@ bool decode_fused_supported(int T, int k, int E, const ClassView& c)
     const int rows = ((n_rg + di.cus - 1) / di.cus) * rpp_d;
     if ((size_t)n * (c.I / 2) > (size_t)MOE_WS_XWORDS) return false;  // tagged h words
     if (c.slot_bytes >= ((int64_t)1 << 31)) return false;                // 32-bit offsets in a slot
-    const size_t static_lds = sizeof(int32_t) * (kMaxE + 7 * kMaxPairs) + sizeof(void*) * kMaxPairs +
-                              sizeof(RouteScratch) * kWaves + 64;
+    const size_t static_lds = sizeof(int32_t) * (kMaxE + 8 * kMaxPairs) + sizeof(RouteScratch) * kWaves +
+                              sizeof(RouteWgScratch<kWaves>) + 64;
     return lds_layout(T, k, E, c.H, c.I, rows).bytes + static_lds <= di.lds_per_block;
 }
 

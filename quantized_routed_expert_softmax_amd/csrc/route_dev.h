@@ -159,9 +159,11 @@ __device__ __forceinline__ float dpp_f(float v)
 }
 
 // (key, id) precedes (ok, oi) in the selection order: larger key, then smaller id.
+// Bitwise, not short-circuit: both operands are always evaluated, so the loads
+// that feed them are never moved under a branch.
 __device__ __forceinline__ bool precedes(float k, int i, float ok, int oi)
 {
-    return k > ok || (k == ok && i < oi);
+    return (k > ok) | ((k == ok) & (i < oi));
 }
 
 // Wave-wide first element in (key desc, id asc) order over one (key, id) per lane:
@@ -206,12 +208,67 @@ __device__ __forceinline__ void wave_first(float& k, int& i)
 // the result equals repeated argmax over all E experts.
 // Per-wave LDS scratch of route_token: candidates and the chosen k.
 struct alignas(16) RouteScratch {
-    float ck[64];
-    int ci[64];
-    float cp[64];
+    uint64_t ck[64];  // candidate order keys (order_key)
+    float cp[64];     // candidate probabilities
     int sel_id[32];
     float sel_p[32];
 };
+
+// Candidate order key: selection keys are finite and >= 0, so their bit patterns
+// order like their values; the low word ~id puts the smaller id first among
+// equal keys.  A larger order key precedes a smaller one.
+__device__ __forceinline__ uint64_t order_key(float key, int id)
+{
+    return ((uint64_t)__float_as_uint(key) << 32) | (uint32_t)~id;
+}
+
+// Rank the `total` (<= 64) candidates held in sc->ck/cp (one per lane) in the
+// selection order (key desc, id asc), keep the first k, and write ids/w from
+// lanes 0..k-1: w_r = p_r / (sum of the chosen p in rank order, left to right).
+// One wave; the candidates must already be visible to it.
+__device__ __forceinline__ void rank_select(RouteScratch* sc, int total, int k, int lane, int32_t* ids, float* w)
+{
+    const uint64_t mk = lane < total ? sc->ck[lane] : 0ull;
+    const float mp = lane < total ? sc->cp[lane] : 0.0f;
+    if (lane < 32) sc->sel_p[lane] = 0.0f;
+    // rank = candidates ahead of this one (64-bit compares, two per LDS read)
+    int rank = 0;
+    for (int q = 0; q < total; q += 4) {
+        const ulonglong2 a = *(const ulonglong2*)&sc->ck[q];
+        const ulonglong2 b = *(const ulonglong2*)&sc->ck[q + 2];
+        rank += (int)(a.x > mk);
+        rank += (int)((q + 1 < total) & (a.y > mk));
+        rank += (int)((q + 2 < total) & (b.x > mk));
+        rank += (int)((q + 3 < total) & (b.y > mk));
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    if (lane < total && rank < k) {
+        sc->sel_id[rank] = (int)~(uint32_t)mk;
+        sc->sel_p[rank] = mp;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // renormalise: the chosen probabilities summed left to right (entries past k
+    // are +0, which leaves a positive sum unchanged)
+    float s = 0.0f;
+    for (int r = 0; r < k; r += 8) {
+        const float4 a = *(const float4*)&sc->sel_p[r];
+        const float4 b = *(const float4*)&sc->sel_p[r + 4];
+        s = s + a.x;
+        s = s + a.y;
+        s = s + a.z;
+        s = s + a.w;
+        s = s + b.x;
+        s = s + b.y;
+        s = s + b.z;
+        s = s + b.w;
+    }
+    if (lane < k) {
+        ids[lane] = sc->sel_id[lane];
+        w[lane] = __fdiv_rn(sc->sel_p[lane], s);
+    }
+}
 
 template <int MJ>
 __device__ __attribute__((noinline)) bool route_token_t(const float* __restrict__ lr, int E, int k, int mode,
@@ -319,55 +376,14 @@ __device__ __attribute__((noinline)) bool route_token_t(const float* __restrict_
                 if ((cm[j] >> lane) & 1ull) {
                     const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(cm[j] >> 32),
                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)cm[j], 0u));
-                    sc->ck[pos] = key[j];
-                    sc->ci[pos] = id[j];
+                    sc->ck[pos] = order_key(key[j], id[j]);
                     sc->cp[pos] = v[j];
                 }
                 base += __popcll(cm[j]);
             }
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            float mk = -INFINITY, mp = 0.0f;
-            int mi = 0x7fffffff;
-            if (lane < total) {
-                mk = sc->ck[lane];
-                mi = sc->ci[lane];
-                mp = sc->cp[lane];
-            }
-            // rank = candidates ahead of this one; four per LDS read (broadcast)
-            int rank = 0;
-            for (int q = 0; q < total; q += 4) {
-                const float4 qk = *(const float4*)&sc->ck[q];
-                const int4 qi = *(const int4*)&sc->ci[q];
-                rank += (precedes(qk.x, qi.x, mk, mi) ? 1 : 0);
-                rank += (q + 1 < total && precedes(qk.y, qi.y, mk, mi)) ? 1 : 0;
-                rank += (q + 2 < total && precedes(qk.z, qi.z, mk, mi)) ? 1 : 0;
-                rank += (q + 3 < total && precedes(qk.w, qi.w, mk, mi)) ? 1 : 0;
-            }
-            if (lane < total && rank < k) {
-                sc->sel_id[rank] = mi;
-                sc->sel_p[rank] = mp;
-            }
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            // renormalise: the chosen probabilities summed left to right
-            float sp[32];
-#pragma unroll
-            for (int r = 0; r < 32; r += 4) {
-                const float4 q4 = *(const float4*)&sc->sel_p[r];
-                sp[r] = q4.x;
-                sp[r + 1] = q4.y;
-                sp[r + 2] = q4.z;
-                sp[r + 3] = q4.w;
-            }
-            float s = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 32; ++r)
-                if (r < k) s = s + sp[r];
-            if (lane < k) {
-                ids[lane] = sc->sel_id[lane];
-                w[lane] = __fdiv_rn(sc->sel_p[lane], s);
-            }
+            rank_select(sc, total, k, lane, ids, w);
             return true;
         }
     }
@@ -431,6 +447,147 @@ __device__ __attribute__((noinline)) bool route_token_t(const float* __restrict_
         w[lane] = __fdiv_rn(my_p, s);
     }
     return true;
+}
+
+// LDS scratch of route_token_wg for W waves.
+template <int W>
+struct alignas(16) RouteWgScratch {
+    float top[64 + 4];  // per-wave top keys (wave w: [w*r, w*r + r)), padded for vector reads
+    float red[3][W];    // per-wave max of the logits, max and min of p
+    int bad[W];
+    float tau;
+    int count;          // candidates placed so far
+    float v[64 * W];    // e_i by expert
+};
+
+// Route one token with all W waves of a workgroup (64 <= E <= 64*W): lane l of
+// wave w holds expert 64w + l.  Every thread of the workgroup calls it with the
+// same arguments (it contains workgroup barriers); ids/w are written by wave 0.
+// The arithmetic is the single-wave routine's, step for step: exact max; the
+// same exp; lane partials S_l = sum over j ascending of e_{l+64j}, then the same
+// halving tree; correctly rounded p; the same keys and selection order.  Only the
+// candidate threshold is found differently: each of the Wf = E/64 full waves
+// lists its r largest keys, r = ceil(k/Wf); these are Wf*r >= k keys of distinct
+// experts, so their k-th largest, tau, is at most the k-th largest key overall
+// and every chosen expert has key >= tau.  Candidates (key >= tau) are ranked
+// by (key desc, id asc), which does not depend on the order they were stored in.
+template <int W>
+__device__ bool route_token_wg(const float* __restrict__ lr, int E, int k, int mode, float L,
+                               const int32_t* __restrict__ table, int32_t* ids, float* w,
+                               RouteScratch* sc0, RouteWgScratch<W>* ws)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = wave * 64 + lane;
+    const bool valid = e < E;
+    const float l = valid ? lr[e] : -INFINITY;
+    const bool bad = valid && !isfinite(l);
+    const float mw = wave_max_f(l);
+    const bool anybad = __any(bad);
+    if (lane == 0) {
+        ws->red[0][wave] = mw;
+        ws->bad[wave] = anybad ? 1 : 0;
+    }
+    __syncthreads();
+    float m = -INFINITY;
+    int nb = 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+        m = fmaxf(m, ws->red[0][i]);
+        nb |= ws->bad[i];
+    }
+    if (nb) {
+        if (wave == 0 && lane < k) {
+            ids[lane] = lane;
+            w[lane] = 0.0f;
+        }
+        return false;
+    }
+    const float v = valid ? exp_contract(l - m) : 0.0f;
+    ws->v[e] = v;
+    __syncthreads();
+    const int nj = (E + 63) >> 6;
+    float S = 0.0f;
+    for (int j = 0; j < nj; ++j) S = S + ws->v[lane + 64 * j];
+    const float Z = tree_sum_lane0(S);
+    const float p = valid ? __fdiv_rn(v, Z) : 0.0f;
+    float key = valid ? p : -INFINITY;
+    if (mode == MOE_ROUTE_SUBST) {
+        const float pmx = wave_max_f(valid ? p : -INFINITY);
+        const float pmn = wave_min_f(valid ? p : INFINITY);
+        if (lane == 0) {
+            ws->red[1][wave] = pmx;
+            ws->red[2][wave] = pmn;
+        }
+        __syncthreads();
+        float pmax = -INFINITY, pmin = INFINITY;
+#pragma unroll
+        for (int i = 0; i < W; ++i) {
+            pmax = fmaxf(pmax, ws->red[1][i]);
+            pmin = fminf(pmin, ws->red[2][i]);
+        }
+        const float range = pmax - pmin;
+        const float c = L * range;
+        if (valid && table[e] >= 0) key = p + c;
+    }
+    // each full wave lists its r largest keys (r rounds: wave max, drop one lane holding it)
+    const int wf = E >> 6;
+    const int r = (k + wf - 1) / wf;
+    const int nt = wf * r;  // <= k + wf - 1 <= 39
+    if (wave < wf) {
+        float x = key;
+        for (int i = 0; i < r; ++i) {
+            const float mx = wave_max_f(x);
+            if (lane == 0) ws->top[wave * r + i] = mx;
+            const unsigned long long at = __ballot(x == mx);
+            if (lane == __ffsll((long long)at) - 1) x = -INFINITY;
+        }
+    }
+    __syncthreads();
+    // tau = k-th largest of the listed keys (equal keys ranked by list position)
+    if (wave == 0) {
+        const float tv = lane < nt ? ws->top[lane] : -INFINITY;
+        int rank = 0;
+        for (int q = 0; q < nt; q += 4) {
+            const float4 t4 = *(const float4*)&ws->top[q];
+            rank += (int)((t4.x > tv) | ((t4.x == tv) & (q < lane)));
+            rank += (int)((q + 1 < nt) & ((t4.y > tv) | ((t4.y == tv) & (q + 1 < lane))));
+            rank += (int)((q + 2 < nt) & ((t4.z > tv) | ((t4.z == tv) & (q + 2 < lane))));
+            rank += (int)((q + 3 < nt) & ((t4.w > tv) | ((t4.w == tv) & (q + 3 < lane))));
+        }
+        if (lane < nt && rank == k - 1) ws->tau = tv;
+        if (lane == 0) ws->count = 0;
+    }
+    __syncthreads();
+    const float tau = ws->tau;
+    const bool cand = valid && key >= tau;
+    const unsigned long long cm = __ballot(cand);
+    int base = 0;
+    if (cm) {
+        if (lane == 0) base = atomicAdd(&ws->count, __popcll(cm));
+        base = __builtin_amdgcn_readfirstlane(base);
+        const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(cm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cm, 0u));
+        if (cand && pos < 64) {
+            sc0->ck[pos] = order_key(key, e);
+            sc0->cp[pos] = p;
+        }
+    }
+    __syncthreads();
+    const int total = ws->count;
+    if (wave == 0) {
+        if (total > 64) return route_token_t<(W <= 8 ? 8 : 16)>(lr, E, k, mode, L, table, lane, ids, w, sc0);
+        rank_select(sc0, total, k, lane, ids, w);
+    }
+    return true;
+}
+
+// E <= 512 only (callers that hold many registers across the call).
+__device__ __forceinline__ bool route_token_512(const float* __restrict__ lr, int E, int k, int mode,
+                                                float L, const int32_t* __restrict__ table, int lane,
+                                                int32_t* ids, float* w, RouteScratch* sc)
+{
+    if (E <= 128) return route_token_t<2>(lr, E, k, mode, L, table, lane, ids, w, sc);
+    if (E <= 256) return route_token_t<4>(lr, E, k, mode, L, table, lane, ids, w, sc);
+    return route_token_t<8>(lr, E, k, mode, L, table, lane, ids, w, sc);
 }
 
 __device__ __forceinline__ bool route_token(const float* __restrict__ lr, int E, int k, int mode,

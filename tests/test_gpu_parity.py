@@ -465,6 +465,8 @@ def test_int8_substitution_with_installs_full_size():
     (3, 512, 16, 256, 4, 3, 3, 1),
     (2, 256, 10, 64, 5, 8, 8, 0),
     (9, 128, 16, 64, 8, 3, 3, 0),     # 72 pairs: falls back to two calls
+    (2, 128, 640, 64, 6, 4, 4, 1),    # E > 512: router kernel, then the fused experts
+    (1, 128, 1024, 64, 32, 3, 3, 0),  # maximum E and k
 ])
 def test_layer_forward_matches_route_plus_forward(shape):
     torch = _torch()
@@ -487,6 +489,45 @@ def test_layer_forward_matches_route_plus_forward(shape):
     # identical to the two-call form on the fused kernel
     out2, _ = run_forward(pr, ids_o, w_o, B.MOE_PATH_GEMV)
     assert np.array_equal(out.view(torch.int16).cpu().numpy(), out2.view(torch.int16).cpu().numpy())
+
+
+@pytest.mark.parametrize("T,E,k,mode,kind,seed", [
+    (1, 512, 10, 0, "normal", 601),
+    (1, 512, 10, 1, "zipf", 602),
+    (2, 512, 32, 0, "normal", 603),
+    (3, 512, 1, 1, "normal", 604),
+    (1, 100, 8, 0, "normal", 605),    # last wave partly filled
+    (2, 64, 5, 1, "normal", 606),     # a single full wave
+    (1, 128, 8, 0, "ties", 607),      # coarse logits: many equal keys
+    (1, 512, 10, 0, "ties", 608),     # ... more than 64 candidates
+    (3, 300, 16, 1, "ties", 609),
+])
+def test_layer_forward_workgroup_routing(T, E, k, mode, kind, seed):
+    """For T <= 3 and E >= 64 the fused kernel routes each token with all of a
+    workgroup's waves; ids and weights must equal the oracle's bit for bit,
+    including ties (lower id first) and the more-than-64-candidates case."""
+    torch = _torch()
+    H, I = 128, 64
+    pr = synth.make_problem(seed, T, H, E, I, k, 4, 4, n_slots=E + 3,
+                            resident=(E // 2 if mode else None), gaussian=False,
+                            zipf_s=(1.1 if kind == "zipf" else 0.0))
+    lg = pr.logits
+    if kind == "ties":
+        lg = (np.round(lg * 2.0) / 2.0).astype(np.float32)
+    desc = B.moe_size_class_init(H, I, 4, 4, pr.pool.shape[0])
+    ew = err_word()
+    out, ids, w = B.moe_layer_forward(to_dev(lg), dev_bf16(pr.x), to_dev(pr.table),
+                                      to_dev(pr.pool.reshape(-1)), desc, k, mode=mode, L=0.15,
+                                      err_word=ew)
+    torch.cuda.synchronize()
+    ids_o, w_o = oracle.route(lg, k, mode=mode, L=0.15, slot_table=pr.table)
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), w_o.view(np.uint32))
+    hit_missing = bool((pr.table[ids_o.reshape(-1)] < 0).any())
+    assert int(ew.item()) == (B.MOE_ERRW_NOT_RESIDENT if hit_missing else 0)
+    if not hit_missing:
+        ref = oracle.layer(pr.x, ids_o, w_o, pr.table, pr.pool, H, I, 4, 4, E, threads=THREADS)
+        check_close(out, ref, f"wg routing {T} {E} {k}")
 
 
 def test_fused_decode_repeated_calls_and_graph_replay():
