@@ -24,6 +24,8 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # no hand-written or compiler-chosen packed fp32 ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results straight into VGPRs (no accumulation-register reads)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", os.path.join(ROOT, "include"),
 ]

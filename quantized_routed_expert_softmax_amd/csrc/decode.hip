@@ -59,8 +59,6 @@ namespace {
 
 constexpr int kMaxPairs = 64;
 constexpr int kMaxE = 1024;
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxGrid = 1024;  // call-tag counters in the reserved workspace region
 constexpr int kGenBase = 64;    // dword index of counter 0
 
@@ -215,9 +213,11 @@ __device__ __forceinline__ void unpack_row(const RowLoad<B, UPL>& r, uint32_t (&
     }
 }
 
-template <int BG, int BD, int UG, int UD>
-__global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
+template <int BG, int BD, int UG, int UD, int W>
+__global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
 {
+    constexpr int kWaves = W;  // waves per workgroup
+    constexpr int kThreads = 64 * W;
     extern __shared__ __attribute__((aligned(16))) uint32_t s_dyn[];  // x, logits, x unit sums, h, h unit sums, partials
     __shared__ int32_t s_table[kMaxE];
     __shared__ int32_t s_ids[kMaxPairs];
@@ -273,9 +273,10 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
                 }
             }
         }
-        int32_t tb[kMaxE / kThreads];
+        constexpr int RT = (kMaxE + kThreads - 1) / kThreads;
+        int32_t tb[RT];
 #pragma unroll
-        for (int r = 0; r < kMaxE / kThreads; ++r) {
+        for (int r = 0; r < RT; ++r) {
             const int i = tid + kThreads * r;
             tb[r] = P.table[i < E ? i : E - 1];
         }
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
             s_w[tid] = P.w_in[tid];
         }
 #pragma unroll
-        for (int r = 0; r < kMaxE / kThreads; ++r) {
+        for (int r = 0; r < RT; ++r) {
             const int i = tid + kThreads * r;
             if (i < E) s_table[i] = tb[r];
         }
@@ -409,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
     const int n_items = n_hit * n_ipr;
     const int gw = blockIdx.x * kWaves + wave, NW = G * kWaves;
     const size_t g_row_dw = (size_t)H * BG / 32;
-    constexpr int D1 = (64 / (4 * UG * (BG + 1))) < 1 ? 1 : ((64 / (4 * UG * (BG + 1))) > 8 ? 8 : (64 / (4 * UG * (BG + 1))));
+    constexpr int D1 = (64 / (4 * UG * (BG + 1))) < 1 ? 1 : ((64 / (4 * UG * (BG + 1))) > 2 ? 2 : (64 / (4 * UG * (BG + 1))));
     RowLoad<BG, UG> gr[D1][2], ur[D1][2];
     int ih[D1], iii[D1], islot[D1];
     const uint32_t g_row_b = (uint32_t)(g_row_dw * 4), g_sb_b = (uint32_t)(H / 16);  // bytes per row
@@ -456,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
     const int row0 = blockIdx.x * P.rows_per_wg;
     const int n_rg = P.rows_per_wg / rpp_d;   // row groups of this workgroup
     const uint32_t d_row_b = (uint32_t)(I * BD / 8), d_sb_b = (uint32_t)(I / 16);  // bytes per row
-    constexpr int D2 = (64 / (UD * (BD + 1))) < 1 ? 1 : ((64 / (UD * (BD + 1))) > 8 ? 8 : (64 / (UD * (BD + 1))));
+    constexpr int D2 = (64 / (UD * (BD + 1))) < 1 ? 1 : ((64 / (UD * (BD + 1))) > 4 ? 4 : (64 / (UD * (BD + 1))));
     // phase-2 items of the workgroup: (row group, hit), i = rg * n_hit + hit; wave w
     // takes i = w, w + kWaves, ... (balanced to within one item per wave)
     const int n_all2 = n_rg * n_hit;
@@ -633,18 +634,18 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeParams P)
     }
 }
 
-template <int BG, int BD, int UG, int UD>
+template <int BG, int BD, int UG, int UD, int W>
 hipError_t launch_t(const DecodeParams& P, int G, size_t lds, hipStream_t s)
 {
-    hipLaunchKernelGGL((decode_layer_kernel<BG, BD, UG, UD>), dim3(G), dim3(kThreads), lds, s, P);
+    hipLaunchKernelGGL((decode_layer_kernel<BG, BD, UG, UD, W>), dim3(G), dim3(64 * W), lds, s, P);
     return hipGetLastError();
 }
 
-template <int BG, int BD, int UG, int UD>
+template <int BG, int BD, int UG, int UD, int W>
 int occupancy_t(size_t lds)
 {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_layer_kernel<BG, BD, UG, UD>, kThreads, lds) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_layer_kernel<BG, BD, UG, UD, W>, 64 * W, lds) != hipSuccess)
         return 0;
     return nb;
 }
@@ -662,16 +663,18 @@ using LaunchFn = hipError_t (*)(const DecodeParams&, int, size_t, hipStream_t);
 using OccFn = int (*)(size_t);
 
 struct Variant {
-    int bg, bd, ug, ud;
+    int bg, bd, ug, ud, w;  // bits gate/up, bits down, units per lane, waves per workgroup
     LaunchFn launch;
     OccFn occ;
 };
 
-#define MOE_V(BG, BD, UG, UD) {BG, BD, UG, UD, launch_t<BG, BD, UG, UD>, occupancy_t<BG, BD, UG, UD>}
+// Waves per workgroup: 10 where the kernel fits 3 waves per SIMD without
+// spilling (one phase-1 item per wave at the decode shape), else 8.
+#define MOE_V(BG, BD, UG, UD, W) {BG, BD, UG, UD, W, launch_t<BG, BD, UG, UD, W>, occupancy_t<BG, BD, UG, UD, W>}
 const Variant kVariants[] = {
-    MOE_V(3, 3, 1, 1), MOE_V(4, 4, 1, 1), MOE_V(6, 6, 1, 1), MOE_V(8, 8, 1, 1),
-    MOE_V(4, 6, 1, 1), MOE_V(3, 3, 1, 3), MOE_V(4, 4, 1, 3), MOE_V(4, 6, 1, 3),
-    MOE_V(8, 8, 2, 1), MOE_V(4, 4, 2, 1), MOE_V(3, 3, 2, 1), MOE_V(6, 6, 1, 3),
+    MOE_V(3, 3, 1, 1, 10), MOE_V(4, 4, 1, 1, 10), MOE_V(6, 6, 1, 1, 8), MOE_V(8, 8, 1, 1, 10),
+    MOE_V(4, 6, 1, 1, 10), MOE_V(3, 3, 1, 3, 8), MOE_V(4, 4, 1, 3, 8), MOE_V(4, 6, 1, 3, 8),
+    MOE_V(8, 8, 2, 1, 8), MOE_V(4, 4, 2, 1, 8), MOE_V(3, 3, 2, 1, 8), MOE_V(6, 6, 1, 3, 8),
 };
 #undef MOE_V
 
@@ -710,7 +713,7 @@ struct LdsLayout {
     size_t bytes;
 };
 
-LdsLayout lds_layout(int T, int k, int E, int H, int I, int rows_per_wg)
+LdsLayout lds_layout(int T, int k, int E, int H, int I, int rows_per_wg, int W)
 {
     LdsLayout L;
     const int n = T * k;
@@ -719,7 +722,7 @@ LdsLayout lds_layout(int T, int k, int E, int H, int I, int rows_per_wg)
     L.h2 = up4(L.xs1 + T * (H / 32));
     L.xs2 = up4(L.h2 + n * (I / 2));
     L.part = up4(L.xs2 + n * (I / 32));
-    L.bytes = (size_t)4 * L.part + sizeof(float) * (size_t)kWaves * rows_per_wg * T;
+    L.bytes = (size_t)4 * L.part + sizeof(float) * (size_t)W * rows_per_wg * T;
     return L;
 }
 
@@ -732,7 +735,8 @@ bool decode_fused_supported(int T, int k, int E, const ClassView& c)
     int lg, ug, ld, ud;
     lanes_of(c.H / 32, &lg, &ug);
     lanes_of(c.I / 32, &ld, &ud);
-    if (!find_variant(c.bits_gu, c.bits_d, ug, ud)) return false;
+    const Variant* v = find_variant(c.bits_gu, c.bits_d, ug, ud);
+    if (!v) return false;
     const DevInfo di = dev_info();
     if (di.cus <= 0) return false;
     const int rpp_d = 64 / ld;
@@ -740,9 +744,9 @@ bool decode_fused_supported(int T, int k, int E, const ClassView& c)
     const int rows = ((n_rg + di.cus - 1) / di.cus) * rpp_d;
     if ((size_t)n * (c.I / 2) > (size_t)MOE_WS_XWORDS) return false;  // tagged h words
     if (c.slot_bytes >= ((int64_t)1 << 31)) return false;                // 32-bit offsets in a slot
-    const size_t static_lds = sizeof(int32_t) * (kMaxE + 8 * kMaxPairs) + sizeof(RouteScratch) * kWaves +
-                              sizeof(RouteWgScratch<kWaves>) + 64;
-    return lds_layout(T, k, E, c.H, c.I, rows).bytes + static_lds <= di.lds_per_block;
+    const size_t static_lds = sizeof(int32_t) * (kMaxE + 8 * kMaxPairs) + sizeof(RouteScratch) * v->w +
+                              sizeof(RouteWgScratch<10>) + 64;
+    return lds_layout(T, k, E, c.H, c.I, rows, v->w).bytes + static_lds <= di.lds_per_block;
 }
 
 hipError_t launch_decode_fused(const float* logits, int mode, float L, const int32_t* ids_in,
@@ -765,7 +769,7 @@ hipError_t launch_decode_fused(const float* logits, int mode, float L, const int
     int G = n_rg < di.cus ? n_rg : di.cus;
     if (G > kMaxGrid) G = kMaxGrid;
     const int rows = ((n_rg + G - 1) / G) * rpp_d;
-    const LdsLayout LL = lds_layout(T, k, E, c.H, c.I, rows);
+    const LdsLayout LL = lds_layout(T, k, E, c.H, c.I, rows, v->w);
     const size_t lds = LL.bytes;
     if (v->occ(lds) < 1) return hipErrorInvalidConfiguration;
     DecodeParams P;
@@ -803,8 +807,8 @@ hipError_t launch_decode_fused(const float* logits, int mode, float L, const int
     P.part_dw = LL.part;
     const int rpp = 64 / lg;
     const int n_ipr = c.I / (rpp > 1 ? rpp : 2);
-    P.nw_q = G * kWaves / n_ipr;
-    P.nw_r = G * kWaves % n_ipr;
+    P.nw_q = G * v->w / n_ipr;
+    P.nw_r = G * v->w % n_ipr;
     P.spin_limit = 1u << 20;
     return v->launch(P, G, lds, s);
 }

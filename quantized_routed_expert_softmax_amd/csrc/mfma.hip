@@ -9,12 +9,15 @@
 //
 // Work split: a workgroup owns (hit expert, 64 output columns); each of its 4
 // waves owns 16 columns and loops over the expert's rows (its sorted pairs) in
-// M-tiles of 16, up to 4 M-tiles per sweep of K.  Weights are read once per
-// sweep straight from the slot pool into registers: lane (column n, lane group
-// g) reads the few dwords holding its 8 codes of the current 32-wide K step and
-// turns them into 4 bf16 pairs (128 + c, the P16 pairing) without LDS.  The
-// activations were laid out in the same P16 order, so one 16-byte load per lane
-// is the A operand.
+// M-tiles of 16, MT M-tiles per sweep of K.  The K sweep is a software pipeline
+// of 128-input stages: coalesced 16-byte loads of the stage's raw codes,
+// scale/bias and activation rows go to registers two stages ahead, are written
+// to an LDS double buffer one stage ahead, and the matrix cores consume the
+// current stage from LDS.  Workgroup barriers fence LDS only, so the global
+// loads of later stages stay in flight across them.  Lane (column n, lane group
+// g) turns the dwords of its unit in LDS into 4 bf16 pairs (128 + c, the P16
+// pairing); the activations were laid out in the same P16 order, so one 16-byte
+// LDS read per lane is the A operand.
 //
 // The affine map is applied per group of 64 inputs after the matrix core has
 // summed codes against activations:
@@ -98,20 +101,27 @@ __device__ __forceinline__ u32x4_t lane_pairs(const uint32_t* __restrict__ unit,
     return r;
 }
 
-constexpr int kMT = 4;            // M-tiles (of 16 rows) per sweep of K
 constexpr int kKC = 128;          // K per pipeline stage
 constexpr int kUPC = kKC / 32;    // pack units per stage
 constexpr int kGPC = kKC / 64;    // groups per stage
 constexpr int kAROW = kKC + 8;    // bf16 per staged activation row (padding: conflict-free reads)
 
 // One pipeline stage in LDS: raw codes and scale/bias of the workgroup's NB*64
-// weight rows for kKC inputs, and kKC activations of up to kMT*16 rows.
-template <int B, int NB>
+// weight rows for kKC inputs, and kKC activations of up to MT*16 rows.
+template <int B, int NB, int MT>
 struct Stage {
     uint32_t codes[NB * 64][kUPC * B];
     uint32_t sb[NB * 64][kGPC];
-    uint16_t a[kMT * 16][kAROW];
+    uint16_t a[MT * 16][kAROW];
 };
+
+// Workgroup barrier that orders LDS only: global loads in flight stay in flight.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // The 4 P16 pairs of lane group g from the dwords of one unit held in LDS
 // (same bit arithmetic as lane_pairs, reading LDS instead of global memory).
@@ -126,14 +136,15 @@ __device__ __forceinline__ u32x4_t lds_pairs(const uint32_t* __restrict__ unit, 
 }
 
 // Grouped dequantizing GEMM for one hit expert and 64 output columns per
-// workgroup (16 per wave), pipelined through LDS in stages of kKC inputs.
+// workgroup (16 per wave), pipelined through registers and LDS in stages of kKC
+// inputs (see the top of this file).
 //   GU = true : gate/up.  Weight rows: gate n0..n0+63 and up I+n0..; A = P16 x
 //               rows of the expert's pairs (via sorted_pairs); epilogue SwiGLU
 //               -> h (bf16, P16) at the pair's sorted position.
 //   GU = false: down.  Weight rows n0..n0+63 of the down matrix; A = h rows;
 //               epilogue y (fp32) at [pair id][n].
-template <int B, bool GU>
-__global__ __launch_bounds__(256, 2) void mfma_grouped_kernel(
+template <int B, bool GU, int MT, int CBW>
+__global__ __launch_bounds__(256) void mfma_grouped_kernel(
     const uint16_t* __restrict__ act, int H, int I, int k, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table,
     const int32_t* __restrict__ table, const uint8_t* __restrict__ pool, int64_t n_slots,
@@ -141,8 +152,17 @@ __global__ __launch_bounds__(256, 2) void mfma_grouped_kernel(
     float* __restrict__ ybuf, uint32_t* __restrict__ err)
 {
     constexpr int NB = GU ? 2 : 1;
-    __shared__ Stage<B, NB> st[2];
-    const int hit = blockIdx.y;
+    __shared__ Stage<B, NB, MT> st[2];
+    // XCD-aware tile order: workgroup L runs on XCD L % 8, so the workgroups of
+    // one expert are given the same L % 8 -- they share one L2 and fetch the
+    // expert's activation rows from memory once, not once per workgroup.  A
+    // workgroup takes CBW consecutive column blocks of 64.
+    const int ncb = (GU ? I : H) / 64;          // column blocks per expert
+    const int nwg = (ncb + CBW - 1) / CBW;      // workgroups per expert
+    const int L = blockIdx.x, r8 = L >> 3;
+    const int cb0 = (r8 % nwg) * CBW;
+    const int ncb_wg = min(CBW, ncb - cb0);     // column blocks of this workgroup
+    const int hit = (r8 / nwg) * 8 + (L & 7);
     if (hit >= pass_table[0]) return;
     const int e = pass_table[2 + hit];
     const int32_t slot = table[e];
@@ -154,11 +174,10 @@ __global__ __launch_bounds__(256, 2) void mfma_grouped_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const int K = GU ? H : I;            // reduction length
-    const int n0 = blockIdx.x * 64;      // first output column of the workgroup
-    const int n = n0 + wave * 16 + c16;  // this lane's column
-    const int NC = K / kKC;              // stages per sweep (K is a multiple of 64)
+    const int NC = K / kKC;              // full K stages per column block
     const bool tail = (K % kKC) != 0;    // a last half stage of 64 inputs
-    const int n_stages = NC + (tail ? 1 : 0);
+    const int n_kc = NC + (tail ? 1 : 0);
+    const int n_stages = ncb_wg * n_kc;  // stage s: column block cb0 + s / n_kc, K chunk s % n_kc
 
     const uint8_t* rowb = pool + (size_t)slot * (size_t)slot_bytes;
     const size_t row_dw = (size_t)K * B / 32;
@@ -168,17 +187,17 @@ __global__ __launch_bounds__(256, 2) void mfma_grouped_kernel(
     const u32x4_t ones = {MOE_ONES_PAIR, MOE_ONES_PAIR, MOE_ONES_PAIR, MOE_ONES_PAIR};
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 
-    // weight row (in the whole matrix) of the workgroup's local row r
-#define wrow(R) (GU ? ((R) < 64 ? n0 + (R) : I + n0 + ((R) - 64)) : n0 + (R))
+    // weight row (in the whole matrix) of local row r of the column block at n0
+#define wrow(R) (GU ? ((R) < 64 ? n0_ + (R) : I + n0_ + ((R) - 64)) : n0_ + (R))
 
     // staging assignment: B pieces (16 B), sb dwords, A pieces (16 B)
     constexpr int BPIECES = NB * 64 * B;                 // per stage (B pieces of 16 B per row)
     constexpr int BPT = (BPIECES + 255) / 256;
     constexpr int SBN = NB * 64 * kGPC;                  // sb dwords per stage
-    constexpr int APT = kMT * 16 * (kKC / 8) / 256;      // A pieces per thread (= 4)
+    constexpr int APT = MT * 16 * (kKC / 8) / 256;       // A pieces per thread
 
-    for (int m0 = 0; m0 < cnt; m0 += 16 * kMT) {
-        const int rows = min(16 * kMT, cnt - m0);
+    for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
+        const int rows = min(16 * MT, cnt - m0);
         const int nmt = (rows + 15) >> 4;
         // activation row pointers of this thread's A pieces (fixed for the sweep)
         // rows past the expert's last pair re-read its last row (results discarded)
@@ -191,14 +210,15 @@ __global__ __launch_bounds__(256, 2) void mfma_grouped_kernel(
             if (GU) arow[i] = act + (size_t)(sorted_pairs[base + m0 + m] / k) * H;
             else arow[i] = act + (size_t)(base + m0 + m) * I;
         }
-        u32x4_t rb[BPT];
-        uint32_t rs;
-        u32x4_t ra[APT];
-// every staging load is unconditional (indices clamped to valid data), so the
-// staging registers are never spilled and the loads stay in flight
-#define MOE_LOAD_STAGE(C)                                                                       \
+        // two register sets (stages in flight); every staging load is unconditional
+        // (indices clamped to valid data), so the staging registers are never spilled
+        u32x4_t rb0[BPT], ra0[APT], rb1[BPT], ra1[APT];
+        uint32_t rs0, rs1;
+#define MOE_LOAD_STAGE(C, RB, RS, RA)                                                           \
     {                                                                                           \
-        const int kin_ = (C) * kKC;                                                             \
+        const int cbl_ = (C) / n_kc;                                                            \
+        const int n0_ = (cb0 + cbl_) * 64;                                                      \
+        const int kin_ = ((C) - cbl_ * n_kc) * kKC;                                             \
         const int units_ = (kin_ + kKC <= K) ? kUPC : (K - kin_) / 32;                          \
         static_for<BPT>([&](auto I_) {                                                          \
             constexpr int i = decltype(I_)::value;                                              \
@@ -207,107 +227,127 @@ __global__ __launch_bounds__(256, 2) void mfma_grouped_kernel(
             const int r = q / B;                                                                \
             int p = q - r * B;                                                                  \
             p = p * 4 < units_ * B ? p : 0;                                                     \
-            rb[i] = *(const u32x4_t*)(codes + (size_t)wrow(r) * row_dw + (size_t)(kin_ / 32) * B + p * 4); \
+            RB[i] = *(const u32x4_t*)(codes + (size_t)wrow(r) * row_dw + (size_t)(kin_ / 32) * B + p * 4); \
         });                                                                                     \
         {                                                                                       \
             const int qs = tid < SBN ? tid : SBN - 1;                                           \
             const int r = qs / kGPC;                                                            \
             int gg = qs - r * kGPC;                                                             \
             gg = gg * 64 < units_ * 32 ? gg : 0;                                                \
-            rs = sbg[(size_t)wrow(r) * (K / 64) + kin_ / 64 + gg];                              \
+            RS = sbg[(size_t)wrow(r) * (K / 64) + kin_ / 64 + gg];                              \
         }                                                                                       \
         static_for<APT>([&](auto I_) {                                                          \
             constexpr int i = decltype(I_)::value;                                              \
             int p = (tid + 256 * i) % (kKC / 8);                                                \
             p = p * 8 < units_ * 32 ? p : 0;                                                    \
-            ra[i] = *(const u32x4_t*)(arow[i] + kin_ + p * 8);                                  \
+            RA[i] = *(const u32x4_t*)(arow[i] + kin_ + p * 8);                                  \
         });                                                                                     \
     }
-#define MOE_STORE_STAGE(BUF)                                                                    \
+#define MOE_STORE_STAGE(BUF, RB, RS, RA)                                                        \
     {                                                                                           \
-        Stage<B, NB>& S_ = st[(BUF)];                                                           \
+        Stage<B, NB, MT>& S_ = st[(BUF)];                                                       \
         static_for<BPT>([&](auto I_) {                                                          \
             constexpr int i = decltype(I_)::value;                                              \
             const int q = tid + 256 * i;                                                        \
             if (q < BPIECES) {                                                                  \
                 const int r = q / B, p = q - r * B;                                             \
-                *(u32x4_t*)(&S_.codes[r][p * 4]) = rb[i];                                       \
+                *(u32x4_t*)(&S_.codes[r][p * 4]) = RB[i];                                       \
             }                                                                                   \
         });                                                                                     \
-        if (tid < SBN) S_.sb[tid / kGPC][tid % kGPC] = rs;                                      \
+        if (tid < SBN) S_.sb[tid / kGPC][tid % kGPC] = RS;                                      \
         static_for<APT>([&](auto I_) {                                                          \
             constexpr int i = decltype(I_)::value;                                              \
             const int q = tid + 256 * i;                                                        \
-            *(u32x4_t*)(&S_.a[q / (kKC / 8)][(q % (kKC / 8)) * 8]) = ra[i];                    \
+            *(u32x4_t*)(&S_.a[q / (kKC / 8)][(q % (kKC / 8)) * 8]) = RA[i];                    \
         });                                                                                     \
     }
+#define MOE_COMPUTE_STAGE(BUF, C)                                                               \
+    {                                                                                           \
+        const Stage<B, NB, MT>& S = st[(BUF)];                                                  \
+        const int cbl = (C) / n_kc;                                                             \
+        const int kin = ((C) - cbl * n_kc) * kKC;                                               \
+        const int groups = (kin + kKC <= K) ? kGPC : (K - kin) / 64;                            \
+        for (int G2 = 0; G2 < groups; ++G2) {                                                   \
+            u32x4_t bw[NB][2];                                                                  \
+            float sc[NB], zc[NB];                                                               \
+            _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                                 \
+                const int r = nb * 64 + wave * 16 + c16;                                        \
+                bw[nb][0] = lds_pairs<B>(&S.codes[r][(2 * G2) * B], g);                         \
+                bw[nb][1] = lds_pairs<B>(&S.codes[r][(2 * G2 + 1) * B], g);                     \
+                const uint32_t s2 = S.sb[r][G2];                                                \
+                sc[nb] = half_bits_to_f32(s2 & 0xFFFFu);                                        \
+                zc[nb] = __builtin_fmaf(-off, sc[nb], half_bits_to_f32(s2 >> 16));              \
+            }                                                                                   \
+            _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                                 \
+                if (mt < nmt) {                                                                 \
+                    const u32x4_t a0 = *(const u32x4_t*)(&S.a[mt * 16 + c16][(2 * G2) * 32 + 8 * g]); \
+                    const u32x4_t a1 = *(const u32x4_t*)(&S.a[mt * 16 + c16][(2 * G2 + 1) * 32 + 8 * g]); \
+                    f32x4_t tx = mfma(a0, ones, zero);                                          \
+                    tx = mfma(a1, ones, tx);                                                    \
+                    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                         \
+                        f32x4_t t = mfma(a0, bw[nb][0], zero);                                  \
+                        t = mfma(a1, bw[nb][1], t);                                             \
+                        _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_)                        \
+                            acc[nb][mt][q_] = __builtin_fmaf(sc[nb], t[q_], __builtin_fmaf(zc[nb], tx[q_], acc[nb][mt][q_])); \
+                    }                                                                           \
+                }                                                                               \
+            }                                                                                   \
+        }                                                                                       \
+        if (kin + kKC >= K) {                                                                   \
+            epilogue((cb0 + cbl) * 64 + wave * 16 + c16);                                       \
+            _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                   \
+                _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = zero;           \
+        }                                                                                       \
+    }
 
-        f32x4_t acc[NB][kMT];
+        f32x4_t acc[NB][MT];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int mt = 0; mt < kMT; ++mt) acc[nb][mt] = zero;
-
-        MOE_LOAD_STAGE(0)
-        MOE_STORE_STAGE(0)
-        __syncthreads();
-        for (int c = 0; c < n_stages; ++c) {
-            if (c + 1 < n_stages) MOE_LOAD_STAGE(c + 1)
-            const Stage<B, NB>& S = st[c & 1];
-            const int kin = c * kKC;
-            const int groups = (kin + kKC <= K) ? kGPC : (K - kin) / 64;
-            for (int G2 = 0; G2 < groups; ++G2) {
-                u32x4_t bw[NB][2];
-                float sc[NB], zc[NB];
+            for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = zero;
+        // results of this lane's column n for the sweep's rows
+        auto epilogue = [&](int n) {
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const int r = nb * 64 + wave * 16 + c16;
-                    bw[nb][0] = lds_pairs<B>(&S.codes[r][(2 * G2) * B], g);
-                    bw[nb][1] = lds_pairs<B>(&S.codes[r][(2 * G2 + 1) * B], g);
-                    const uint32_t s2 = S.sb[r][G2];
-                    sc[nb] = half_bits_to_f32(s2 & 0xFFFFu);
-                    zc[nb] = __builtin_fmaf(-off, sc[nb], half_bits_to_f32(s2 >> 16));
-                }
+            for (int mt = 0; mt < MT; ++mt) {
+                if (mt < nmt) {
 #pragma unroll
-                for (int mt = 0; mt < kMT; ++mt) {
-                    if (mt < nmt) {
-                        const u32x4_t a0 = *(const u32x4_t*)(&S.a[mt * 16 + c16][(2 * G2) * 32 + 8 * g]);
-                        const u32x4_t a1 = *(const u32x4_t*)(&S.a[mt * 16 + c16][(2 * G2 + 1) * 32 + 8 * g]);
-                        f32x4_t tx = mfma(a0, ones, zero);
-                        tx = mfma(a1, ones, tx);
-#pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) {
-                            f32x4_t t = mfma(a0, bw[nb][0], zero);
-                            t = mfma(a1, bw[nb][1], t);
-                            acc[nb][mt] += sc[nb] * t + zc[nb] * tx;
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = m0 + mt * 16 + 4 * g + i;
+                        if (r < cnt) {
+                            if constexpr (GU) {
+                                const int pos = (n & ~31) | p16_pos(n & 31);
+                                hbuf[(size_t)(base + r) * I + pos] = f32_to_bf16(silu_mul(acc[0][mt][i], acc[1][mt][i]));
+                            } else {
+                                ybuf[(size_t)sorted_pairs[base + r] * H + n] = acc[0][mt][i];
+                            }
                         }
                     }
                 }
             }
-            if (c + 1 < n_stages) MOE_STORE_STAGE((c + 1) & 1)
-            __syncthreads();
+        };
+
+        // prologue: stages 0 and 1 in flight, stage 0 into LDS
+        MOE_LOAD_STAGE(0, rb0, rs0, ra0)
+        if (n_stages > 1) MOE_LOAD_STAGE(1, rb1, rs1, ra1)
+        MOE_STORE_STAGE(0, rb0, rs0, ra0)
+        lds_barrier();
+        for (int c = 0; c < n_stages; c += 2) {
+            // even stage c: registers 0 take stage c+2, LDS 1 takes stage c+1
+            if (c + 2 < n_stages) MOE_LOAD_STAGE(c + 2, rb0, rs0, ra0)
+            MOE_COMPUTE_STAGE(0, c)
+            if (c + 1 < n_stages) MOE_STORE_STAGE(1, rb1, rs1, ra1)
+            lds_barrier();
+            if (c + 1 >= n_stages) break;
+            // odd stage c+1: registers 1 take stage c+3, LDS 0 takes stage c+2
+            if (c + 3 < n_stages) MOE_LOAD_STAGE(c + 3, rb1, rs1, ra1)
+            MOE_COMPUTE_STAGE(1, c + 1)
+            if (c + 2 < n_stages) MOE_STORE_STAGE(0, rb0, rs0, ra0)
+            lds_barrier();
         }
 #undef MOE_LOAD_STAGE
 #undef MOE_STORE_STAGE
+#undef MOE_COMPUTE_STAGE
 
-        // epilogue
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-            if (mt < nmt) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = m0 + mt * 16 + 4 * g + i;
-                    if (r < cnt) {
-                        if constexpr (GU) {
-                            const int pos = (n & ~31) | p16_pos(n & 31);
-                            hbuf[(size_t)(base + r) * I + pos] = f32_to_bf16(silu_mul(acc[0][mt][i], acc[1][mt][i]));
-                        } else {
-                            ybuf[(size_t)sorted_pairs[base + r] * H + n] = acc[0][mt][i];
-                        }
-                    }
-                }
-            }
-        }
     }
 #undef wrow
 }
@@ -360,24 +400,36 @@ hipError_t launch_permute_x(const uint16_t* x, int T, int H, uint16_t* xp, hipSt
     return hipGetLastError();
 }
 
+// M-tiles per sweep: 2 (32 rows) when experts average few rows, else 4.
+static int pick_mt(int T, int k, int E)
+{
+    const int64_t pairs = (int64_t)T * k;
+    const int64_t hits = pairs < E ? pairs : E;
+    return pairs > 40 * hits ? 4 : 2;
+}
+
 hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const SortView& sv,
                               const int32_t* table, const uint8_t* pool, const ClassView& c,
                               uint16_t* hbuf, uint32_t* err, hipStream_t s)
 {
     const int max_hit = (int64_t)T * k < E ? T * k : E;
-    dim3 grid(c.I / 64, max_hit);
-#define MOE_MG(BB)                                                                                 \
-    hipLaunchKernelGGL((mfma_grouped_kernel<BB, true>), grid, dim3(256), 0, s, xp, c.H, c.I, k,    \
+    constexpr int CBW = 1;  // column blocks per workgroup
+    dim3 grid((unsigned)(((c.I / 64 + CBW - 1) / CBW) * ((max_hit + 7) / 8) * 8));  // see the kernel's tile order
+    const int mt = pick_mt(T, k, E);
+#define MOE_MG(BB, MM)                                                                             \
+    hipLaunchKernelGGL((mfma_grouped_kernel<BB, true, MM, CBW>), grid, dim3(256), 0, s, xp, c.H, c.I, k, \
                        sv.offsets, sv.sorted_pairs, sv.pass_table, table, pool, c.n_slots,         \
                        c.slot_bytes, c.off_gu_codes, c.off_gu_sb, hbuf, nullptr, err)
+#define MOE_MG2(BB) { if (mt == 4) MOE_MG(BB, 4); else MOE_MG(BB, 2); }
     switch (c.bits_gu) {
-    case 3: MOE_MG(3); break;
-    case 4: MOE_MG(4); break;
-    case 6: MOE_MG(6); break;
-    case 8: MOE_MG(8); break;
+    case 3: MOE_MG2(3); break;
+    case 4: MOE_MG2(4); break;
+    case 6: MOE_MG2(6); break;
+    case 8: MOE_MG2(8); break;
     default: return hipErrorInvalidValue;
     }
 #undef MOE_MG
+#undef MOE_MG2
     return hipGetLastError();
 }
 
@@ -386,19 +438,23 @@ hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, const int32
                             float* ybuf, uint32_t* err, hipStream_t s)
 {
     const int max_hit = (int64_t)T * k < E ? T * k : E;
-    dim3 grid(c.H / 64, max_hit);
-#define MOE_MD(BB)                                                                                 \
-    hipLaunchKernelGGL((mfma_grouped_kernel<BB, false>), grid, dim3(256), 0, s, hbuf, c.H, c.I, k, \
-                       sv.offsets, sv.sorted_pairs, sv.pass_table, table, pool, c.n_slots,         \
+    constexpr int CBW = 1;  // column blocks per workgroup
+    dim3 grid((unsigned)(((c.H / 64 + CBW - 1) / CBW) * ((max_hit + 7) / 8) * 8));  // see the kernel's tile order
+    const int mt = pick_mt(T, k, E);
+#define MOE_MD(BB, MM)                                                                             \
+    hipLaunchKernelGGL((mfma_grouped_kernel<BB, false, MM, CBW>), grid, dim3(256), 0, s, hbuf, c.H, c.I, \
+                       k, sv.offsets, sv.sorted_pairs, sv.pass_table, table, pool, c.n_slots,      \
                        c.slot_bytes, c.off_d_codes, c.off_d_sb, nullptr, ybuf, err)
+#define MOE_MD2(BB) { if (mt == 4) MOE_MD(BB, 4); else MOE_MD(BB, 2); }
     switch (c.bits_d) {
-    case 3: MOE_MD(3); break;
-    case 4: MOE_MD(4); break;
-    case 6: MOE_MD(6); break;
-    case 8: MOE_MD(8); break;
+    case 3: MOE_MD2(3); break;
+    case 4: MOE_MD2(4); break;
+    case 6: MOE_MD2(6); break;
+    case 8: MOE_MD2(8); break;
     default: return hipErrorInvalidValue;
     }
 #undef MOE_MD
+#undef MOE_MD2
     return hipGetLastError();
 }
 

@@ -449,6 +449,16 @@ __device__ __attribute__((noinline)) bool route_token_t(const float* __restrict_
     return true;
 }
 
+// E <= 512 only (callers that hold many registers across the call).
+__device__ __forceinline__ bool route_token_512(const float* __restrict__ lr, int E, int k, int mode,
+                                                float L, const int32_t* __restrict__ table, int lane,
+                                                int32_t* ids, float* w, RouteScratch* sc)
+{
+    if (E <= 128) return route_token_t<2>(lr, E, k, mode, L, table, lane, ids, w, sc);
+    if (E <= 256) return route_token_t<4>(lr, E, k, mode, L, table, lane, ids, w, sc);
+    return route_token_t<8>(lr, E, k, mode, L, table, lane, ids, w, sc);
+}
+
 // LDS scratch of route_token_wg for W waves.
 template <int W>
 struct alignas(16) RouteWgScratch {
@@ -460,7 +470,7 @@ struct alignas(16) RouteWgScratch {
     float v[64 * W];    // e_i by expert
 };
 
-// Route one token with all W waves of a workgroup (64 <= E <= 64*W): lane l of
+// Route one token with all W waves of a workgroup (64 <= E <= min(512, 64*W)): lane l of
 // wave w holds expert 64w + l.  Every thread of the workgroup calls it with the
 // same arguments (it contains workgroup barriers); ids/w are written by wave 0.
 // The arithmetic is the single-wave routine's, step for step: exact max; the
@@ -574,20 +584,10 @@ __device__ bool route_token_wg(const float* __restrict__ lr, int E, int k, int m
     __syncthreads();
     const int total = ws->count;
     if (wave == 0) {
-        if (total > 64) return route_token_t<(W <= 8 ? 8 : 16)>(lr, E, k, mode, L, table, lane, ids, w, sc0);
+        if (total > 64) return route_token_512(lr, E, k, mode, L, table, lane, ids, w, sc0);
         rank_select(sc0, total, k, lane, ids, w);
     }
     return true;
-}
-
-// E <= 512 only (callers that hold many registers across the call).
-__device__ __forceinline__ bool route_token_512(const float* __restrict__ lr, int E, int k, int mode,
-                                                float L, const int32_t* __restrict__ table, int lane,
-                                                int32_t* ids, float* w, RouteScratch* sc)
-{
-    if (E <= 128) return route_token_t<2>(lr, E, k, mode, L, table, lane, ids, w, sc);
-    if (E <= 256) return route_token_t<4>(lr, E, k, mode, L, table, lane, ids, w, sc);
-    return route_token_t<8>(lr, E, k, mode, L, table, lane, ids, w, sc);
 }
 
 __device__ __forceinline__ bool route_token(const float* __restrict__ lr, int E, int k, int mode,

@@ -149,23 +149,46 @@ __global__ __launch_bounds__(1024) void sort_place_kernel(const int32_t* __restr
     __shared__ int s_hit[1024];
     const int tid = threadIdx.x;
     if (tid < E) {
+        // running sum over tiles; 16 independent loads per round trip
         int run = 0;
-        for (int b = 0; b < n_tiles; ++b) {
-            int32_t* c = tile_counts + (size_t)b * E + tid;
-            const int v = *c;
-            *c = run;  // tile base of expert tid
-            run += v;
+        for (int b0 = 0; b0 < n_tiles; b0 += 16) {
+            int v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                v[j] = b0 + j < n_tiles ? tile_counts[(size_t)(b0 + j) * E + tid] : 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (b0 + j < n_tiles) {
+                    tile_counts[(size_t)(b0 + j) * E + tid] = run;  // tile base of expert tid
+                    run += v[j];
+                }
+            }
         }
         s_cnt[tid] = run;
     }
     __syncthreads();
     write_offsets_and_passes(s_cnt, s_tmp, s_hit, E, P, offsets, pass_table);
     __syncthreads();
-    for (int p = tid; p < n; p += 1024) {
-        const int e = ids[p];
-        if (e < 0 || e >= E) continue;
-        const int b = p / kTile;
-        sorted_pairs[s_cnt[e] + tile_counts[(size_t)b * E + e] + rank_in[p]] = p;
+    // placement, 8 pairs per thread per round (independent loads first)
+    for (int p0 = tid; p0 < n; p0 += 1024 * 8) {
+        int e[8], r[8], tb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int p = p0 + 1024 * j;
+            e[j] = p < n ? ids[p] : -1;
+            r[j] = p < n ? rank_in[p] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int p = p0 + 1024 * j;
+            const bool ok = e[j] >= 0 && e[j] < E;
+            tb[j] = ok ? tile_counts[(size_t)(p / kTile) * E + e[j]] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int p = p0 + 1024 * j;
+            if (e[j] >= 0 && e[j] < E) sorted_pairs[s_cnt[e[j]] + tb[j] + r[j]] = p;
+        }
     }
 }
 
