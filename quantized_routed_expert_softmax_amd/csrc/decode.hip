@@ -521,17 +521,27 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
                 const uint32_t* act = s_act + t * (H / 2);
                 const float* xs = s_xs1 + t * Ug;
                 uint32_t hb[2] = {0u, 0u};
-#pragma unroll
-                for (int sb = 0; sb < 2; ++sb) {
-                    if (sb < nsub) {
-                        float g = row_dot_raw<BG, UG>(gr[d][sb], act, xs, seg, lpr);
-                        float u = row_dot_raw<BG, UG>(ur[d][sb], act, xs, seg, lpr);
-                        g = seg_sum(g, lpr);
-                        u = seg_sum(u, lpr);
-                        hb[sb] = f32_to_bf16(silu_mul(g, u));
-                    }
+                if (nsub == 2) {
+                    // both rows of the pair on all 64 lanes: one transposed reduction of
+                    // (g0, g1, u0, u1); lanes 0-15 then hold g0 and, after the i^32 swap,
+                    // u0; lanes 16-31 hold g1 and u1
+                    const float g0 = row_dot_raw<BG, UG>(gr[d][0], act, xs, seg, lpr);
+                    const float g1 = row_dot_raw<BG, UG>(gr[d][1], act, xs, seg, lpr);
+                    const float u0 = row_dot_raw<BG, UG>(ur[d][0], act, xs, seg, lpr);
+                    const float u1 = row_dot_raw<BG, UG>(ur[d][1], act, xs, seg, lpr);
+                    const float sm = wave_sum4(g0, g1, u0, u1, lane);
+                    const auto ru = __builtin_amdgcn_permlane32_swap(__float_as_uint(sm), __float_as_uint(sm), false, false);
+                    const uint32_t h = f32_to_bf16(silu_mul(sm, __uint_as_float(ru[1])));
+                    hb[0] = __builtin_amdgcn_readlane(h, 0);
+                    hb[1] = __builtin_amdgcn_readlane(h, 16);
+                } else {
+                    float g = row_dot_raw<BG, UG>(gr[d][0], act, xs, seg, lpr);
+                    float u = row_dot_raw<BG, UG>(ur[d][0], act, xs, seg, lpr);
+                    g = seg_sum(g, lpr);
+                    u = seg_sum(u, lpr);
+                    hb[0] = f32_to_bf16(silu_mul(g, u));
+                    hb[1] = (uint32_t)__shfl_xor((int)hb[0], lpr, 64);
                 }
-                if (nsub == 1) hb[1] = (uint32_t)__shfl_xor((int)hb[0], lpr, 64);
                 if (pub_lane)
                     __hip_atomic_store(&P.xw[(size_t)pos * (I / 2) + pidx], tag_hi | hb[0] | (hb[1] << 16),
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -541,8 +551,6 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
         if (it0 < n_items) issue_p1(it0);
     }
 
-    // the phase-2 rows stream in while h is exchanged (they do not depend on h)
-    issue_p2(pre, 0);
 
     // ---- stage h of every valid pair (P16, unit-contiguous: layout swz),
     //      polling each tagged word until it carries this call's tag.  Consecutive
@@ -551,13 +559,40 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     {
         constexpr int R = 8;
         const int nh = n_valid * (I / 2);
-        for (int q0 = tid; q0 < nh; q0 += kThreads * R) {
-            uint64_t hv[R];
+        uint64_t hv[R];
+        auto poll = [&](int q0) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int q = q0 + kThreads * r;
                 hv[r] = q < nh ? __hip_atomic_load(&P.xw[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag_hi;
             }
+        };
+        // First poll, then the phase-2 weight loads (they do not depend on h and
+        // stream in during the exchange).  Loads complete in issue order as far
+        // as the wait counter is concerned, so the poll goes first: reading its
+        // words never waits for the weights.
+        poll(tid);
+        issue_p2(pre, 0);
+        // a second look at the first words a little later, without waiting for the
+        // first: a word published just after the first poll then costs no extra
+        // round trip
+        uint64_t hv2[R];
+        __builtin_amdgcn_s_sleep(8);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int q = tid + kThreads * r;
+            hv2[r] = q < nh ? __hip_atomic_load(&P.xw[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag_hi;
+        }
+        bool stale = false;
+#pragma unroll
+        for (int r = 0; r < R; ++r) stale = stale || (uint32_t)(hv[r] >> 32) != tag;
+        if (stale) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if ((uint32_t)(hv[r] >> 32) != tag) hv[r] = hv2[r];
+        }
+        for (int q0 = tid; q0 < nh; q0 += kThreads * R) {
+            if (q0 != tid) poll(q0);
             unsigned spins = 0;
             for (;;) {
                 bool ready = true;
@@ -764,8 +799,8 @@ hipError_t launch_decode_fused(const float* logits, int mode, float L, const int
     if (di.cus <= 0) return hipErrorInvalidDevice;
     const int rpp_d = 64 / ld;
     const int n_rg = c.H / rpp_d;
-    // one workgroup per compute unit: every workgroup is resident, so the grid
-    // barrier completes; fewer if there are fewer row groups than units
+    // one workgroup per compute unit: every workgroup is resident, so every
+    // polled h word is eventually written; fewer if there are fewer row groups
     int G = n_rg < di.cus ? n_rg : di.cus;
     if (G > kMaxGrid) G = kMaxGrid;
     const int rows = ((n_rg + G - 1) / G) * rpp_d;

@@ -162,9 +162,29 @@ __device__ __forceinline__ float seg_sum(float v, int width)
     }
 }
 
+// silu(g) * u = g / (1 + e^-g) * u, with the hardware reciprocal (about 1 ulp).
 __device__ __forceinline__ float silu_mul(float g, float u)
 {
-    return g / (1.0f + __expf(-g)) * u;
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+// Sums of a, b, c, d over the 64 lanes of a wave, as one transposed reduction:
+// at the i^32 step a lane keeps two of its four values and trades the other two
+// with its partner, at the i^16 step one of two, then a sum within rows of 16.
+// On return lanes 0-15 hold sum(a), 16-31 sum(b), 32-47 sum(c), 48-63 sum(d).
+__device__ __forceinline__ float wave_sum4(float a, float b, float c, float d, int lane)
+{
+    const bool lo = lane < 32;
+    const float x = lo ? c : a, y = lo ? d : b;  // the values this lane hands over
+    const auto rx = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const auto ry = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    const float v0 = (lo ? a : c) + __uint_as_float(lo ? rx[1] : rx[0]);
+    const float v1 = (lo ? b : d) + __uint_as_float(lo ? ry[1] : ry[0]);
+    const bool even = (lane & 16) == 0;
+    const float z = even ? v1 : v0;
+    const auto rz = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+    const float w = (even ? v0 : v1) + __uint_as_float(even ? rz[1] : rz[0]);
+    return seg_sum_w<16>(w);
 }
 
 // Position of input c (0..31) of a chunk in the P16 activation layout.
