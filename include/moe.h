@@ -19,7 +19,9 @@
  * ---------------------------------------------------------------------------
  * Ownership.  The caller allocates and owns every buffer and every stream/event.
  *   Device pointers are plain device addresses; the library never frees them.
- *   The only memory the library allocates is host memory inside a moe_cache.
+ *   The library allocates host memory only: inside a moe_cache, a moe_store, and
+ *   a moe_pipeline (whose pinned host tier and staging rows come from
+ *   hipHostMalloc, with its HIP events); never device memory.
  * Asynchrony.  Every GPU entry point only enqueues work on the given stream and
  *   returns.  Its status covers host-side argument checks and launch errors.
  * Errors.  Entry points return MOE_OK (0) or a negative MOE_E_* code and set a
@@ -101,6 +103,7 @@ extern "C" {
 #define MOE_E_HIP           (-5) /* a HIP runtime call failed                   */
 #define MOE_E_BUSY          (-6) /* a fill of this entry is still in flight     */
 #define MOE_E_WORKSPACE     (-7) /* workspace smaller than the size query says  */
+#define MOE_E_IO            (-8) /* the expert store could not be read          */
 
 /* ---- device error-word bits --------------------------------------------- */
 #define MOE_ERRW_NOT_RESIDENT  0x1u /* routed expert has slot_table[e] < 0      */
@@ -310,6 +313,137 @@ int  moe_cache_table(const moe_cache* c, int layer, int32_t* table);
 int  moe_cache_lookup(const moe_cache* c, int layer, int expert, int64_t* slot);
 int  moe_cache_stats(const moe_cache* c, int64_t* hits, int64_t* misses, int64_t* evictions);
 int  moe_cache_class_of(const moe_cache* c, int layer);
+
+/*
+ * Cache introspection and repair.
+ * moe_cache_shape: number of classes, layers and experts per layer (any may be NULL).
+ * moe_cache_class_desc: copy of class `cls`'s descriptor.
+ * moe_cache_class_stats: hits, misses, evictions of one class since creation;
+ *   the per-class hit rate the size-class design reports ([CLASS] PR description:
+ *   each class has its own slots and LRU, the measured replay gives its hit rate).
+ * moe_cache_abort_fill: drop an entry whose fill failed: it becomes absent and its
+ *   slot empty at the LRU's back.  MOE_E_BUSY while the entry is pinned.
+ */
+int  moe_cache_shape(const moe_cache* c, int* n_classes, int* n_layers, int* E);
+int  moe_cache_class_desc(const moe_cache* c, int cls, moe_size_class_desc* d);
+int  moe_cache_class_stats(const moe_cache* c, int cls, int64_t* hits, int64_t* misses,
+                           int64_t* evictions);
+int  moe_cache_abort_fill(moe_cache* c, int layer, int expert);
+
+/*
+ * Expert store: where experts live when no cache holds them.  One contiguous row
+ * per (layer, expert) in the slot byte format, layer-major: the row of (l, e)
+ * starts at base(l) + e * slot_bytes(class(l)), base(l) = sum over l' < l of
+ * E * slot_bytes(class(l')).  Sources: [RFC] "How the prototype works", Quantized
+ * experts bullet (a one-time conversion writes one contiguous row per expert) and
+ * Reads bullet (one contiguous read per expert); [HF-PR] commit message (reads go
+ * through one descriptor per shard).
+ *
+ * moe_store_open_file: a file at `path`, opened once read-only; every reader
+ *   shares the descriptor (positioned reads).  It must hold at least
+ *   moe_store_bytes() bytes.  NULL on error (MOE_E_IO: cannot open / too short).
+ * moe_store_open_memory: `bytes` of caller-owned host memory at `mem` stand in
+ *   for the file (kept by the caller until moe_store_close).
+ * moe_store_read: synchronous read of one row into host memory `dst`.
+ * moe_store_row_offset: byte offset of a row, -1 on bad arguments.
+ */
+typedef struct moe_store moe_store;
+moe_store* moe_store_open_file(const char* path, const moe_size_class_desc* classes, int n_classes,
+                               const int32_t* layer_class, int n_layers, int E);
+moe_store* moe_store_open_memory(const void* mem, int64_t bytes, const moe_size_class_desc* classes,
+                                 int n_classes, const int32_t* layer_class, int n_layers, int E);
+void    moe_store_close(moe_store* s);
+int64_t moe_store_bytes(const moe_store* s);
+int64_t moe_store_row_offset(const moe_store* s, int layer, int expert);
+int     moe_store_read(const moe_store* s, int layer, int expert, void* dst);
+
+/*
+ * Miss pipeline: fills a moe_cache's device pools from a moe_store, through an
+ * optional tier of expert rows in pinned host memory.
+ * Sources: [RFC] "How the prototype works", Reads bullet (each layer brings its
+ * routing to the host once; misses are read on I/O threads into recycled pinned
+ * buffers, one contiguous read and one non-blocking host-to-device copy per
+ * expert; the next layers' experts are guessed and read in the background) and
+ * Host tier bullet (pinned rows between storage and the device cache, so a device
+ * miss costs one host-to-device copy; optional preload at load time); [HF-PR]
+ * host-tier commit message (rows handed out stay reserved until the copy that
+ * reads them has run) and mps_commit commit message (guessed reads still in
+ * flight are skipped, never waited for); [RFC] Cache bullet (when every expert is
+ * resident no layer waits for the host); [CLASS] PR description (every layer
+ * keeps the same share).
+ *
+ * moe_pipeline_config:
+ *   host_tier_bytes  pinned host bytes for expert rows (0 = no host tier), split
+ *                    between classes in proportion to the bytes of all their
+ *                    experts; one LRU of rows per class.
+ *   host_preload     nonzero: fill the host tier from the store at creation
+ *                    (layers ascending, experts ascending, until each class's rows
+ *                    are full).
+ *   io_threads       store readers, 1..64.
+ *   staging_rows     recycled pinned buffers (largest row each) for store reads
+ *                    that do not land in a host row; io_threads..1024.
+ *
+ * moe_pipeline_create: `class_pools[c]` is class c's device pool (n_slots rows of
+ *   slot_bytes, 256-byte aligned), `copy_stream` the stream every install copy
+ *   runs on (caller-owned, default priority).  The current device is the pools'
+ *   device.  The cache and store stay owned by the caller and must outlive the
+ *   pipeline; while it exists only the pipeline acquires, fills or pins entries of
+ *   that cache.  NULL on error.
+ * moe_pipeline_prepare: make the experts `ids[0..n)` (duplicates allowed) of
+ *   `layer` resident for a forward about to be enqueued on `compute`.  Hits are
+ *   touched; each miss takes the class's LRU victim, is copied from its host row
+ *   (inline) or read from the store on an I/O thread, then copied on the copy
+ *   stream after the copy stream has waited for the last forward that read the
+ *   victim slot.  Returns once every needed copy is enqueued (store reads done);
+ *   never waits for a copy itself: `compute` is made to wait for the install
+ *   events, then receives one host-to-device copy of the layer's expert -> slot
+ *   table (int32 [E], -1 absent) into the device buffer `table_dev`.  The experts
+ *   stay pinned until moe_pipeline_release(layer).  Errors: MOE_E_BUSY (layer
+ *   prepared and not released), MOE_E_NO_SLOT (every slot of the class pinned),
+ *   MOE_E_IO (store read failed; nothing stays pinned), MOE_E_HIP.
+ * moe_pipeline_release: call after the layer's forward has been enqueued on
+ *   `compute`: records the event that later installs into these slots wait for,
+ *   and unpins the layer's experts.
+ * moe_pipeline_prefetch: guessed experts of `layer`: absent ones start installs
+ *   in the background without pinning; resident or in-flight ones are skipped.
+ *   Never waits.  Returns the number of installs started (>= 0) or an error.
+ * moe_pipeline_drain: wait until every read and copy has finished.
+ * moe_pipeline_stats_get: counters of one class (moe_pipeline_stats).
+ * moe_pipeline_host_rows: host-tier rows of class `cls` (0 without a host tier).
+ * Threads: prepare, release, prefetch, drain and destroy from one thread; the
+ * I/O threads are internal.
+ */
+typedef struct moe_pipeline_config {
+    int64_t host_tier_bytes;
+    int32_t host_preload;
+    int32_t io_threads;
+    int32_t staging_rows;
+    int32_t reserved0;
+} moe_pipeline_config;
+
+typedef struct moe_pipeline_stats {
+    int64_t requests;          /* distinct experts asked for by prepare              */
+    int64_t hits;              /* resident with the install complete                 */
+    int64_t inflight_hits;     /* resident, install still in flight (e.g. a guess)   */
+    int64_t host_hits;         /* installs copied from a host-tier row               */
+    int64_t store_reads;       /* installs read from the store first                 */
+    int64_t prefetches;        /* guesses that started an install                    */
+    int64_t prefetch_skipped;  /* guesses resident, in flight, or with no free slot  */
+    int64_t bytes_copied;      /* host-to-device install bytes enqueued              */
+    int64_t bytes_read;        /* bytes read from the store (preload included)       */
+} moe_pipeline_stats;
+
+typedef struct moe_pipeline moe_pipeline;
+moe_pipeline* moe_pipeline_create(moe_cache* cache, moe_store* store, void* const* class_pools,
+                                  const moe_pipeline_config* cfg, hipStream_t copy_stream);
+void    moe_pipeline_destroy(moe_pipeline* p);
+int     moe_pipeline_prepare(moe_pipeline* p, int layer, const int32_t* ids, int n,
+                             int32_t* table_dev, hipStream_t compute);
+int     moe_pipeline_release(moe_pipeline* p, int layer, hipStream_t compute);
+int     moe_pipeline_prefetch(moe_pipeline* p, int layer, const int32_t* ids, int n);
+int     moe_pipeline_drain(moe_pipeline* p);
+int     moe_pipeline_stats_get(const moe_pipeline* p, int cls, moe_pipeline_stats* out);
+int64_t moe_pipeline_host_rows(const moe_pipeline* p, int cls);
 
 /* Thread-local message for the last failing call on this thread. */
 const char* moe_last_error(void);

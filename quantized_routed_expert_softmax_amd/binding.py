@@ -25,6 +25,7 @@ MOE_E_NO_SLOT = -4
 MOE_E_HIP = -5
 MOE_E_BUSY = -6
 MOE_E_WORKSPACE = -7
+MOE_E_IO = -8
 
 MOE_ERRW_NOT_RESIDENT = 0x1
 MOE_ERRW_BAD_SLOT = 0x2
@@ -59,6 +60,21 @@ class SizeClassDesc(ctypes.Structure):
                 ("n_slots", ctypes.c_int64), ("off_gu_codes", ctypes.c_int64),
                 ("off_gu_sb", ctypes.c_int64), ("off_d_codes", ctypes.c_int64),
                 ("off_d_sb", ctypes.c_int64), ("slot_bytes", ctypes.c_int64)]
+
+
+class PipelineConfig(ctypes.Structure):
+    _fields_ = [("host_tier_bytes", ctypes.c_int64), ("host_preload", ctypes.c_int32),
+                ("io_threads", ctypes.c_int32), ("staging_rows", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32)]
+
+
+class PipelineStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "requests", "hits", "inflight_hits", "host_hits", "store_reads", "prefetches",
+        "prefetch_skipped", "bytes_copied", "bytes_read")]
+
+    def as_dict(self) -> dict:
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
 
 
 def lib() -> ctypes.CDLL:
@@ -99,6 +115,25 @@ def lib() -> ctypes.CDLL:
                 "moe_cache_lookup": (I32, [P, I32, I32, ctypes.POINTER(I64)]),
                 "moe_cache_stats": (I32, [P, ctypes.POINTER(I64), ctypes.POINTER(I64), ctypes.POINTER(I64)]),
                 "moe_cache_class_of": (I32, [P, I32]),
+                "moe_cache_shape": (I32, [P, ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+                "moe_cache_class_desc": (I32, [P, I32, D]),
+                "moe_cache_class_stats": (I32, [P, I32, ctypes.POINTER(I64), ctypes.POINTER(I64),
+                                                ctypes.POINTER(I64)]),
+                "moe_cache_abort_fill": (I32, [P, I32, I32]),
+                "moe_store_open_file": (P, [ctypes.c_char_p, D, I32, P, I32, I32]),
+                "moe_store_open_memory": (P, [P, I64, D, I32, P, I32, I32]),
+                "moe_store_close": (None, [P]),
+                "moe_store_bytes": (I64, [P]),
+                "moe_store_row_offset": (I64, [P, I32, I32]),
+                "moe_store_read": (I32, [P, I32, I32, P]),
+                "moe_pipeline_create": (P, [P, P, P, ctypes.POINTER(PipelineConfig), P]),
+                "moe_pipeline_destroy": (None, [P]),
+                "moe_pipeline_prepare": (I32, [P, I32, P, I32, P, P]),
+                "moe_pipeline_release": (I32, [P, I32, P]),
+                "moe_pipeline_prefetch": (I32, [P, I32, P, I32]),
+                "moe_pipeline_drain": (I32, [P]),
+                "moe_pipeline_stats_get": (I32, [P, I32, ctypes.POINTER(PipelineStats)]),
+                "moe_pipeline_host_rows": (I64, [P, I32]),
                 "moe_last_error": (ctypes.c_char_p, []),
             }
             for name, (res, args) in sig.items():
@@ -355,3 +390,149 @@ def moe_cache_stats(c: int) -> tuple[int, int, int]:
 
 def moe_cache_class_of(c: int, layer: int) -> int:
     return lib().moe_cache_class_of(c, layer)
+
+
+def moe_cache_shape(c: int) -> tuple[int, int, int]:
+    a, b, e = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().moe_cache_shape(c, ctypes.byref(a), ctypes.byref(b), ctypes.byref(e)))
+    return a.value, b.value, e.value
+
+
+def moe_cache_class_desc(c: int, cls: int) -> SizeClassDesc:
+    d = SizeClassDesc()
+    _check(lib().moe_cache_class_desc(c, cls, ctypes.byref(d)))
+    return d
+
+
+def moe_cache_class_stats(c: int, cls: int) -> tuple[int, int, int]:
+    h, m, e = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().moe_cache_class_stats(c, cls, ctypes.byref(h), ctypes.byref(m), ctypes.byref(e)))
+    return h.value, m.value, e.value
+
+
+def moe_cache_abort_fill(c: int, layer: int, expert: int):
+    _check(lib().moe_cache_abort_fill(c, layer, expert))
+
+
+# --------------------------------------------------------------------------- #
+# expert store and miss pipeline                                               #
+# --------------------------------------------------------------------------- #
+_store_refs: dict = {}  # memory stores: keep the caller's bytes alive until close
+
+
+def _classes_arg(classes, layer_class):
+    arr = (SizeClassDesc * len(classes))(*classes)
+    lc = (ctypes.c_int32 * len(layer_class))(*layer_class)
+    return arr, lc
+
+
+def moe_store_open_file(path: str, classes: list[SizeClassDesc], layer_class: list[int], E: int) -> int:
+    arr, lc = _classes_arg(classes, layer_class)
+    h = lib().moe_store_open_file(os.fsencode(path), arr, len(classes), lc, len(layer_class), E)
+    if not h:
+        raise MoeError(MOE_E_IO, moe_last_error())
+    return h
+
+
+def moe_store_open_memory(mem, classes: list[SizeClassDesc], layer_class: list[int], E: int) -> int:
+    """`mem`: a C-contiguous uint8 numpy array or CPU torch tensor (kept alive here)."""
+    import numpy as np
+    if isinstance(mem, np.ndarray):
+        if mem.dtype != np.uint8 or not mem.flags["C_CONTIGUOUS"]:
+            raise ValueError("store memory must be a contiguous uint8 array")
+        ptr, nbytes = mem.ctypes.data, mem.nbytes
+    else:
+        torch = _torch()
+        if mem.device.type != "cpu" or mem.dtype != torch.uint8 or not mem.is_contiguous():
+            raise ValueError("store memory must be a contiguous uint8 CPU tensor")
+        ptr, nbytes = mem.data_ptr(), mem.numel()
+    arr, lc = _classes_arg(classes, layer_class)
+    h = lib().moe_store_open_memory(ctypes.c_void_p(ptr), nbytes, arr, len(classes), lc,
+                                    len(layer_class), E)
+    if not h:
+        raise MoeError(MOE_E_INVALID, moe_last_error())
+    _store_refs[h] = mem
+    return h
+
+
+def moe_store_close(s: int):
+    lib().moe_store_close(s)
+    _store_refs.pop(s, None)
+
+
+def moe_store_bytes(s: int) -> int:
+    return lib().moe_store_bytes(s)
+
+
+def moe_store_row_offset(s: int, layer: int, expert: int) -> int:
+    o = lib().moe_store_row_offset(s, layer, expert)
+    if o < 0:
+        raise MoeError(MOE_E_INVALID, moe_last_error())
+    return o
+
+
+def moe_store_read(s: int, layer: int, expert: int, dst):
+    """Read one row into the contiguous uint8 numpy array `dst`."""
+    if dst.dtype.itemsize != 1 or not dst.flags["C_CONTIGUOUS"]:
+        raise ValueError("dst must be a contiguous byte array")
+    _check(lib().moe_store_read(s, layer, expert, ctypes.c_void_p(dst.ctypes.data)))
+
+
+def moe_pipeline_create(cache: int, store: int, pools: list, host_tier_bytes: int = 0,
+                        host_preload: bool = False, io_threads: int = 4, staging_rows: int = 8,
+                        copy_stream=None) -> int:
+    """pools[c]: class c's device pool (uint8 tensor); copy_stream: a torch stream."""
+    torch = _torch()
+    ptrs = (ctypes.c_void_p * len(pools))(*[_dev_ptr(p, torch.uint8, f"pools[{i}]").value
+                                           for i, p in enumerate(pools)])
+    cfg = PipelineConfig(host_tier_bytes, int(bool(host_preload)), io_threads, staging_rows, 0)
+    if copy_stream is None:
+        raise ValueError("copy_stream is required")
+    h = lib().moe_pipeline_create(cache, store, ptrs, ctypes.byref(cfg), _stream(copy_stream))
+    if not h:
+        raise MoeError(MOE_E_INVALID, moe_last_error())
+    return h
+
+
+def moe_pipeline_destroy(p: int):
+    lib().moe_pipeline_destroy(p)
+
+
+def _ids_arg(ids):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).reshape(-1))
+    return a, ctypes.c_void_p(a.ctypes.data), a.size
+
+
+def moe_pipeline_prepare(p: int, layer: int, ids, table_dev, stream=None):
+    """ids: host int32 array of the layer's routed experts (any shape)."""
+    torch = _torch()
+    a, ptr, n = _ids_arg(ids)
+    _check(lib().moe_pipeline_prepare(p, layer, ptr, n, _dev_ptr(table_dev, torch.int32, "table_dev", 1),
+                                      _stream(stream)))
+
+
+def moe_pipeline_release(p: int, layer: int, stream=None):
+    _check(lib().moe_pipeline_release(p, layer, _stream(stream)))
+
+
+def moe_pipeline_prefetch(p: int, layer: int, ids) -> int:
+    a, ptr, n = _ids_arg(ids)
+    rc = lib().moe_pipeline_prefetch(p, layer, ptr, n)
+    if rc < 0:
+        raise MoeError(rc, moe_last_error())
+    return rc
+
+
+def moe_pipeline_drain(p: int):
+    _check(lib().moe_pipeline_drain(p))
+
+
+def moe_pipeline_stats_get(p: int, cls: int) -> dict:
+    st = PipelineStats()
+    _check(lib().moe_pipeline_stats_get(p, cls, ctypes.byref(st)))
+    return st.as_dict()
+
+
+def moe_pipeline_host_rows(p: int, cls: int) -> int:
+    return lib().moe_pipeline_host_rows(p, cls)

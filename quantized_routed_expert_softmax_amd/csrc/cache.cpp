@@ -38,6 +38,7 @@ struct CacheClass {
     moe_size_class_desc desc;
     std::vector<CacheSlot> slots;
     std::list<int64_t> lru;  // front = most recently used, back = next victim
+    int64_t hits = 0, misses = 0, evictions = 0;
 };
 
 struct moe_cache {
@@ -110,6 +111,23 @@ moe_cache* moe_cache_create(const moe_size_class_desc* classes, int n_classes,
 
 void moe_cache_destroy(moe_cache* c) { delete c; }
 
+int moe_cache_shape(const moe_cache* c, int* n_classes, int* n_layers, int* E)
+{
+    if (!c) return cache_fail(MOE_E_INVALID, "moe_cache_shape: NULL cache");
+    if (n_classes) *n_classes = (int)c->classes.size();
+    if (n_layers) *n_layers = (int)c->layer_class.size();
+    if (E) *E = c->E;
+    return MOE_OK;
+}
+
+int moe_cache_class_desc(const moe_cache* c, int cls, moe_size_class_desc* d)
+{
+    if (!c || !d || cls < 0 || cls >= (int)c->classes.size())
+        return cache_fail(MOE_E_INVALID, "moe_cache_class_desc: bad arguments");
+    *d = c->classes[cls].desc;
+    return MOE_OK;
+}
+
 int moe_cache_class_of(const moe_cache* c, int layer)
 {
     if (!c || layer < 0 || layer >= (int)c->layer_class.size()) return -1;
@@ -131,6 +149,7 @@ int moe_cache_acquire(moe_cache* c, int layer, int expert, int64_t* slot, int* n
         k.lru.splice(k.lru.begin(), k.lru, cs.it);
         if (cs.inflight) return MOE_E_BUSY;
         ++c->hits;
+        ++k.hits;
         return MOE_OK;
     }
     // miss: the least recently used slot that is neither pinned nor in flight
@@ -142,6 +161,7 @@ int moe_cache_acquire(moe_cache* c, int layer, int expert, int64_t* slot, int* n
         if (cs.layer >= 0) {
             c->table[cs.layer][cs.expert] = -1;
             ++c->evictions;
+            ++k.evictions;
         }
         cs.layer = layer;
         cs.expert = expert;
@@ -150,6 +170,7 @@ int moe_cache_acquire(moe_cache* c, int layer, int expert, int64_t* slot, int* n
         c->table[layer][expert] = v;
         k.lru.splice(k.lru.begin(), k.lru, cs.it);
         ++c->misses;
+        ++k.misses;
         *slot = v;
         *needs_fill = 1;
         return MOE_OK;
@@ -173,6 +194,26 @@ int moe_cache_fill_done(moe_cache* c, int layer, int expert, hipEvent_t ev)
         cs.inflight = false;
         cs.ev = nullptr;
     }
+    return MOE_OK;
+}
+
+int moe_cache_abort_fill(moe_cache* c, int layer, int expert)
+{
+    if (!layer_ok(c, layer, expert)) return cache_fail(MOE_E_INVALID, "moe_cache_abort_fill: bad arguments");
+    std::lock_guard<std::mutex> lock(c->mu);
+    const int64_t s = c->table[layer][expert];
+    if (s < 0) return cache_fail(MOE_E_NOT_RESIDENT, "moe_cache_abort_fill: entry not resident");
+    CacheClass& k = c->classes[c->layer_class[layer]];
+    CacheSlot& cs = k.slots[(size_t)s];
+    if (!cs.inflight) return cache_fail(MOE_E_INVALID, "moe_cache_abort_fill: no fill in flight");
+    if (cs.pins > 0) return cache_fail(MOE_E_BUSY, "moe_cache_abort_fill: entry is pinned");
+    // the slot holds nothing usable: empty it and put it where empty slots sit
+    c->table[layer][expert] = -1;
+    cs.layer = -1;
+    cs.expert = -1;
+    cs.inflight = false;
+    cs.ev = nullptr;
+    k.lru.splice(k.lru.end(), k.lru, cs.it);
     return MOE_OK;
 }
 
@@ -235,6 +276,19 @@ int moe_cache_stats(const moe_cache* c, int64_t* hits, int64_t* misses, int64_t*
     if (hits) *hits = c->hits;
     if (misses) *misses = c->misses;
     if (evictions) *evictions = c->evictions;
+    return MOE_OK;
+}
+
+int moe_cache_class_stats(const moe_cache* c, int cls, int64_t* hits, int64_t* misses,
+                          int64_t* evictions)
+{
+    if (!c || cls < 0 || cls >= (int)c->classes.size())
+        return cache_fail(MOE_E_INVALID, "moe_cache_class_stats: bad arguments");
+    std::lock_guard<std::mutex> lock(c->mu);
+    const CacheClass& k = c->classes[cls];
+    if (hits) *hits = k.hits;
+    if (misses) *misses = k.misses;
+    if (evictions) *evictions = k.evictions;
     return MOE_OK;
 }
 

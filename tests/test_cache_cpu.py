@@ -160,3 +160,68 @@ def test_bad_arguments():
             B.moe_cache_pin(c, 0, 3)
     finally:
         B.moe_cache_destroy(c)
+
+
+def test_per_class_stats_and_tables_match_the_reference_model():
+    """Two classes, layers interleaved, batches of distinct experts acquired as a
+    layer's prepare does: every slot, table and per-class counter agrees with the
+    plain list model."""
+    from lru_model import CacheModel
+    rng = np.random.default_rng(11)
+    E, layer_class, slots = 10, [0, 1, 0, 0, 1], [9, 5]
+    c = make(n_a=slots[0], n_b=slots[1], layers=layer_class, E=E)
+    model = CacheModel(slots, layer_class, E)
+    try:
+        for step in range(300):
+            layer = int(rng.integers(len(layer_class)))
+            ids = rng.integers(0, E, size=int(rng.integers(1, 5)))
+            expect = model.prepare(layer, ids)
+            got = []
+            for e, _, _ in expect:
+                rc, slot, nf = B.moe_cache_acquire(c, layer, e)
+                assert rc == B.MOE_OK
+                B.moe_cache_pin(c, layer, e)
+                got.append((e, slot, bool(nf)))
+            assert got == expect, step
+            for e, _, miss in expect:
+                if miss:
+                    B.moe_cache_fill_done(c, layer, e, None)
+                B.moe_cache_unpin(c, layer, e)
+        for l in range(len(layer_class)):
+            assert B.moe_cache_table(c, l, E).tolist() == model.table(l)
+        tot = [0, 0, 0]
+        for cls in range(2):
+            st = B.moe_cache_class_stats(c, cls)
+            assert st == model.class_stats(cls)
+            tot = [a + b for a, b in zip(tot, st)]
+        assert tuple(tot) == B.moe_cache_stats(c)
+        assert B.moe_cache_shape(c) == (2, len(layer_class), E)
+        d = B.moe_cache_class_desc(c, 1)
+        assert (d.bits_d, d.n_slots) == (6, slots[1])
+    finally:
+        B.moe_cache_destroy(c)
+
+
+def test_abort_fill_empties_the_slot_and_it_is_taken_next():
+    c = make(n_a=3, layers=(0,), E=8)
+    try:
+        fill(c, 0, 0)
+        fill(c, 0, 1)
+        rc, s, nf = B.moe_cache_acquire(c, 0, 2)
+        assert rc == B.MOE_OK and nf == 1
+        B.moe_cache_pin(c, 0, 2)
+        with pytest.raises(B.MoeError) as ei:      # pinned: the pinning caller drops it
+            B.moe_cache_abort_fill(c, 0, 2)
+        assert ei.value.code == B.MOE_E_BUSY
+        B.moe_cache_unpin(c, 0, 2)
+        B.moe_cache_abort_fill(c, 0, 2)
+        assert B.moe_cache_lookup(c, 0, 2) == -1
+        assert B.moe_cache_poll(c) == 0
+        with pytest.raises(B.MoeError):            # nothing in flight any more
+            B.moe_cache_abort_fill(c, 0, 2)
+        s2, nf = fill(c, 0, 5)                     # the emptied slot sits at the back
+        assert s2 == s and nf == 1
+        with pytest.raises(B.MoeError):            # a completed fill cannot be aborted
+            B.moe_cache_abort_fill(c, 0, 0)
+    finally:
+        B.moe_cache_destroy(c)
