@@ -42,6 +42,13 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=12, help="oracle sample: decode layers")
     p.add_argument("--eager", action="store_true", help="no HIP graph (launch-bound)")
+    p.add_argument("--replay", action="store_true",
+                   help="only the cache replay: mixed 48-layer decode through the miss pipeline")
+    p.add_argument("--replay-tokens", type=int, default=48, help="timed decode steps per replay")
+    p.add_argument("--replay-warmup", type=int, default=32, help="untimed steps (cache warm-up)")
+    p.add_argument("--replay-share", type=float, default=0.5, help="device share of each layer's experts")
+    p.add_argument("--io-threads", type=int, default=8)
+    p.add_argument("--copy-streams", type=int, default=2, help="install copy streams (1 to 4)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (to scale the FETCH_SIZE / WRITE_SIZE "
                         "counters of a profiling run)")
@@ -118,6 +125,150 @@ def decode_inputs(torch, synth, wl):
     return lg, x0
 
 
+def replay_main(args, torch, B, synth):
+    """Decode steps of the mixed workload (48 layers, 128 experts, top-8, two size
+    classes) through a device cache that holds a share of each layer's experts,
+    filled by the miss pipeline from an expert store in host memory.  Per layer:
+    route on the GPU, bring the routing to the host once, prepare (hits touched,
+    misses installed on the copy stream), forward, release."""
+    wl = synth.WORKLOADS["mixed"]
+    dev = torch.device("cuda")
+    L, E, k, H, I = wl.layers, wl.E, wl.k, wl.H, wl.I
+    kinds = sorted({synth.layer_bits(wl, l) for l in range(L)})
+    layer_class = [kinds.index(synth.layer_bits(wl, l)) for l in range(L)]
+    n_layers_c = [layer_class.count(c) for c in range(len(kinds))]
+    lays = [synth.Layout(H, I, bg, bd) for bg, bd in kinds]
+
+    # expert store: every expert of every layer, generated on the device, kept in
+    # host memory (stands in for the file the one-time conversion writes)
+    t_setup = time.time()
+    total = sum(E * lays[c].slot_bytes for c in layer_class)
+    store_np = np.empty(total, np.uint8)
+    tmp = torch.empty(E * max(l.slot_bytes for l in lays), dtype=torch.uint8, device=dev)
+    off = 0
+    for l in range(L):
+        sb = lays[layer_class[l]].slot_bytes
+        pool = tmp[:E * sb].view(E, sb)
+        synth.fill_pool_device(pool, lays[layer_class[l]], np.arange(E), wl.seed, l)
+        torch.from_numpy(store_np[off:off + E * sb]).copy_(pool.view(-1))
+        off += E * sb
+    del tmp
+    torch.cuda.synchronize()
+    log(f"replay store {total / 1e9:.2f} GB in {time.time() - t_setup:.1f}s")
+
+    def run(T, share, host_mode, resident_first=False, n_copy=args.copy_streams):
+        slots = [max(int(round(share * E)) * n, T * k) for n in n_layers_c]
+        classes = [B.moe_size_class_init(H, I, bg, bd, s) for (bg, bd), s in zip(kinds, slots)]
+        pools = [torch.empty(d.n_slots * d.slot_bytes, dtype=torch.uint8, device=dev) for d in classes]
+        cache = B.moe_cache_create(classes, layer_class, E)
+        store = B.moe_store_open_memory(store_np, classes, layer_class, E)
+        copies = [torch.cuda.Stream() for _ in range(n_copy)]
+        host_bytes = {"all": total, "none": 0}[host_mode]
+        t0 = time.time()
+        p = B.moe_pipeline_create(cache, store, pools, host_tier_bytes=host_bytes,
+                                  host_preload=host_bytes > 0, io_threads=args.io_threads,
+                                  staging_rows=2 * args.io_threads, copy_streams=copies)
+        t_create = time.time() - t0
+        try:
+            if resident_first:  # every expert installed before the run
+                for l in range(L):
+                    B.moe_pipeline_prefetch(p, l, np.arange(E, dtype=np.int32))
+                B.moe_pipeline_drain(p)
+            g = torch.Generator(device=dev)
+            g.manual_seed(wl.seed * 7919 + T)
+            n_tok = args.replay_warmup + args.replay_tokens
+            logits = torch.randn((n_tok, L, T, E), generator=g, device=dev, dtype=torch.float32)
+            x0 = torch.randn((T, H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            xbuf = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+            ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+            w = torch.empty((T, k), dtype=torch.float32, device=dev)
+            ids_host = torch.empty((T, k), dtype=torch.int32, pin_memory=True)
+            table = torch.full((E,), -1, dtype=torch.int32, device=dev)
+            ws = torch.zeros(B.moe_forward_workspace_size(T, k, E, classes[0]) + 4096, dtype=torch.uint8,
+                             device=dev)
+            err = torch.zeros(1, dtype=torch.int32, device=dev)
+            ev = torch.cuda.Event()
+
+            def token(t):
+                x = x0
+                for l in range(L):
+                    c = layer_class[l]
+                    B.moe_route_topk(logits[t, l], k, topk_ids=ids, topk_w=w, err_word=err)
+                    ids_host.copy_(ids, non_blocking=True)  # the layer's routing, to the host once
+                    ev.record()
+                    ev.synchronize()
+                    B.moe_pipeline_prepare(p, l, ids_host.numpy(), table)
+                    y = xbuf[l & 1]
+                    B.moe_experts_forward(x, ids, w, E, table, pools[c], classes[c], out=y, ws=ws,
+                                          err_word=err)
+                    B.moe_pipeline_release(p, l)
+                    x = y
+
+            for t in range(args.replay_warmup):
+                token(t)
+            B.moe_pipeline_drain(p)
+            torch.cuda.synchronize()
+            before = [B.moe_pipeline_stats_get(p, c) for c in range(len(classes))]
+            t0 = time.perf_counter()
+            for t in range(args.replay_warmup, n_tok):
+                token(t)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            after = [B.moe_pipeline_stats_get(p, c) for c in range(len(classes))]
+            assert int(err.item()) == 0, f"device error word {int(err.item()):#x}"
+            assert bool(torch.isfinite(xbuf[(L - 1) & 1].float()).all())
+            per_class = []
+            copied = 0
+            for c in range(len(classes)):
+                d = {key: after[c][key] - before[c][key] for key in after[c]}
+                copied += d["bytes_copied"]
+                hits = d["hits"] + d["inflight_hits"]
+                per_class.append({
+                    "class": c, "bits_gate_up": kinds[c][0], "bits_down": kinds[c][1],
+                    "layers": n_layers_c[c], "slot_bytes": classes[c].slot_bytes,
+                    "slots": classes[c].n_slots, "requests": d["requests"],
+                    "hit_rate": round(hits / max(d["requests"], 1), 4),
+                    "misses_per_token": round((d["requests"] - hits) / args.replay_tokens, 2),
+                    "host_hits": d["host_hits"], "store_reads": d["store_reads"]})
+            return {"batch": T, "share": share, "host_tier": host_mode, "copy_streams": n_copy,
+                    "tok_s": round(T * args.replay_tokens / wall, 2),
+                    "ms_per_step": round(1000 * wall / args.replay_tokens, 3),
+                    "install_GBps": round(copied / wall / 1e9, 2),
+                    "install_bytes_per_token": int(copied / (T * args.replay_tokens)),
+                    "pipeline_create_s": round(t_create, 2),
+                    "classes": per_class}
+        finally:
+            B.moe_pipeline_destroy(p)
+            B.moe_cache_destroy(cache)
+            B.moe_store_close(store)
+            del pools
+            torch.cuda.empty_cache()
+
+    runs = []
+    for T in (1, 8):
+        runs.append(run(T, 1.0, "none", resident_first=True))
+        log(json.dumps(runs[-1]))
+        for mode in ("all", "none"):
+            runs.append(run(T, args.replay_share, mode))
+            log(json.dumps(runs[-1]))
+    main_run = next(r for r in runs if r["batch"] == 1 and r["host_tier"] == "all" and r["share"] < 1)
+    result = {
+        "metric": "mixed decode replay tok/s through the bounded cache (per-class hit rates)",
+        "value": main_run["tok_s"], "unit": "tok/s", "n_gpus": 1,
+        "steps": args.replay_tokens, "warmup": args.replay_warmup,
+        "ms_per_step": main_run["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "mixed: 48 layers x (hidden 2048, 128 experts, intermediate 768, top-8), "
+                               "4-bit experts with 6-bit down on every 4th layer (two size classes), "
+                               f"device share {args.replay_share} of each layer's experts, "
+                               "router logits N(0,1), store in host memory",
+                   "io_threads": args.io_threads, "copy_streams": args.copy_streams,
+                   "store_GB": round(total / 1e9, 3)},
+        "runs": runs,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -135,6 +286,9 @@ def main():
         sys.exit(1)
     B.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda")
+    if args.replay:
+        replay_main(args, torch, B, synth)
+        return
     if args.calibrate_copy:
         n = 1 << 30
         src = torch.ones(n, dtype=torch.uint8, device=dev)

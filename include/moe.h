@@ -384,9 +384,11 @@ int     moe_store_read(const moe_store* s, int layer, int expert, void* dst);
  *                    that do not land in a host row; io_threads..1024.
  *
  * moe_pipeline_create: `class_pools[c]` is class c's device pool (n_slots rows of
- *   slot_bytes, 256-byte aligned), `copy_stream` the stream every install copy
- *   runs on (caller-owned, default priority).  The current device is the pools'
- *   device.  The cache and store stay owned by the caller and must outlive the
+ *   slot_bytes, 256-byte aligned); `copy_streams[0..n_copy_streams)` (1 to 4,
+ *   caller-owned, default priority, not the compute stream) carry the install
+ *   copies: every copy that reads one host row or staging buffer runs on that
+ *   buffer's stream, and rows spread over the streams so copies overlap each
+ *   other.  The current device is the pools' device.  The cache and store stay owned by the caller and must outlive the
  *   pipeline; while it exists only the pipeline acquires, fills or pins entries of
  *   that cache.  NULL on error.
  * moe_pipeline_prepare: make the experts `ids[0..n)` (duplicates allowed) of
@@ -410,7 +412,8 @@ int     moe_store_read(const moe_store* s, int layer, int expert, void* dst);
  * moe_pipeline_drain: wait until every read and copy has finished.
  * moe_pipeline_stats_get: counters of one class (moe_pipeline_stats).
  * moe_pipeline_host_rows: host-tier rows of class `cls` (0 without a host tier).
- * Threads: prepare, release, prefetch, drain and destroy from one thread; the
+ * Threads: prepare, release, prefetch, drain and destroy from one thread, and
+ * prepare/release always on the same compute stream (else MOE_E_INVALID); the
  * I/O threads are internal.
  */
 typedef struct moe_pipeline_config {
@@ -435,7 +438,8 @@ typedef struct moe_pipeline_stats {
 
 typedef struct moe_pipeline moe_pipeline;
 moe_pipeline* moe_pipeline_create(moe_cache* cache, moe_store* store, void* const* class_pools,
-                                  const moe_pipeline_config* cfg, hipStream_t copy_stream);
+                                  const moe_pipeline_config* cfg, const hipStream_t* copy_streams,
+                                  int n_copy_streams);
 void    moe_pipeline_destroy(moe_pipeline* p);
 int     moe_pipeline_prepare(moe_pipeline* p, int layer, const int32_t* ids, int n,
                              int32_t* table_dev, hipStream_t compute);

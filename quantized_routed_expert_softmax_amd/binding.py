@@ -126,7 +126,7 @@ def lib() -> ctypes.CDLL:
                 "moe_store_bytes": (I64, [P]),
                 "moe_store_row_offset": (I64, [P, I32, I32]),
                 "moe_store_read": (I32, [P, I32, I32, P]),
-                "moe_pipeline_create": (P, [P, P, P, ctypes.POINTER(PipelineConfig), P]),
+                "moe_pipeline_create": (P, [P, P, P, ctypes.POINTER(PipelineConfig), P, I32]),
                 "moe_pipeline_destroy": (None, [P]),
                 "moe_pipeline_prepare": (I32, [P, I32, P, I32, P, P]),
                 "moe_pipeline_release": (I32, [P, I32, P]),
@@ -480,15 +480,18 @@ def moe_store_read(s: int, layer: int, expert: int, dst):
 
 def moe_pipeline_create(cache: int, store: int, pools: list, host_tier_bytes: int = 0,
                         host_preload: bool = False, io_threads: int = 4, staging_rows: int = 8,
-                        copy_stream=None) -> int:
-    """pools[c]: class c's device pool (uint8 tensor); copy_stream: a torch stream."""
+                        copy_streams=None) -> int:
+    """pools[c]: class c's device pool (uint8 tensor); copy_streams: torch streams (1 to 4)."""
     torch = _torch()
     ptrs = (ctypes.c_void_p * len(pools))(*[_dev_ptr(p, torch.uint8, f"pools[{i}]").value
                                            for i, p in enumerate(pools)])
     cfg = PipelineConfig(host_tier_bytes, int(bool(host_preload)), io_threads, staging_rows, 0)
-    if copy_stream is None:
-        raise ValueError("copy_stream is required")
-    h = lib().moe_pipeline_create(cache, store, ptrs, ctypes.byref(cfg), _stream(copy_stream))
+    if not copy_streams:
+        raise ValueError("copy_streams is required")
+    if not isinstance(copy_streams, (list, tuple)):
+        copy_streams = [copy_streams]
+    arr = (ctypes.c_void_p * len(copy_streams))(*[_stream(st).value for st in copy_streams])
+    h = lib().moe_pipeline_create(cache, store, ptrs, ctypes.byref(cfg), arr, len(copy_streams))
     if not h:
         raise MoeError(MOE_E_INVALID, moe_last_error())
     return h

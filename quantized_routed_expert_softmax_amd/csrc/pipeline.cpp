@@ -16,7 +16,8 @@
 // not waited for).
 //
 // Ordering without host waits.  Three event rings carry every dependency:
-//   fill ring (copy stream)    — recorded after each install copy.  The compute
+//   fill rings (one per copy   — recorded after each install copy.  The compute
+//   stream)
 //                                stream waits on it before the layer that reads the
 //                                slot; the slot stays "in flight" in the cache until
 //                                it completes; a host row or staging buffer is not
@@ -28,9 +29,10 @@
 //                                while a queued forward may still read it.
 //   table ring (compute)       — the pinned copy of a layer's expert -> slot table
 //                                is reused only after its transfer has run.
-// A ring entry may be re-recorded by a later operation on the same stream; since
-// each stream runs in order, waiting on (or querying) the later record is
-// conservative, never wrong.  Every wait targets a record made before the waiting
+// A ring entry may be re-recorded by a later operation, always on the same stream
+// (each copy stream has its own fill ring, and every copy that reads a given host
+// row or staging buffer runs on that buffer's stream); since each stream runs in
+// order, waiting on (or querying) the later record is conservative, never wrong.  Every wait targets a record made before the waiting
 // operation was enqueued, so the two streams cannot wait on each other in a cycle.
 #include <hip/hip_runtime.h>
 
@@ -201,7 +203,8 @@ int moe_store_read(const moe_store* s, int layer, int expert, void* dst)
 // --------------------------------------------------------------------------
 namespace {
 
-constexpr int kFillRing = 1024;
+constexpr int kMaxCopyStreams = 4;
+constexpr int kFillRing = 1024;  // per copy stream
 constexpr int kUseRing = 256;
 constexpr int kTableRing = 64;
 
@@ -262,7 +265,9 @@ struct moe_pipeline {
     std::vector<moe_size_class_desc> desc;
     std::vector<int> layer_class;
     std::vector<uint8_t*> pools;
-    hipStream_t copy = nullptr;
+    std::vector<hipStream_t> copies;
+    hipStream_t compute = nullptr;  // the one compute stream prepare/release run on
+    bool compute_set = false;
 
     std::vector<HostClass> host;
     std::vector<int64_t> host_of;  // [layer * E + expert] -> host row, -1 absent
@@ -271,15 +276,16 @@ struct moe_pipeline {
     std::vector<Held> held;                    // [layer]
     std::vector<moe_pipeline_stats> stats;     // [class]
 
-    hipEvent_t fill_ring[kFillRing] = {};
+    hipEvent_t fill_ring[kMaxCopyStreams * kFillRing] = {};  // entry q * kFillRing + j on stream q
     hipEvent_t use_ring[kUseRing] = {};
     hipEvent_t table_ring[kTableRing] = {};
     bool table_used[kTableRing] = {};
     int32_t* table_host = nullptr;  // pinned [kTableRing][E]
-    int64_t fill_next = 0, use_next = 0, table_next = 0;
+    int64_t fill_next[kMaxCopyStreams] = {};
+    int64_t use_next = 0, table_next = 0;
 
     mutable std::mutex mu;  // everything above that threads share
-    std::mutex copy_mu;  // copy-stream enqueue + fill-ring record
+    std::mutex copy_mu[kMaxCopyStreams];  // per copy stream: enqueue + fill-ring record
     std::condition_variable cv_jobs, cv_done;
     std::deque<Job> jobs;
     int active_jobs = 0;
@@ -298,17 +304,28 @@ struct moe_pipeline {
         return host[cls].mem + (size_t)r * (size_t)host[cls].row_bytes;
     }
 
-    // Enqueue one install copy; returns the fill-ring entry, or -1 on a HIP error.
-    int enqueue_copy(int cls, int64_t s, const uint8_t* src, int use_ev)
+    // Copy stream of a source buffer: fixed per host row / staging buffer, so every
+    // copy that reads one buffer runs on one stream.
+    int row_queue(int64_t r) const { return (int)(r % (int64_t)copies.size()); }
+
+    // Enqueue one install copy on copy stream q; returns the fill-ring entry, or
+    // -1 on a HIP error.
+    int enqueue_copy(int q, int cls, int64_t s, const uint8_t* src, int use_ev)
     {
-        std::lock_guard<std::mutex> g(copy_mu);
-        if (use_ev >= 0 && hipStreamWaitEvent(copy, use_ring[use_ev], 0) != hipSuccess) return -1;
+        std::lock_guard<std::mutex> g(copy_mu[q]);
+        const hipStream_t st = copies[(size_t)q];
+        if (use_ev >= 0 && hipStreamWaitEvent(st, use_ring[use_ev], 0) != hipSuccess) return -1;
         if (hipMemcpyAsync(slot_ptr(cls, s), src, (size_t)desc[cls].slot_bytes, hipMemcpyHostToDevice,
-                           copy) != hipSuccess)
+                           st) != hipSuccess)
             return -1;
-        const int i = (int)(fill_next++ % kFillRing);
-        if (hipEventRecord(fill_ring[i], copy) != hipSuccess) return -1;
+        const int i = q * kFillRing + (int)(fill_next[q]++ % kFillRing);
+        if (hipEventRecord(fill_ring[i], st) != hipSuccess) return -1;
         return i;
+    }
+
+    void sync_copies()
+    {
+        for (hipStream_t st : copies) hipStreamSynchronize(st);
     }
 
     // A host row that may be overwritten: least recently used, nobody reading or
@@ -376,7 +393,7 @@ struct moe_pipeline {
         host[cls].row[(size_t)r].readers++;
         host_touch(cls, r);
         lk.unlock();
-        const int ev = enqueue_copy(cls, s, host_ptr(cls, r), use_ev);
+        const int ev = enqueue_copy(row_queue(r), cls, s, host_ptr(cls, r), use_ev);
         lk.lock();
         HostRow& row = host[cls].row[(size_t)r];
         row.readers--;
@@ -438,7 +455,8 @@ struct moe_pipeline {
         uint8_t* buf = r >= 0 ? host_ptr(j.cls, r) : staging[(size_t)sidx].mem;
         lk.unlock();
         const bool read_ok = store_read(store, j.layer, j.expert, buf) == 0;
-        const int ev = read_ok ? enqueue_copy(j.cls, j.slot, buf, j.use_ev) : -1;
+        const int q = r >= 0 ? row_queue(r) : sidx % (int)copies.size();
+        const int ev = read_ok ? enqueue_copy(q, j.cls, j.slot, buf, j.use_ev) : -1;
         lk.lock();
         if (r >= 0) {
             HostRow& row = host[j.cls].row[(size_t)r];
@@ -531,7 +549,7 @@ struct moe_pipeline {
         }
         cv_jobs.notify_all();
         for (auto& t : threads) t.join();
-        if (copy) hipStreamSynchronize(copy);
+        sync_copies();
         for (auto& h : host)
             if (h.mem) hipHostFree(h.mem);
         for (auto& b : staging)
@@ -547,6 +565,17 @@ struct moe_pipeline {
 };
 
 namespace {
+
+// prepare and release must all use one compute stream: the use and table rings
+// are re-recorded on it, which is only conservative on a single in-order stream
+bool same_compute(moe_pipeline* p, hipStream_t compute)
+{
+    if (!p->compute_set) {
+        p->compute = compute;
+        p->compute_set = true;
+    }
+    return p->compute == compute;
+}
 
 bool ids_ok(const moe_pipeline* p, int layer, const int32_t* ids, int n)
 {
@@ -574,12 +603,22 @@ std::vector<int> distinct(const int32_t* ids, int n, int E)
 extern "C" {
 
 moe_pipeline* moe_pipeline_create(moe_cache* cache, moe_store* store, void* const* class_pools,
-                                  const moe_pipeline_config* cfg, hipStream_t copy_stream)
+                                  const moe_pipeline_config* cfg, const hipStream_t* copy_streams,
+                                  int n_copy_streams)
 {
-    if (!cache || !store || !class_pools || !cfg || !copy_stream) {
+    if (!cache || !store || !class_pools || !cfg || !copy_streams) {
         pfail(MOE_E_INVALID, "moe_pipeline_create: NULL argument");
         return nullptr;
     }
+    if (n_copy_streams < 1 || n_copy_streams > kMaxCopyStreams) {
+        pfail(MOE_E_INVALID, "moe_pipeline_create: need 1 to 4 copy streams");
+        return nullptr;
+    }
+    for (int q = 0; q < n_copy_streams; ++q)
+        if (!copy_streams[q]) {
+            pfail(MOE_E_INVALID, "moe_pipeline_create: NULL copy stream");
+            return nullptr;
+        }
     if (cfg->io_threads < 1 || cfg->io_threads > 64 || cfg->staging_rows < cfg->io_threads ||
         cfg->staging_rows > 1024 || cfg->host_tier_bytes < 0) {
         pfail(MOE_E_INVALID, "moe_pipeline_create: need 1 <= io_threads <= 64, "
@@ -604,7 +643,7 @@ moe_pipeline* moe_pipeline_create(moe_cache* cache, moe_store* store, void* cons
     };
     p->cache = cache;
     p->store = store;
-    p->copy = copy_stream;
+    p->copies.assign(copy_streams, copy_streams + n_copy_streams);
     p->n_classes = nc;
     p->n_layers = nl;
     p->E = E;
@@ -631,7 +670,8 @@ moe_pipeline* moe_pipeline_create(moe_cache* cache, moe_store* store, void* cons
     p->held.resize(nl);
 
     for (auto* ring : {p->fill_ring, p->use_ring, p->table_ring}) {
-        const int n = ring == p->fill_ring ? kFillRing : ring == p->use_ring ? kUseRing : kTableRing;
+        const int n = ring == p->fill_ring ? (int)p->copies.size() * kFillRing
+                      : ring == p->use_ring ? kUseRing : kTableRing;
         for (int i = 0; i < n; ++i)
             if (hipEventCreateWithFlags(&ring[i], hipEventDisableTiming) != hipSuccess)
                 return bail(MOE_E_HIP, "moe_pipeline_create: event creation failed");
@@ -706,6 +746,8 @@ int moe_pipeline_prepare(moe_pipeline* p, int layer, const int32_t* ids, int n, 
 {
     if (!ids_ok(p, layer, ids, n) || !table_dev)
         return pfail(MOE_E_INVALID, "moe_pipeline_prepare: bad arguments");
+    if (!same_compute(p, compute))
+        return pfail(MOE_E_INVALID, "moe_pipeline_prepare: another compute stream than before");
     Held& h = p->held[(size_t)layer];
     if (h.active) return pfail(MOE_E_BUSY, "moe_pipeline_prepare: layer prepared and not yet released");
     const int cls = p->cls_of(layer);
@@ -726,7 +768,7 @@ int moe_pipeline_prepare(moe_pipeline* p, int layer, const int32_t* ids, int n, 
                 std::unique_lock<std::mutex> l2(p->mu);
                 p->wait_idle(l2);
             }
-            hipStreamSynchronize(p->copy);
+            p->sync_copies();
             lk.lock();
             rc = moe_cache_acquire(p->cache, layer, e, &s, &needs_fill);
         }
@@ -794,6 +836,8 @@ int moe_pipeline_release(moe_pipeline* p, int layer, hipStream_t compute)
     if (!p || layer < 0 || layer >= p->n_layers) return pfail(MOE_E_INVALID, "moe_pipeline_release: bad arguments");
     Held& h = p->held[(size_t)layer];
     if (!h.active) return pfail(MOE_E_INVALID, "moe_pipeline_release: layer not prepared");
+    if (!same_compute(p, compute))
+        return pfail(MOE_E_INVALID, "moe_pipeline_release: another compute stream than prepare's");
     const int u = (int)(p->use_next++ % kUseRing);
     if (hipEventRecord(p->use_ring[u], compute) != hipSuccess) {
         p->unpin_all(layer);
@@ -844,7 +888,8 @@ int moe_pipeline_drain(moe_pipeline* p)
         std::unique_lock<std::mutex> lk(p->mu);
         p->wait_idle(lk);
     }
-    if (hipStreamSynchronize(p->copy) != hipSuccess) return pfail(MOE_E_HIP, "moe_pipeline_drain: copy stream");
+    for (hipStream_t st : p->copies)
+        if (hipStreamSynchronize(st) != hipSuccess) return pfail(MOE_E_HIP, "moe_pipeline_drain: copy stream");
     moe_cache_poll(p->cache);
     std::lock_guard<std::mutex> g(p->mu);
     if (p->io_error) return pfail(p->io_error, "moe_pipeline_drain: an install failed");

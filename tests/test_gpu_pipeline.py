@@ -99,17 +99,18 @@ class Replay:
 
 
 def run_pipeline(rp: Replay, ids, ws, ids_host, store, host_tier_bytes=0, preload=False,
-                 io_threads=2, staging_rows=4, drain_each=False, prefetch=False, model=None):
+                 io_threads=2, staging_rows=4, drain_each=False, prefetch=False, model=None,
+                 n_copy=1):
     """Decode steps through the pipeline; no host synchronisation between layers
     unless drain_each.  Returns (outputs, per-class stats, pools, cache tables)."""
     torch = _torch()
     pools = [torch.zeros(d.n_slots * d.slot_bytes, dtype=torch.uint8, device="cuda")
              for d in rp.classes]
     cache = B.moe_cache_create(rp.classes, rp.layer_class, E)
-    copy = torch.cuda.Stream()
+    copies = [torch.cuda.Stream() for _ in range(n_copy)]
     p = B.moe_pipeline_create(cache, store, pools, host_tier_bytes=host_tier_bytes,
                               host_preload=preload, io_threads=io_threads,
-                              staging_rows=staging_rows, copy_stream=copy)
+                              staging_rows=staging_rows, copy_streams=copies)
     try:
         table = torch.full((E,), -1, dtype=torch.int32, device="cuda")
         ws_buf = torch.zeros(B.moe_forward_workspace_size(rp.T, K, E, rp.classes[0]) + 4096,
@@ -210,7 +211,7 @@ def test_replay_overlapped_installs_without_host_waits(replay):
     store = B.moe_store_open_memory(rp.store_bytes, rp.classes, rp.layer_class, E)
     try:
         outs, stats, cstats, pools, tables, _ = run_pipeline(rp, ids, ws, host, store, io_threads=4,
-                                                             staging_rows=4)
+                                                             staging_rows=4, n_copy=2)
     finally:
         B.moe_store_close(store)
     check_outputs(outs, ref)
@@ -229,7 +230,7 @@ def test_replay_host_tier_preloaded(replay):
         model = CacheModel(rp.class_slots, rp.layer_class, E)
         outs, stats, cstats, pools, tables, host_rows = run_pipeline(
             rp, ids, ws, host, store, host_tier_bytes=rp.store_bytes.size, preload=True,
-            drain_each=True, model=model)
+            drain_each=True, model=model, n_copy=2)
     finally:
         B.moe_store_close(store)
     check_outputs(outs, ref)
@@ -252,7 +253,7 @@ def test_replay_partial_host_tier_and_perfect_guesses(replay):
     try:
         outs, stats, cstats, pools, tables, host_rows = run_pipeline(
             rp, ids, ws, host, store, host_tier_bytes=rp.store_bytes.size // 3, io_threads=3,
-            staging_rows=3, prefetch=True)
+            staging_rows=3, prefetch=True, n_copy=3)
     finally:
         B.moe_store_close(store)
     check_outputs(outs, ref)
@@ -293,7 +294,7 @@ def test_prepare_twice_without_release_is_rejected(replay):
              for d in rp.classes]
     cache = B.moe_cache_create(rp.classes, rp.layer_class, E)
     p = B.moe_pipeline_create(cache, store, pools, io_threads=1, staging_rows=1,
-                              copy_stream=torch.cuda.Stream())
+                              copy_streams=[torch.cuda.Stream()])
     try:
         table = torch.full((E,), -1, dtype=torch.int32, device="cuda")
         B.moe_pipeline_prepare(p, 0, host[0], table)
@@ -304,6 +305,8 @@ def test_prepare_twice_without_release_is_rejected(replay):
             B.moe_pipeline_release(p, 1)          # layer 1 was never prepared
         with pytest.raises(B.MoeError):
             B.moe_pipeline_prepare(p, 1, np.array([E], np.int32), table)   # id out of range
+        with pytest.raises(B.MoeError):                                    # another compute stream
+            B.moe_pipeline_prepare(p, 1, host[1], table, stream=torch.cuda.Stream())
         B.moe_pipeline_release(p, 0)
         B.moe_pipeline_drain(p)
         torch.cuda.synchronize()

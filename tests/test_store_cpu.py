@@ -82,17 +82,21 @@ def test_pipeline_create_rejects_bad_configs_before_any_gpu_call():
     s = B.moe_store_open_memory(data, classes, layer_class, E)
     try:
         pools = (ctypes.c_void_p * 2)(0x10000, 0x20000)  # never dereferenced
-        stream = ctypes.c_void_p(0x1000)
+        streams = (ctypes.c_void_p * 5)(*([0x1000] * 5))
         for threads, staging, host in ((0, 4, 0), (65, 80, 0), (4, 2, 0), (2, 4, -1)):
             cfg = B.PipelineConfig(host, 0, threads, staging, 0)
-            assert not L.moe_pipeline_create(c, s, pools, ctypes.byref(cfg), stream)
+            assert not L.moe_pipeline_create(c, s, pools, ctypes.byref(cfg), streams, 1)
             assert B.moe_last_error()
         cfg = B.PipelineConfig(0, 0, 2, 4, 0)
-        assert not L.moe_pipeline_create(None, s, pools, ctypes.byref(cfg), stream)
-        assert not L.moe_pipeline_create(c, None, pools, ctypes.byref(cfg), stream)
+        assert not L.moe_pipeline_create(None, s, pools, ctypes.byref(cfg), streams, 1)
+        assert not L.moe_pipeline_create(c, None, pools, ctypes.byref(cfg), streams, 1)
+        for n in (0, 5):                                   # 1 to 4 copy streams
+            assert not L.moe_pipeline_create(c, s, pools, ctypes.byref(cfg), streams, n)
+        nulls = (ctypes.c_void_p * 2)(0x1000, None)
+        assert not L.moe_pipeline_create(c, s, pools, ctypes.byref(cfg), nulls, 2)
         s3 = B.moe_store_open_memory(rows_bytes(classes, [0, 1, 0], E), classes, [0, 1, 0], E)
         try:   # layer count differs from the cache's
-            assert not L.moe_pipeline_create(c, s3, pools, ctypes.byref(cfg), stream)
+            assert not L.moe_pipeline_create(c, s3, pools, ctypes.byref(cfg), streams, 1)
         finally:
             B.moe_store_close(s3)
     finally:
