@@ -62,8 +62,9 @@ def _load():
             lib.oracle_dequant.argtypes = [P, i32, i32, i32, i32, i32, P]
             lib.oracle_layer.argtypes = [P, i32, i32, i32, i32, i32, P, P, i32, i32, P, P, i64,
                                          P, i32, P, i32]
+            lib.oracle_router_logits.argtypes = [P, i32, i32, P, i32, i32, P]
             for f in ("oracle_softmax", "oracle_route", "oracle_sort", "oracle_layout",
-                      "oracle_dequant", "oracle_layer"):
+                      "oracle_dequant", "oracle_layer", "oracle_router_logits"):
                 getattr(lib, f).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -164,4 +165,20 @@ def layer(x_bf16: np.ndarray, ids: np.ndarray, w: np.ndarray, slot_table: np.nda
     out = np.empty((n_out, H), dtype=np.float64)
     _check(_load().oracle_layer(_p(x), T, H, I, bits_gu, bits_d, _p(a), _p(ww), k, E, _p(st),
                                 _p(pl), n_slots, _p(tk), n_out, _p(out), threads))
+    return out
+
+
+def router_logits(x_bf16: np.ndarray, w_bf16: np.ndarray) -> np.ndarray:
+    """Router logits of consecutive layers on one set of hidden states, fp64:
+    logits[m, t, e] = sum_i x[t, i] * Wr_m[e, i] ("RFC ...", How the prototype
+    works, Reads: the next layers' routers run on the current hidden states to
+    guess their experts).  x: bf16 bits [T, H]; w: bf16 bits [n, E, H]."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    T, H = x.shape
+    n, E, H2 = w.shape
+    if H2 != H:
+        raise ValueError("router width differs from the hidden size")
+    out = np.empty((n, T, E), dtype=np.float64)
+    _check(_load().oracle_router_logits(_p(x), T, H, _p(w), n, E, _p(out)))
     return out

@@ -21,6 +21,10 @@
  *  - Sort by expert and passes of at most 64 hit experts ("POC: Experts
  *    offload", commit messages: sorted prefill runs 64 experts at a time; RFC,
  *    How the prototype works, Prefill).
+ *  - Router logits for the lookahead guesses ("RFC ...", How the prototype
+ *    works, Reads: the next two layers' experts are guessed by running their
+ *    routers on the current hidden states): logits[m][t][e] = sum_i x[t][i] *
+ *    Wr_m[e][i] in fp64 over the bf16 values, a plain linear map per layer.
  *  - The layer ("RFC ...", How the prototype works: experts are gated,
  *    concatenated, untransposed and without bias, run on the slot pool through a
  *    per-layer expert -> slot table; quantized experts in a group-wise affine
@@ -355,5 +359,26 @@ int oracle_layer(const uint16_t* x, int T, int H, int I, int bits_gu, int bits_d
         free(xt);
         free(h);
     }
+    return OR_OK;
+}
+
+/*
+ * Router logits of n_mats consecutive layers on the same hidden states:
+ * logits[m][t][e] = sum_i x[t][i] * w[m][e][i], x bf16 [T][H], w bf16
+ * [n_mats][E][H], accumulated in fp64 with i ascending.
+ */
+int oracle_router_logits(const uint16_t* x, int T, int H, const uint16_t* w, int n_mats, int E,
+                         double* logits)
+{
+    if (!x || !w || !logits || T < 0 || H < 1 || n_mats < 1 || E < 1) return OR_INVALID;
+    for (int m = 0; m < n_mats; m++)
+        for (int t = 0; t < T; t++)
+            for (int e = 0; e < E; e++) {
+                const uint16_t* wr = w + ((size_t)m * E + e) * (size_t)H;
+                const uint16_t* xr = x + (size_t)t * H;
+                double acc = 0.0;
+                for (int i = 0; i < H; i++) acc += bf16_to_double(xr[i]) * bf16_to_double(wr[i]);
+                logits[((size_t)m * T + t) * E + e] = acc;
+            }
     return OR_OK;
 }
