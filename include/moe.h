@@ -169,6 +169,22 @@ int moe_size_class_init(moe_size_class_desc* d, int H, int I, int bits_gu, int b
                         int group, int align, int64_t n_slots);
 
 /*
+ * Router logits of n_mats consecutive layers on one set of hidden states:
+ * logits[m][t][e] = sum_i x[t][i] * w[m][e][i].  x: bf16 [T, H] (device);
+ * w: bf16 [n_mats, E, H], the routers of the layers stacked in order (device);
+ * logits: fp32 [n_mats, T, E] (device), fp32 sums of exact bf16 products.
+ * These logits feed moe_route_topk to guess the experts the next layers will
+ * ask for, before their hidden states exist.  Source: [RFC] "How the prototype
+ * works", Reads bullet (the next two layers' experts are guessed by running
+ * their routers on the current hidden states and read in the background).
+ * Limits: H a positive multiple of 8, 1 <= E <= 1024, 1 <= n_mats <= 8, x and w
+ * 16-byte aligned; T = 0 is a no-op.  Sized for decode batches (each four tokens
+ * re-read the routers, from L2).
+ */
+int moe_router_logits(const void* x, int T, int H, const void* w, int n_mats, int E, float* logits,
+                      hipStream_t stream);
+
+/*
  * Router: softmax over E logits, top-k, renormalised weights, per the routing
  * numeric contract above.  In MOE_ROUTE_SUBST mode every expert with
  * slot_table[e] >= 0 gets L times the token's probability range added to its

@@ -96,6 +96,7 @@ def lib() -> ctypes.CDLL:
             sig = {
                 "moe_size_class_init": (I32, [D, I32, I32, I32, I32, I32, I32, I64]),
                 "moe_route_topk": (I32, [P, I32, I32, I32, I32, F32, P, P, P, P, P]),
+                "moe_router_logits": (I32, [P, I32, I32, P, I32, I32, P, P]),
                 "moe_sort_by_expert": (I32, [P, I32, I32, I32, I32, P, P, P, P, SZ, P, P]),
                 "moe_sort_workspace_size": (SZ, [I32, I32, I32]),
                 "moe_pass_table_size": (I32, [I32, I32]),
@@ -216,6 +217,23 @@ def moe_route_topk(logits, k: int, mode: int = MOE_ROUTE_PLAIN, L: float = 0.0, 
                                 _dev_ptr(topk_w, torch.float32, "topk_w"),
                                 _opt_ptr(err_word, torch.int32, "err_word"), _stream(stream)))
     return topk_ids, topk_w
+
+
+def moe_router_logits(x, w, logits=None, stream=None):
+    """Router logits of consecutive layers: x bf16 [T, H], w bf16 [n, E, H] -> fp32 [n, T, E]."""
+    torch = _torch()
+    T, H = x.shape
+    n, E, H2 = w.shape
+    if H2 != H:
+        raise ValueError(f"router width {H2} differs from the hidden size {H}")
+    if logits is None:
+        logits = torch.empty((n, T, E), dtype=torch.float32, device=x.device)
+    elif tuple(logits.shape) != (n, T, E):
+        raise ValueError("logits must be [n, T, E]")
+    _check(lib().moe_router_logits(_dev_ptr(x, torch.bfloat16, "x", 2), T, H,
+                                   _dev_ptr(w, torch.bfloat16, "w", 3), n, E,
+                                   _dev_ptr(logits, torch.float32, "logits", 3), _stream(stream)))
+    return logits
 
 
 def moe_pass_table_size(E: int, pass_experts: int = PASS_EXPERTS) -> int:

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["route.hip", "sort.hip", "gemv.hip", "decode.hip", "mfma.hip", "api.cpp", "cache.cpp", "pipeline.cpp"]
+SOURCES = ["router.hip", "route.hip", "sort.hip", "gemv.hip", "decode.hip", "mfma.hip", "api.cpp", "cache.cpp", "pipeline.cpp"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -164,6 +164,22 @@ int moe_route_topk(const float* logits, int T, int E, int k, int mode, float L,
     return MOE_OK;
 }
 
+int moe_router_logits(const void* x, int T, int H, const void* w, int n_mats, int E, float* logits,
+                      hipStream_t stream)
+{
+    if (T < 0) return fail(MOE_E_INVALID, "T < 0");
+    if (H < 8 || H % 8) return fail(MOE_E_INVALID, "H must be a positive multiple of 8 (got %d)", H);
+    if (E < 1 || E > 1024) return fail(MOE_E_INVALID, "E must be in [1, 1024] (got %d)", E);
+    if (n_mats < 1 || n_mats > 8) return fail(MOE_E_INVALID, "n_mats must be in [1, 8] (got %d)", n_mats);
+    if (T == 0) return MOE_OK;
+    if (!x || !w || !logits) return fail(MOE_E_INVALID, "NULL buffer");
+    if (!aligned(x, 16) || !aligned(w, 16)) return fail(MOE_E_INVALID, "x and w need 16-byte alignment");
+    hipError_t e = moe::launch_router_logits((const uint16_t*)x, T, H, (const uint16_t*)w, n_mats, E,
+                                             logits, stream);
+    if (e != hipSuccess) return hip_fail(e, "router logits launch");
+    return MOE_OK;
+}
+
 int moe_pass_table_size(int E, int pass_experts)
 {
     if (E < 1 || pass_experts < 1) return 0;

@@ -27,6 +27,11 @@ struct SortView {
 hipError_t launch_route(const float* logits, int T, int E, int k, int mode, float L,
                         const int32_t* table, int32_t* ids, float* w, uint32_t* err, hipStream_t s);
 
+// Router logits of n_mats consecutive layers: logits [n_mats][T][E] fp32 from
+// x bf16 [T][H] and w bf16 [n_mats][E][H].
+hipError_t launch_router_logits(const uint16_t* x, int T, int H, const uint16_t* w, int n_mats, int E,
+                                float* logits, hipStream_t s);
+
 size_t sort_ws_bytes(int T, int k, int E);
 hipError_t launch_sort(const int32_t* ids, int T, int k, int E, int P, int32_t* offsets,
                        int32_t* sorted_pairs, int32_t* pass_table, void* ws, uint32_t* err,

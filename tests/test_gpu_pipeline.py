@@ -315,3 +315,101 @@ def test_prepare_twice_without_release_is_rejected(replay):
         B.moe_pipeline_destroy(p)
         B.moe_cache_destroy(cache)
         B.moe_store_close(store)
+
+
+class RouterModel:
+    """A residual decode stack driven by routers: layer l routes with its router
+    on x_l, and x_{l+1} = x_l + moe_l(x_l).  The lookahead runs the routers of
+    layers l+1 and l+2 on x_l too, to guess their experts ("RFC ...", How the
+    prototype works, Reads bullet)."""
+
+    def __init__(self, rp: Replay, seed=7):
+        torch = _torch()
+        rng = synth.rng_for(seed, 9)
+        w = (rng.standard_normal((rp.L, E, H)) / np.sqrt(H)).astype(np.float32)
+        self.routers = torch.from_numpy(synth.f32_to_bf16_bits(w).view(np.int16)).cuda().view(torch.bfloat16)
+        self.rp = rp
+
+    def run(self, forward, prepare=None, prefetch=None, release=None, ahead=2):
+        """Decode every token; forward(l, x, ids, w) returns moe_l(x).  Returns the
+        per-layer outputs and the routed ids of every (token, layer)."""
+        torch = _torch()
+        rp = self.rp
+        outs, routed = [], []
+        for t in range(rp.tokens):
+            x = torch.from_numpy(rp.x0[t].view(np.int16)).cuda().view(torch.bfloat16)
+            for l in range(rp.L):
+                n = min(1 + ahead, rp.L - l)
+                logits = B.moe_router_logits(x, self.routers[l:l + n])
+                ids, w = B.moe_route_topk(logits.view(n * rp.T, E), K)
+                ids_h = ids.cpu().numpy()          # this layer's routing + the guesses
+                routed.append(ids_h[:rp.T].copy())
+                if prepare is not None:
+                    prepare(l, ids_h[:rp.T])
+                if prefetch is not None:
+                    for a in range(1, n):
+                        prefetch(l + a, ids_h[a * rp.T:(a + 1) * rp.T])
+                y = forward(l, x, ids[:rp.T], w[:rp.T])
+                if release is not None:
+                    release(l)
+                x = x + y
+                outs.append(y)
+        torch.cuda.synchronize()
+        return [o.cpu() for o in outs], routed
+
+
+def test_lookahead_guesses_match_resident_run_and_cut_misses():
+    """Guesses of the next two layers' experts, issued from the current hidden
+    state, start installs before those layers route; outputs stay bit-identical
+    to an all-resident run of the same router-driven stack (the guesses change
+    where experts sit, never what a layer computes), and they cut the demand
+    misses of the same routing sequence."""
+    torch = _torch()
+    rp = Replay(seed=3, tokens=5, T=1)
+    model = RouterModel(rp)
+    full_pools = []
+    for l in range(rp.L):
+        full_pools.append(torch.from_numpy(np.ascontiguousarray(
+            np.stack([rp.row(l, e) for e in range(E)]))).cuda().view(-1))
+    ident = torch.arange(E, dtype=torch.int32, device="cuda")
+    ws_ref = torch.zeros(B.moe_forward_workspace_size(rp.T, K, E, rp.full[0]) + 4096,
+                         dtype=torch.uint8, device="cuda")
+
+    def fwd_ref(l, x, ids, w):
+        return B.moe_experts_forward(x, ids, w, E, ident, full_pools[l], rp.full[rp.layer_class[l]], ws=ws_ref)
+
+    ref, ref_ids = model.run(fwd_ref)
+    misses = {}
+    for ahead in (0, 2):
+        store = B.moe_store_open_memory(rp.store_bytes, rp.classes, rp.layer_class, E)
+        pools = [torch.zeros(d.n_slots * d.slot_bytes, dtype=torch.uint8, device="cuda") for d in rp.classes]
+        cache = B.moe_cache_create(rp.classes, rp.layer_class, E)
+        p = B.moe_pipeline_create(cache, store, pools, host_tier_bytes=rp.store_bytes.size,
+                                  host_preload=True, io_threads=2, staging_rows=2,
+                                  copy_streams=[torch.cuda.Stream(), torch.cuda.Stream()])
+        table = torch.full((E,), -1, dtype=torch.int32, device="cuda")
+        ws_buf = torch.zeros(B.moe_forward_workspace_size(rp.T, K, E, rp.classes[0]) + 4096,
+                             dtype=torch.uint8, device="cuda")
+        try:
+            def fwd(l, x, ids, w):
+                c = rp.layer_class[l]
+                return B.moe_experts_forward(x, ids, w, E, table, pools[c], rp.classes[c], ws=ws_buf)
+
+            got, got_ids = model.run(
+                fwd, prepare=lambda l, ids: B.moe_pipeline_prepare(p, l, ids, table),
+                prefetch=lambda l, ids: B.moe_pipeline_prefetch(p, l, ids),
+                release=lambda l: B.moe_pipeline_release(p, l), ahead=ahead)
+            B.moe_pipeline_drain(p)
+            stats = [B.moe_pipeline_stats_get(p, c) for c in range(len(rp.classes))]
+        finally:
+            B.moe_pipeline_destroy(p)
+            B.moe_cache_destroy(cache)
+            B.moe_store_close(store)
+        assert all(np.array_equal(a, b) for a, b in zip(got_ids, ref_ids))
+        check_outputs(got, ref)
+        m = sum(st["requests"] - st["hits"] - st["inflight_hits"] for st in stats)
+        prefetches = sum(st["prefetches"] for st in stats)
+        assert sum(st["host_hits"] for st in stats) == m + prefetches
+        assert (prefetches > 0) == (ahead > 0)
+        misses[ahead] = m
+    assert misses[2] < misses[0]
