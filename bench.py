@@ -164,11 +164,12 @@ def replay_main(args, torch, B, synth):
     gr.manual_seed(wl.seed * 104729 + 1)
     routers = (torch.randn((L, E, H), generator=gr, device=dev) / float(np.sqrt(H))).to(torch.bfloat16)
 
-    def run(T, share, host_mode, resident_first=False, n_copy=args.copy_streams, ahead=None):
+    def run(T, share, host_mode, resident_first=False, n_copy=args.copy_streams, ahead=None,
+            policy=B.MOE_EVICT_LRU, per_layer=False):
         slots = [max(int(round(share * E)) * n, T * k) for n in n_layers_c]
         classes = [B.moe_size_class_init(H, I, bg, bd, s) for (bg, bd), s in zip(kinds, slots)]
         pools = [torch.empty(d.n_slots * d.slot_bytes, dtype=torch.uint8, device=dev) for d in classes]
-        cache = B.moe_cache_create(classes, layer_class, E)
+        cache = B.moe_cache_create(classes, layer_class, E, policy=policy, per_layer=per_layer)
         store = B.moe_store_open_memory(store_np, classes, layer_class, E)
         copies = [torch.cuda.Stream() for _ in range(n_copy)]
         host_bytes = {"all": total, "none": 0}[host_mode]
@@ -270,6 +271,7 @@ def replay_main(args, torch, B, synth):
                     "host_hits": d["host_hits"], "store_reads": d["store_reads"]})
             return {"batch": T, "share": share, "host_tier": host_mode, "copy_streams": n_copy,
                     "routing": "logits N(0,1)" if ahead is None else f"routers on x_l, {ahead} layers guessed",
+                    "eviction": ("LFU" if policy == B.MOE_EVICT_LFU else "LRU") + (" per layer" if per_layer else " per class"),
                     "tok_s": round(T * args.replay_tokens / wall, 2),
                     "ms_per_step": round(1000 * wall / args.replay_tokens, 3),
                     "install_GBps": round(copied / wall / 1e9, 2),
@@ -324,10 +326,14 @@ def replay_main(args, torch, B, synth):
         for ahead in (0, 2):  # router-driven stack, without and with the lookahead guesses
             runs.append(run(T, args.replay_share, "all", ahead=ahead))
             log(json.dumps(runs[-1]))
+        if T == 1:  # eviction variants on the router-driven stack with guesses
+            for policy, per_layer in ((B.MOE_EVICT_LFU, False), (B.MOE_EVICT_LRU, True)):
+                runs.append(run(T, args.replay_share, "all", ahead=2, policy=policy, per_layer=per_layer))
+                log(json.dumps(runs[-1]))
         runs.append(run(T, 1.0, "none", resident_first=True, ahead=0))
         log(json.dumps(runs[-1]))
     main_run = next(r for r in runs if r["batch"] == 1 and r["host_tier"] == "all" and r["share"] < 1
-                    and r["routing"].startswith("logits"))
+                    and r["routing"].startswith("logits") and r["eviction"] == "LRU per class")
     result = {
         "metric": "mixed decode replay tok/s through the bounded cache (per-class hit rates)",
         "value": main_run["tok_s"], "unit": "tok/s", "n_gpus": 1,

@@ -319,6 +319,25 @@ int moe_cache_install(void* slot_pool, const moe_size_class_desc* d, int64_t slo
 typedef struct moe_cache moe_cache;
 moe_cache* moe_cache_create(const moe_size_class_desc* classes, int n_classes,
                             const int32_t* layer_class, int n_layers, int E);
+
+/*
+ * Eviction variants.  Sources: [RFC] "How the prototype works", Cache bullet (LRU,
+ * optional LFU); [CLASS] PR description (one LRU per class, or one per layer with
+ * --per-layer; every layer keeps the same share).
+ * policy MOE_EVICT_LRU: the least recently used candidate goes.  MOE_EVICT_LFU:
+ *   the candidate with the fewest acquires since it took its expert goes, ties to
+ *   the least recently used.  A candidate is neither pinned nor in flight; empty
+ *   slots always go first.
+ * per_layer 0: one eviction order per class (moe_cache_create).  1: the class's
+ *   n_slots are split between its layers in layer order, each a contiguous run of
+ *   n_slots / L_c slots (the first n_slots % L_c layers one more), each with its
+ *   own order; a layer never evicts another layer's expert.
+ */
+#define MOE_EVICT_LRU 0
+#define MOE_EVICT_LFU 1
+moe_cache* moe_cache_create_ex(const moe_size_class_desc* classes, int n_classes,
+                               const int32_t* layer_class, int n_layers, int E, int policy,
+                               int per_layer);
 void moe_cache_destroy(moe_cache* c);
 int  moe_cache_acquire(moe_cache* c, int layer, int expert, int64_t* slot, int* needs_fill);
 int  moe_cache_fill_done(moe_cache* c, int layer, int expert, hipEvent_t ev);

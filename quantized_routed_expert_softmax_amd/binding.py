@@ -41,6 +41,8 @@ MOE_PATH_MFMA = 2
 MOE_PATH_GEMV3 = 3
 MOE_SRC_HOST = 0
 MOE_SRC_DEVICE = 1
+MOE_EVICT_LRU = 0
+MOE_EVICT_LFU = 1
 
 PASS_EXPERTS = 64
 
@@ -106,6 +108,7 @@ def lib() -> ctypes.CDLL:
                 "moe_layer_forward": (I32, [P, I32, I32, I32, I32, F32, P, P, P, D, P, P, P, P, SZ, P, P]),
                 "moe_cache_install": (I32, [P, D, I64, P, I32, P, P]),
                 "moe_cache_create": (P, [D, I32, P, I32, I32]),
+                "moe_cache_create_ex": (P, [D, I32, P, I32, I32, I32, I32]),
                 "moe_cache_destroy": (None, [P]),
                 "moe_cache_acquire": (I32, [P, I32, I32, ctypes.POINTER(I64), ctypes.POINTER(I32)]),
                 "moe_cache_fill_done": (I32, [P, I32, I32, P]),
@@ -343,10 +346,14 @@ def moe_cache_install(slot_pool, desc: SizeClassDesc, slot: int, src, stream=Non
 # --------------------------------------------------------------------------- #
 # host cache                                                                   #
 # --------------------------------------------------------------------------- #
-def moe_cache_create(classes: list[SizeClassDesc], layer_class: list[int], E: int) -> int:
+def moe_cache_create(classes: list[SizeClassDesc], layer_class: list[int], E: int,
+                     policy: int = MOE_EVICT_LRU, per_layer: bool = False) -> int:
     arr = (SizeClassDesc * len(classes))(*classes)
     lc = (ctypes.c_int32 * len(layer_class))(*layer_class)
-    h = lib().moe_cache_create(arr, len(classes), lc, len(layer_class), E)
+    if policy == MOE_EVICT_LRU and not per_layer:
+        h = lib().moe_cache_create(arr, len(classes), lc, len(layer_class), E)
+    else:
+        h = lib().moe_cache_create_ex(arr, len(classes), lc, len(layer_class), E, policy, int(per_layer))
     if not h:
         raise MoeError(MOE_E_INVALID, moe_last_error())
     return h

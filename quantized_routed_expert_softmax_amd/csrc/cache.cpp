@@ -1,6 +1,6 @@
-// cache.cpp — host side of the bounded expert cache: size classes, one LRU per
-// class, per-layer expert -> slot tables, reservation of slots whose fill is in
-// flight.
+// cache.cpp — host side of the bounded expert cache: size classes, one eviction
+// order per class (or per layer), per-layer expert -> slot tables, reservation of
+// slots whose fill is in flight.
 //
 // Sources: "RFC: stream MoE experts from disk in from_pretrained", How the
 // prototype works, Cache (one preallocated pool of expert slots, LRU, per-layer
@@ -10,10 +10,18 @@
 // "moe: expert slots in size classes", PR description and the ExpertCache
 // constructor in its review (layers grouped by bytes per expert; each group has
 // its own slots and LRU; slots of a class are contiguous; empty slots sit at the
-// LRU's back and are taken first; budget never moves between classes).
+// LRU's back and are taken first; budget never moves between classes; with
+// --per-layer every layer has its own LRU and the same share); the RFC's Cache
+// bullet (LRU, optional LFU).
 //
-// All operations are O(1) (list splice + table lookup) and guarded by one mutex:
-// fills may be reported from I/O threads.
+// A class's slots form one partition (shared LRU) or one partition per layer of
+// the class (per-layer mode: slots split as evenly as possible, in layer order,
+// contiguous).  Each partition keeps its slots in a recency list.  LRU evicts the
+// least recently used candidate; LFU evicts the candidate with the fewest uses
+// since it became resident, ties to the least recently used.  A candidate is
+// neither pinned nor in flight; empty slots always go first.  Hits, touches and
+// LRU victims are O(1) (list splice + table lookup); an LFU victim scans its
+// partition.  One mutex guards everything: fills may be reported from I/O threads.
 #include <hip/hip_runtime.h>
 
 #include <cstring>
@@ -29,21 +37,30 @@ struct CacheSlot {
     int32_t layer = -1;
     int32_t expert = -1;
     int32_t pins = 0;
+    int32_t part = 0;  // partition of the class that owns the slot
+    int64_t uses = 0;  // acquires since the slot took its current expert
     bool inflight = false;
     hipEvent_t ev = nullptr;
     std::list<int64_t>::iterator it;
 };
 
+struct CachePart {
+    std::list<int64_t> lru;  // front = most recently used, back = least
+};
+
 struct CacheClass {
     moe_size_class_desc desc;
     std::vector<CacheSlot> slots;
-    std::list<int64_t> lru;  // front = most recently used, back = next victim
+    std::vector<CachePart> parts;
     int64_t hits = 0, misses = 0, evictions = 0;
 };
 
 struct moe_cache {
     std::vector<CacheClass> classes;
     std::vector<int32_t> layer_class;
+    std::vector<int32_t> layer_part;  // partition of the layer within its class
+    int policy = MOE_EVICT_LRU;
+    int per_layer = 0;
     int E = 0;
     std::vector<std::vector<int64_t>> table;  // [layer][expert] -> slot, -1 absent
     int64_t hits = 0, misses = 0, evictions = 0;
@@ -70,6 +87,27 @@ bool layer_ok(const moe_cache* c, int layer, int expert)
     return c && layer >= 0 && layer < (int)c->layer_class.size() && expert >= 0 && expert < c->E;
 }
 
+// The victim of a partition: an empty slot if any (they sit at the back), else the
+// least recently used (LRU) or least used, then least recently used (LFU)
+// candidate.  -1 when every slot is pinned or in flight.
+int64_t pick_victim(moe_cache* c, CacheClass& k, CachePart& part)
+{
+    int64_t best = -1;
+    int64_t best_uses = 0;
+    for (auto it = part.lru.rbegin(); it != part.lru.rend(); ++it) {
+        CacheSlot& cs = k.slots[(size_t)*it];
+        poll_slot(cs);
+        if (cs.pins > 0 || cs.inflight) continue;
+        if (cs.layer < 0) return *it;  // empty
+        if (c->policy == MOE_EVICT_LRU) return *it;
+        if (best < 0 || cs.uses < best_uses) {  // strict: ties stay with the less recent
+            best = *it;
+            best_uses = cs.uses;
+        }
+    }
+    return best;
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,8 +115,19 @@ extern "C" {
 moe_cache* moe_cache_create(const moe_size_class_desc* classes, int n_classes,
                             const int32_t* layer_class, int n_layers, int E)
 {
+    return moe_cache_create_ex(classes, n_classes, layer_class, n_layers, E, MOE_EVICT_LRU, 0);
+}
+
+moe_cache* moe_cache_create_ex(const moe_size_class_desc* classes, int n_classes,
+                               const int32_t* layer_class, int n_layers, int E, int policy,
+                               int per_layer)
+{
     if (!classes || n_classes < 1 || !layer_class || n_layers < 1 || E < 1) {
         cache_fail(MOE_E_INVALID, "moe_cache_create: bad arguments");
+        return nullptr;
+    }
+    if (policy != MOE_EVICT_LRU && policy != MOE_EVICT_LFU) {
+        cache_fail(MOE_E_INVALID, "moe_cache_create: unknown eviction policy");
         return nullptr;
     }
     for (int l = 0; l < n_layers; ++l)
@@ -89,7 +138,10 @@ moe_cache* moe_cache_create(const moe_size_class_desc* classes, int n_classes,
     moe_cache* c = new (std::nothrow) moe_cache;
     if (!c) return nullptr;
     c->E = E;
+    c->policy = policy;
+    c->per_layer = per_layer ? 1 : 0;
     c->layer_class.assign(layer_class, layer_class + n_layers);
+    c->layer_part.assign(n_layers, 0);
     c->table.assign(n_layers, std::vector<int64_t>(E, -1));
     c->classes.resize(n_classes);
     for (int ci = 0; ci < n_classes; ++ci) {
@@ -100,10 +152,26 @@ moe_cache* moe_cache_create(const moe_size_class_desc* classes, int n_classes,
             cache_fail(MOE_E_INVALID, "moe_cache_create: negative slot count");
             return nullptr;
         }
+        int n_parts = 1;
+        if (c->per_layer) {
+            n_parts = 0;
+            for (int l = 0; l < n_layers; ++l)
+                if (layer_class[l] == ci) c->layer_part[l] = n_parts++;
+            if (n_parts == 0) n_parts = 1;  // a class no layer uses
+        }
+        k.parts.resize((size_t)n_parts);
         k.slots.resize((size_t)k.desc.n_slots);
-        for (int64_t s = 0; s < k.desc.n_slots; ++s) {
-            k.lru.push_back(s);  // empty slots at the back: taken first
-            k.slots[(size_t)s].it = std::prev(k.lru.end());
+        // partition p owns a contiguous run of n/P (+1 for the first n % P) slots
+        const int64_t base = k.desc.n_slots / n_parts, extra = k.desc.n_slots % n_parts;
+        int64_t s = 0;
+        for (int pi = 0; pi < n_parts; ++pi) {
+            const int64_t cnt = base + (pi < extra ? 1 : 0);
+            for (int64_t i = 0; i < cnt; ++i, ++s) {
+                CachePart& part = k.parts[(size_t)pi];
+                part.lru.push_back(s);  // empty slots at the back: taken first
+                k.slots[(size_t)s].it = std::prev(part.lru.end());
+                k.slots[(size_t)s].part = pi;
+            }
         }
     }
     return c;
@@ -140,24 +208,23 @@ int moe_cache_acquire(moe_cache* c, int layer, int expert, int64_t* slot, int* n
         return cache_fail(MOE_E_INVALID, "moe_cache_acquire: bad arguments");
     std::lock_guard<std::mutex> lock(c->mu);
     CacheClass& k = c->classes[c->layer_class[layer]];
+    CachePart& part = k.parts[(size_t)c->layer_part[layer]];
     *needs_fill = 0;
     int64_t s = c->table[layer][expert];
     if (s >= 0) {
         CacheSlot& cs = k.slots[(size_t)s];
         poll_slot(cs);
         *slot = s;
-        k.lru.splice(k.lru.begin(), k.lru, cs.it);
+        part.lru.splice(part.lru.begin(), part.lru, cs.it);
+        ++cs.uses;
         if (cs.inflight) return MOE_E_BUSY;
         ++c->hits;
         ++k.hits;
         return MOE_OK;
     }
-    // miss: the least recently used slot that is neither pinned nor in flight
-    for (auto it = k.lru.rbegin(); it != k.lru.rend(); ++it) {
-        CacheSlot& cs = k.slots[(size_t)*it];
-        poll_slot(cs);
-        if (cs.pins > 0 || cs.inflight) continue;
-        const int64_t v = *it;
+    const int64_t v = pick_victim(c, k, part);
+    if (v >= 0) {
+        CacheSlot& cs = k.slots[(size_t)v];
         if (cs.layer >= 0) {
             c->table[cs.layer][cs.expert] = -1;
             ++c->evictions;
@@ -165,10 +232,11 @@ int moe_cache_acquire(moe_cache* c, int layer, int expert, int64_t* slot, int* n
         }
         cs.layer = layer;
         cs.expert = expert;
+        cs.uses = 1;
         cs.inflight = true;
         cs.ev = nullptr;
         c->table[layer][expert] = v;
-        k.lru.splice(k.lru.begin(), k.lru, cs.it);
+        part.lru.splice(part.lru.begin(), part.lru, cs.it);
         ++c->misses;
         ++k.misses;
         *slot = v;
@@ -211,9 +279,11 @@ int moe_cache_abort_fill(moe_cache* c, int layer, int expert)
     c->table[layer][expert] = -1;
     cs.layer = -1;
     cs.expert = -1;
+    cs.uses = 0;
     cs.inflight = false;
     cs.ev = nullptr;
-    k.lru.splice(k.lru.end(), k.lru, cs.it);
+    CachePart& part = k.parts[(size_t)cs.part];
+    part.lru.splice(part.lru.end(), part.lru, cs.it);
     return MOE_OK;
 }
 

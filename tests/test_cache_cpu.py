@@ -15,10 +15,10 @@ import pytest
 from quantized_routed_expert_softmax_amd import binding as B
 
 
-def make(n_a=4, n_b=2, layers=(0, 0, 1), E=8):
+def make(n_a=4, n_b=2, layers=(0, 0, 1), E=8, policy=B.MOE_EVICT_LRU, per_layer=False):
     a = B.moe_size_class_init(256, 128, 4, 4, n_a)
     b = B.moe_size_class_init(256, 128, 4, 6, n_b)
-    return B.moe_cache_create([a, b], list(layers), E)
+    return B.moe_cache_create([a, b], list(layers), E, policy=policy, per_layer=per_layer)
 
 
 def fill(c, layer, expert):
@@ -162,19 +162,24 @@ def test_bad_arguments():
         B.moe_cache_destroy(c)
 
 
-def test_per_class_stats_and_tables_match_the_reference_model():
+@pytest.mark.parametrize("policy", [B.MOE_EVICT_LRU, B.MOE_EVICT_LFU])
+@pytest.mark.parametrize("per_layer", [False, True])
+def test_per_class_stats_and_tables_match_the_reference_model(policy, per_layer):
     """Two classes, layers interleaved, batches of distinct experts acquired as a
     layer's prepare does: every slot, table and per-class counter agrees with the
-    plain list model."""
+    plain list model, for LRU and LFU, shared per class or split per layer."""
     from lru_model import CacheModel
-    rng = np.random.default_rng(11)
-    E, layer_class, slots = 10, [0, 1, 0, 0, 1], [9, 5]
-    c = make(n_a=slots[0], n_b=slots[1], layers=layer_class, E=E)
-    model = CacheModel(slots, layer_class, E)
+    rng = np.random.default_rng(11 + policy + 2 * per_layer)
+    E, layer_class, slots = 10, [0, 1, 0, 0, 1], [13, 9]   # 13 over 3 layers: 5 + 4 + 4
+    c = make(n_a=slots[0], n_b=slots[1], layers=layer_class, E=E, policy=policy, per_layer=per_layer)
+    model = CacheModel(slots, layer_class, E, lfu=policy == B.MOE_EVICT_LFU, per_layer=per_layer)
+    # popular experts (Zipf-like) so that LFU and LRU choose differently
+    popularity = 1.0 / np.arange(1, E + 1)
+    popularity /= popularity.sum()
     try:
-        for step in range(300):
+        for step in range(400):
             layer = int(rng.integers(len(layer_class)))
-            ids = rng.integers(0, E, size=int(rng.integers(1, 5)))
+            ids = rng.choice(E, size=int(rng.integers(1, 5)), p=popularity)
             expect = model.prepare(layer, ids)
             got = []
             for e, _, _ in expect:
@@ -198,6 +203,12 @@ def test_per_class_stats_and_tables_match_the_reference_model():
         assert B.moe_cache_shape(c) == (2, len(layer_class), E)
         d = B.moe_cache_class_desc(c, 1)
         assert (d.bits_d, d.n_slots) == (6, slots[1])
+        if per_layer:   # a layer's experts only ever sit in its own run of slots
+            runs = {0: [(0, 5), None, (5, 9), (9, 13), None], 1: [None, (0, 5), None, None, (5, 9)]}
+            for l, cls in enumerate(layer_class):
+                lo, hi = runs[cls][l]
+                t = B.moe_cache_table(c, l, E)
+                assert all(lo <= v < hi for v in t if v >= 0)
     finally:
         B.moe_cache_destroy(c)
 
@@ -225,3 +236,34 @@ def test_abort_fill_empties_the_slot_and_it_is_taken_next():
             B.moe_cache_abort_fill(c, 0, 0)
     finally:
         B.moe_cache_destroy(c)
+
+
+def test_lfu_keeps_the_frequent_expert_that_lru_would_drop():
+    """Two slots; expert 0 is used three times, then 1, then 2 arrives: LRU drops
+    0 (least recent), LFU drops 1 (fewest uses)."""
+    for policy, dropped in ((B.MOE_EVICT_LRU, 0), (B.MOE_EVICT_LFU, 1)):
+        c = make(n_a=2, layers=(0,), E=8, policy=policy)
+        try:
+            for e in (0, 0, 0, 1, 2):
+                fill(c, 0, e)
+            assert B.moe_cache_lookup(c, 0, dropped) == -1
+            assert B.moe_cache_lookup(c, 0, 1 - dropped) >= 0
+        finally:
+            B.moe_cache_destroy(c)
+
+
+def test_per_layer_split_and_bad_policy():
+    c = make(n_a=5, layers=(0, 0), E=8, per_layer=True)   # 3 + 2 slots
+    try:
+        for e in range(6):
+            fill(c, 1, e)      # layer 1 churns its own two slots
+        assert sorted(v for v in B.moe_cache_table(c, 1, 8) if v >= 0) == [3, 4]
+        for e in range(3):
+            fill(c, 0, e)
+        assert sorted(v for v in B.moe_cache_table(c, 0, 8) if v >= 0) == [0, 1, 2]
+        assert sorted(v for v in B.moe_cache_table(c, 1, 8) if v >= 0) == [3, 4]
+    finally:
+        B.moe_cache_destroy(c)
+    a = B.moe_size_class_init(256, 128, 4, 4, 2)
+    with pytest.raises(B.MoeError):
+        B.moe_cache_create([a], [0], 8, policy=7)

@@ -100,13 +100,13 @@ class Replay:
 
 def run_pipeline(rp: Replay, ids, ws, ids_host, store, host_tier_bytes=0, preload=False,
                  io_threads=2, staging_rows=4, drain_each=False, prefetch=False, model=None,
-                 n_copy=1):
+                 n_copy=1, policy=B.MOE_EVICT_LRU, per_layer=False):
     """Decode steps through the pipeline; no host synchronisation between layers
     unless drain_each.  Returns (outputs, per-class stats, pools, cache tables)."""
     torch = _torch()
     pools = [torch.zeros(d.n_slots * d.slot_bytes, dtype=torch.uint8, device="cuda")
              for d in rp.classes]
-    cache = B.moe_cache_create(rp.classes, rp.layer_class, E)
+    cache = B.moe_cache_create(rp.classes, rp.layer_class, E, policy=policy, per_layer=per_layer)
     copies = [torch.cuda.Stream() for _ in range(n_copy)]
     p = B.moe_pipeline_create(cache, store, pools, host_tier_bytes=host_tier_bytes,
                               host_preload=preload, io_threads=io_threads,
@@ -196,6 +196,29 @@ def test_replay_from_store_matches_resident_run_and_lru_model(replay, kind, tmp_
         assert st["store_reads"] == mm and st["host_hits"] == 0
         assert st["bytes_copied"] == mm * rp.classes[c].slot_bytes == st["bytes_read"]
         assert mev > 0                       # the half-size cache really evicts
+    for l in range(rp.L):
+        assert tables[l].tolist() == model.table(l)
+
+
+@pytest.mark.parametrize("policy,per_layer", [(B.MOE_EVICT_LFU, False), (B.MOE_EVICT_LRU, True),
+                                              (B.MOE_EVICT_LFU, True)])
+def test_replay_eviction_variants_match_model(replay, policy, per_layer):
+    """LFU and per-layer LRU caches behind the pipeline: same outputs, and the
+    per-class counters and tables of the plain model."""
+    rp, ids, ws, host, ref = replay
+    store = B.moe_store_open_memory(rp.store_bytes, rp.classes, rp.layer_class, E)
+    try:
+        model = CacheModel(rp.class_slots, rp.layer_class, E, lfu=policy == B.MOE_EVICT_LFU,
+                           per_layer=per_layer)
+        outs, stats, cstats, pools, tables, _ = run_pipeline(rp, ids, ws, host, store, drain_each=True,
+                                                             model=model, policy=policy,
+                                                             per_layer=per_layer, n_copy=2)
+    finally:
+        B.moe_store_close(store)
+    check_outputs(outs, ref)
+    check_pools(rp, pools, tables)
+    for c in range(len(rp.classes)):
+        assert cstats[c] == model.class_stats(c)
     for l in range(rp.L):
         assert tables[l].tolist() == model.table(l)
 
