@@ -32,7 +32,7 @@
  *   synchronising; rows touched by such a fault hold unspecified values.
  *   `err_word` may be NULL, in which case device faults are not reported.
  * Limits.  1 <= E <= 1024; 1 <= k <= min(E, 32); H and I multiples of 64;
- *   bits in {3, 4, 6, 8}; T >= 0 (T == 0 is a no-op returning MOE_OK).
+ *   bits in {3, 4, 6, 8, 16}; T >= 0 (T == 0 is a no-op returning MOE_OK).
  * Streams.  hipStream_t 0 is the null stream.  No entry point synchronises.
  *
  * ---------------------------------------------------------------------------
@@ -59,6 +59,12 @@
  * byte offset 4*(n*(C/64) + g): an IEEE fp16 scale s then an IEEE fp16 bias z,
  * both little-endian.  The dequantized weight is  w[n][c] = s*q + z  with q the
  * unsigned code; s*q is exact in fp32, so the only rounding is the add.
+ *
+ * Width 16 (unquantized experts; [RFC] "How the prototype works", Cache bullet:
+ * BF16 experts run from the same pool): the "codes" are the bf16 weights
+ * themselves (the rule above with b = 16 is the plain row-major little-endian
+ * bf16 matrix) and the scale/bias block is empty (0 bytes), so the next block
+ * starts at the same offset.  Each matrix's width is chosen separately.
  *
  * ---------------------------------------------------------------------------
  * Routing numeric contract ([RFC] "Motivation": each token uses k of E experts;
@@ -147,8 +153,8 @@ extern "C" {
 typedef struct moe_size_class_desc {
     int32_t H;            /* hidden size (multiple of 64)                      */
     int32_t I;            /* expert intermediate size (multiple of 64)         */
-    int32_t bits_gu;      /* code width of gate_up: 3, 4, 6 or 8               */
-    int32_t bits_d;       /* code width of down:    3, 4, 6 or 8               */
+    int32_t bits_gu;      /* code width of gate_up: 3, 4, 6, 8 or 16 (bf16)    */
+    int32_t bits_d;       /* code width of down:    3, 4, 6, 8 or 16 (bf16)    */
     int32_t group;        /* quantization group along the input dim: 64        */
     int32_t align;        /* block alignment in bytes: 256                     */
     int64_t n_slots;      /* slots in this class's pool                        */

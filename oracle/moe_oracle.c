@@ -219,17 +219,20 @@ int oracle_sort(const int32_t* ids, int T, int k, int E, int P,
 static int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 /* offs[0..4] = gate_up codes, gate_up scale/bias, down codes, down scale/bias,
- * slot bytes.  Blocks start at multiples of 256 bytes. */
+ * slot bytes.  Blocks start at multiples of 256 bytes.  Width 16 means
+ * unquantized bf16 weights ("RFC ...", How the prototype works, Cache: BF16
+ * experts run from the same pool): the values themselves in row order, and an
+ * empty scale/bias block. */
+static int width_ok(int b) { return b == 3 || b == 4 || b == 6 || b == 8 || b == 16; }
+
 int oracle_layout(int H, int I, int bits_gu, int bits_d, int64_t* offs)
 {
     if (H <= 0 || I <= 0 || H % 64 || I % 64) return OR_INVALID;
-    int ok_gu = bits_gu == 3 || bits_gu == 4 || bits_gu == 6 || bits_gu == 8;
-    int ok_d = bits_d == 3 || bits_d == 4 || bits_d == 6 || bits_d == 8;
-    if (!ok_gu || !ok_d) return OR_INVALID;
+    if (!width_ok(bits_gu) || !width_ok(bits_d)) return OR_INVALID;
     int64_t gu_codes = (int64_t)2 * I * H * bits_gu / 8;
-    int64_t gu_sb = (int64_t)2 * I * (H / 64) * 4;
+    int64_t gu_sb = bits_gu == 16 ? 0 : (int64_t)2 * I * (H / 64) * 4;
     int64_t d_codes = (int64_t)H * I * bits_d / 8;
-    int64_t d_sb = (int64_t)H * (I / 64) * 4;
+    int64_t d_sb = bits_d == 16 ? 0 : (int64_t)H * (I / 64) * 4;
     offs[0] = 0;
     offs[1] = round_up(offs[0] + gu_codes, 256);
     offs[2] = round_up(offs[1] + gu_sb, 256);
@@ -262,12 +265,21 @@ static double half_to_double(uint16_t h)
     return sign ? -v : v;
 }
 
+static double bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
 /* Dequantized weight [n][c] of an R x C matrix given its code block and
- * scale/bias block: s*q + z, exact in double. */
+ * scale/bias block: s*q + z, exact in double; width 16: the bf16 value. */
 static double weight_at(const uint8_t* codes, const uint8_t* sb, int C, int bits, int n, int c)
 {
     const uint8_t* row = codes + (size_t)n * (size_t)C * bits / 8;
     uint32_t q = oracle_code(row, bits, c);
+    if (bits == 16) return bf16_to_double((uint16_t)q);
     const uint8_t* g = sb + ((size_t)n * (C / 64) + c / 64) * 4;
     uint16_t s16 = (uint16_t)(g[0] | (g[1] << 8));
     uint16_t z16 = (uint16_t)(g[2] | (g[3] << 8));
@@ -287,14 +299,6 @@ int oracle_dequant(const uint8_t* slot_row, int H, int I, int bits_gu, int bits_
     for (int n = 0; n < R; n++)
         for (int c = 0; c < C; c++) out[(size_t)n * C + c] = weight_at(codes, sb, C, b, n, c);
     return OR_OK;
-}
-
-static double bf16_to_double(uint16_t b)
-{
-    uint32_t u = (uint32_t)b << 16;
-    float f;
-    memcpy(&f, &u, 4);
-    return (double)f;
 }
 
 /*

@@ -31,7 +31,8 @@ int hip_fail(hipError_t e, const char* what)
     return fail(MOE_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-bool bits_ok(int b) { return b == 3 || b == 4 || b == 6 || b == 8; }
+// code widths: 3, 4, 6, 8 (group-wise affine), 16 (unquantized bf16 weights)
+bool bits_ok(int b) { return b == 3 || b == 4 || b == 6 || b == 8 || b == 16; }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -122,12 +123,12 @@ int moe_size_class_init(moe_size_class_desc* d, int H, int I, int bits_gu, int b
     if (H <= 0 || I <= 0 || H % 64 || I % 64)
         return fail(MOE_E_INVALID, "H and I must be positive multiples of 64 (H=%d I=%d)", H, I);
     if (!bits_ok(bits_gu) || !bits_ok(bits_d))
-        return fail(MOE_E_INVALID, "bits must be 3, 4, 6 or 8 (gate_up %d, down %d)", bits_gu, bits_d);
+        return fail(MOE_E_INVALID, "bits must be 3, 4, 6, 8 or 16 (gate_up %d, down %d)", bits_gu, bits_d);
     if (n_slots < 0) return fail(MOE_E_INVALID, "n_slots < 0");
     const int64_t gu_codes = (int64_t)2 * I * H * bits_gu / 8;
-    const int64_t gu_sb = (int64_t)2 * I * (H / 64) * 4;
+    const int64_t gu_sb = bits_gu == 16 ? 0 : (int64_t)2 * I * (H / 64) * 4;
     const int64_t d_codes = (int64_t)H * I * bits_d / 8;
-    const int64_t d_sb = (int64_t)H * (I / 64) * 4;
+    const int64_t d_sb = bits_d == 16 ? 0 : (int64_t)H * (I / 64) * 4;
     d->H = H;
     d->I = I;
     d->bits_gu = bits_gu;

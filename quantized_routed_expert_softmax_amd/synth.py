@@ -45,8 +45,8 @@ class Layout:
         return 2 * self.I * self.H * self.bits_gu // 8
 
     @property
-    def gu_sb_bytes(self) -> int:
-        return 2 * self.I * (self.H // GROUP) * 4
+    def gu_sb_bytes(self) -> int:  # width 16 (bf16 weights) has no scale/bias
+        return 0 if self.bits_gu == 16 else 2 * self.I * (self.H // GROUP) * 4
 
     @property
     def d_codes_bytes(self) -> int:
@@ -54,7 +54,7 @@ class Layout:
 
     @property
     def d_sb_bytes(self) -> int:
-        return self.H * (self.I // GROUP) * 4
+        return 0 if self.bits_d == 16 else self.H * (self.I // GROUP) * 4
 
     @property
     def off_gu_codes(self) -> int:
@@ -233,26 +233,36 @@ class ExpertQ:
 
 
 def expert_row(lay: Layout, e: ExpertQ) -> np.ndarray:
-    """Serialise one expert into its slot row (uint8 [slot_bytes])."""
+    """Serialise one expert into its slot row (uint8 [slot_bytes]).  A width-16
+    block holds the bf16 bit patterns (uint16 "codes") in row order and has no
+    scale/bias."""
     row = np.zeros(lay.slot_bytes, dtype=np.uint8)
     a = pack_codes(e.gu_q, lay.bits_gu).reshape(-1)
     row[lay.off_gu_codes:lay.off_gu_codes + a.size] = a
-    a = pack_scale_bias(e.gu_s, e.gu_z).reshape(-1)
-    row[lay.off_gu_sb:lay.off_gu_sb + a.size] = a
+    if lay.bits_gu != 16:
+        a = pack_scale_bias(e.gu_s, e.gu_z).reshape(-1)
+        row[lay.off_gu_sb:lay.off_gu_sb + a.size] = a
     a = pack_codes(e.d_q, lay.bits_d).reshape(-1)
     row[lay.off_d_codes:lay.off_d_codes + a.size] = a
-    a = pack_scale_bias(e.d_s, e.d_z).reshape(-1)
-    row[lay.off_d_sb:lay.off_d_sb + a.size] = a
+    if lay.bits_d != 16:
+        a = pack_scale_bias(e.d_s, e.d_z).reshape(-1)
+        row[lay.off_d_sb:lay.off_d_sb + a.size] = a
     return row
 
 
+def _quantize_or_bf16(w: np.ndarray, bits: int):
+    if bits == 16:  # unquantized: bf16 bit patterns as 16-bit codes, no scale/bias
+        return f32_to_bf16_bits(w), None, None
+    return quantize(w, bits)
+
+
 def gaussian_expert(rng: np.random.Generator, H: int, I: int, bits_gu: int, bits_d: int):
-    """fp32 weights N(0, 1/fan_in) quantized by the test quantizer.
-    Returns (ExpertQ, w_gu fp32 [2I, H], w_d fp32 [I -> H] as [H, I])."""
+    """fp32 weights N(0, 1/fan_in) quantized by the test quantizer (width 16:
+    rounded to bf16).  Returns (ExpertQ, w_gu fp32 [2I, H], w_d fp32 [I -> H] as [H, I])."""
     w_gu = (rng.standard_normal((2 * I, H), dtype=np.float32) / np.float32(math.sqrt(H))).astype(np.float32)
     w_d = (rng.standard_normal((H, I), dtype=np.float32) / np.float32(math.sqrt(I))).astype(np.float32)
-    gq, gs, gz = quantize(w_gu, bits_gu)
-    dq, ds, dz = quantize(w_d, bits_d)
+    gq, gs, gz = _quantize_or_bf16(w_gu, bits_gu)
+    dq, ds, dz = _quantize_or_bf16(w_d, bits_d)
     return ExpertQ(gq, gs, gz, dq, ds, dz), w_gu, w_d
 
 
@@ -261,6 +271,9 @@ def random_code_expert(rng: np.random.Generator, H: int, I: int, bits_gu: int, b
     zero-mean with standard deviation about 1/sqrt(fan_in):
     scale = sqrt(12/(4^b - 1))/sqrt(fan_in) * U(0.9, 1.1), bias = -scale*(2^b-1)/2."""
     def one(R, C, b):
+        if b == 16:  # bf16 weights N(0, 1/fan_in)
+            w = (rng.standard_normal((R, C), dtype=np.float32) / np.float32(math.sqrt(C))).astype(np.float32)
+            return f32_to_bf16_bits(w), None, None
         q = rng.integers(0, 1 << b, size=(R, C), dtype=np.uint8)
         base = math.sqrt(12.0 / (4 ** b - 1)) / math.sqrt(C)
         s = (base * rng.uniform(0.9, 1.1, size=(R, C // GROUP))).astype(np.float16)

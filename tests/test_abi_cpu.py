@@ -40,7 +40,7 @@ def test_size_class_init_matches_golden_layout(case):
 
 
 @pytest.mark.parametrize("args", [(100, 64, 4, 4), (64, 96, 4, 4), (64, 64, 5, 4), (64, 64, 4, 2),
-                                  (0, 64, 4, 4), (64, 64, 4, 16)])
+                                  (0, 64, 4, 4), (64, 64, 4, 12), (64, 64, 32, 4)])
 def test_size_class_init_rejects(args):
     with pytest.raises(B.MoeError) as ei:
         B.moe_size_class_init(*args, 4)

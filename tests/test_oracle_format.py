@@ -114,3 +114,38 @@ def test_integer_closed_form():
     row = synth.expert_row(synth.Layout(H, I, b, b), e)
     assert np.array_equal(oracle.dequant(row, H, I, b, b, 0), q_gu.astype(np.float64))
     assert np.array_equal(oracle.dequant(row, H, I, b, b, 1), q_d.astype(np.float64))
+
+
+@pytest.mark.parametrize("bg,bd", [(16, 16), (16, 4), (3, 16)])
+def test_bf16_blocks_hold_the_values_in_row_order(bg, bd):
+    """A width-16 block is the bf16 matrix itself, row-major, little-endian, with
+    no scale/bias block: bytes written here straight from the bf16 bit patterns
+    decode to exactly those values, and the generator's packer writes the same
+    bytes (the unquantized expert path: "RFC ...", How the prototype works, Cache
+    bullet, BF16 experts from the same pool)."""
+    H, I = 128, 64
+    rng = synth.rng_for(44, bg, bd)
+    e, w_gu, w_d = synth.gaussian_expert(rng, H, I, bg, bd)
+    lay = synth.Layout(H, I, bg, bd)
+    row = synth.expert_row(lay, e)
+    offs = oracle.layout(H, I, bg, bd)
+    for which, (bits, q, off, w) in enumerate([(bg, e.gu_q, offs[0], w_gu), (bd, e.d_q, offs[2], w_d)]):
+        if bits != 16:
+            continue
+        raw = np.ascontiguousarray(q, dtype="<u2").view(np.uint8).reshape(-1)
+        assert np.array_equal(row[off:off + raw.size], raw)
+        hand = np.zeros_like(row)
+        hand[off:off + raw.size] = raw
+        if which == 0 and bd != 16:   # keep the other block valid for the decoder
+            hand[offs[2]:] = row[offs[2]:]
+        if which == 1 and bg != 16:
+            hand[:offs[2]] = row[:offs[2]]
+        got = oracle.dequant(hand, H, I, bg, bd, which)
+        assert np.array_equal(got, synth.bf16_bits_to_f32(q).astype(np.float64))
+        # rounding the fp32 weights to bf16 moves each by at most half an ulp
+        assert np.all(np.abs(got - w) <= np.abs(w) * 2.0 ** -8 + 1e-30)
+    # no scale/bias bytes: the next block starts where the code block ends (aligned)
+    if bg == 16:
+        assert offs[1] == offs[2] == 2 * I * H * 2
+    if bd == 16:
+        assert offs[3] == offs[4]

@@ -24,6 +24,8 @@ from quantized_routed_expert_softmax_amd import synth
 
 
 def deq(q, s, z):
+    if s is None:  # width 16: the codes are bf16 bit patterns of the weights
+        return synth.bf16_bits_to_f32(q).astype(np.float64)
     return q.astype(np.float64) * np.repeat(s.astype(np.float64), 64, axis=1) \
         + np.repeat(z.astype(np.float64), 64, axis=1)
 
@@ -61,6 +63,9 @@ def rel_l2(a, b):
     (4, 64, 4, 128, 4, 8, 8),
     (3, 192, 5, 64, 2, 6, 3),
     (2, 128, 3, 64, 1, 4, 6),
+    (4, 128, 5, 64, 2, 16, 16),    # unquantized bf16 experts
+    (3, 128, 4, 64, 2, 16, 4),
+    (2, 64, 3, 128, 1, 4, 16),
 ])
 def test_layer_matches_dense_masked(shape):
     T, H, E, I, k, bg, bd = shape
