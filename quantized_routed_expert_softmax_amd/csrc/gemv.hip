@@ -92,13 +92,15 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
             gw[b] = gc[u * B + b];
             uw[b] = uc[u * B + b];
         }
-        const uint32_t g2 = gsb[u >> 1], u2 = usb[u >> 1];
         unit_pairs<B>(gw, gp[j]);
         unit_pairs<B>(uw, up[j]);
-        gs[j] = half_bits_to_f32(g2 & 0xFFFFu);
-        gz[j] = __builtin_fmaf(-off, gs[j], half_bits_to_f32(g2 >> 16));
-        us[j] = half_bits_to_f32(u2 & 0xFFFFu);
-        uz[j] = __builtin_fmaf(-off, us[j], half_bits_to_f32(u2 >> 16));
+        if constexpr (Code<B>::affine) {
+            const uint32_t g2 = gsb[u >> 1], u2 = usb[u >> 1];
+            gs[j] = half_bits_to_f32(g2 & 0xFFFFu);
+            gz[j] = __builtin_fmaf(-off, gs[j], half_bits_to_f32(g2 >> 16));
+            us[j] = half_bits_to_f32(u2 & 0xFFFFu);
+            uz[j] = __builtin_fmaf(-off, us[j], half_bits_to_f32(u2 >> 16));
+        }
     }
 
     for (int p = 0; p < cnt; ++p) {
@@ -113,12 +115,17 @@ __global__ __launch_bounds__(256) void gemv_gateup_kernel(
             float X = 0.0f, ag = 0.0f, au = 0.0f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                X = dot2(xpair[i], MOE_ONES_PAIR, X);
+                if constexpr (Code<B>::affine) X = dot2(xpair[i], MOE_ONES_PAIR, X);
                 ag = dot2(gp[j][i], xpair[i], ag);
                 au = dot2(up[j][i], xpair[i], au);
             }
-            g += gs[j] * ag + gz[j] * X;
-            uu += us[j] * au + uz[j] * X;
+            if constexpr (Code<B>::affine) {
+                g += gs[j] * ag + gz[j] * X;
+                uu += us[j] * au + uz[j] * X;
+            } else {
+                g += ag;
+                uu += au;
+            }
         }
         g = seg_sum(g, LPR);
         uu = seg_sum(uu, LPR);
@@ -177,7 +184,7 @@ __global__ __launch_bounds__(64) void gemv_down_kernel(
                         const int u = seg + LPR * j;
 #pragma unroll
                         for (int b = 0; b < B; ++b) cw[d][j][b] = c[u * B + b];
-                        sb[d][j] = s2[u >> 1];
+                        if constexpr (Code<B>::affine) sb[d][j] = s2[u >> 1];
                     }
                 }
             }
@@ -190,8 +197,10 @@ __global__ __launch_bounds__(64) void gemv_down_kernel(
 #pragma unroll
             for (int j = 0; j < UPL; ++j) {
                 unit_pairs<B>(cw[d][j], cp[j]);
-                s[j] = half_bits_to_f32(sb[d][j] & 0xFFFFu);
-                z[j] = __builtin_fmaf(-off, s[j], half_bits_to_f32(sb[d][j] >> 16));
+                if constexpr (Code<B>::affine) {
+                    s[j] = half_bits_to_f32(sb[d][j] & 0xFFFFu);
+                    z[j] = __builtin_fmaf(-off, s[j], half_bits_to_f32(sb[d][j] >> 16));
+                }
             }
             for (int p = 0; p < ecnt[d]; ++p) {
                 const int pos = ebase[d] + p;
@@ -213,10 +222,11 @@ __global__ __launch_bounds__(64) void gemv_down_kernel(
                     float X = 0.0f, a = 0.0f;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        X = dot2(hp[i], MOE_ONES_PAIR, X);
+                        if constexpr (Code<B>::affine) X = dot2(hp[i], MOE_ONES_PAIR, X);
                         a = dot2(cp[j][i], hp[i], a);
                     }
-                    y += s[j] * a + z[j] * X;
+                    if constexpr (Code<B>::affine) y += s[j] * a + z[j] * X;
+                    else y += a;
                 }
                 y = seg_sum(y, LPR);
                 if (seg == 0) {
@@ -274,11 +284,13 @@ hipError_t down_b(int upl, dim3 grid, size_t lds, hipStream_t s, int T, int H, i
     hipLaunchKernelGGL((gemv_down_kernel<B, U, D>), grid, dim3(64), lds, s, T, H, I, k,           \
                        sv.offsets, sv.sorted_pairs, sv.pass_table, w, table, pool, c.n_slots,      \
                        c.slot_bytes, c.off_d_codes, c.off_d_sb, hbuf, out, err, lpr)
+    // experts prefetched per step: fewer for bf16 rows (16 words per unit)
+    constexpr int W = B == 16 ? 4 : 1;
     switch (upl) {
-    case 1: MOE_DN(1, 8); break;
-    case 2: MOE_DN(2, 4); break;
-    case 3: MOE_DN(3, 2); break;
-    case 4: MOE_DN(4, 2); break;
+    case 1: MOE_DN(1, 8 / W); break;
+    case 2: MOE_DN(2, (4 / W > 0 ? 4 / W : 1)); break;
+    case 3: MOE_DN(3, (2 / W > 0 ? 2 / W : 1)); break;
+    case 4: MOE_DN(4, (2 / W > 0 ? 2 / W : 1)); break;
     default: return hipErrorInvalidValue;
     }
 #undef MOE_DN
@@ -310,6 +322,7 @@ hipError_t launch_gemv_gateup(const uint16_t* x, int T, int k, int E, const Sort
     case 4: return gateup_b<4>(upl, grid, s, x, c.H, c.I, k, sv, table, pool, c, hbuf, err, lpr);
     case 6: return gateup_b<6>(upl, grid, s, x, c.H, c.I, k, sv, table, pool, c, hbuf, err, lpr);
     case 8: return gateup_b<8>(upl, grid, s, x, c.H, c.I, k, sv, table, pool, c, hbuf, err, lpr);
+    case 16: return gateup_b<16>(upl, grid, s, x, c.H, c.I, k, sv, table, pool, c, hbuf, err, lpr);
     }
     return hipErrorInvalidValue;
 }
@@ -329,6 +342,7 @@ hipError_t launch_gemv_down(int T, int k, int E, const SortView& sv, const float
     case 4: return down_b<4>(upl, grid, lds, s, T, c.H, c.I, k, sv, topk_w, table, pool, c, hbuf, out, err, lpr);
     case 6: return down_b<6>(upl, grid, lds, s, T, c.H, c.I, k, sv, topk_w, table, pool, c, hbuf, out, err, lpr);
     case 8: return down_b<8>(upl, grid, lds, s, T, c.H, c.I, k, sv, topk_w, table, pool, c, hbuf, out, err, lpr);
+    case 16: return down_b<16>(upl, grid, lds, s, T, c.H, c.I, k, sv, topk_w, table, pool, c, hbuf, out, err, lpr);
     }
     return hipErrorInvalidValue;
 }

@@ -64,7 +64,14 @@ template <int B>
 __device__ __forceinline__ u32x4_t lane_pairs(const uint32_t* __restrict__ unit, int g)
 {
     u32x4_t r;
-    if constexpr (B == 8) {
+    if constexpr (B == 16) {  // bf16 weights: values 4g+r at half r&1 of word 2g + r/2, +16 at word 8 + ...
+        const uint32_t l0 = unit[2 * g], l1 = unit[2 * g + 1];
+        const uint32_t h0 = unit[8 + 2 * g], h1 = unit[9 + 2 * g];
+        r.x = __builtin_amdgcn_perm(h0, l0, 0x05040100u);
+        r.y = __builtin_amdgcn_perm(h0, l0, 0x07060302u);
+        r.z = __builtin_amdgcn_perm(h1, l1, 0x05040100u);
+        r.w = __builtin_amdgcn_perm(h1, l1, 0x07060302u);
+    } else if constexpr (B == 8) {
         const uint32_t lo = unit[g], hi = unit[4 + g];
         const float a0 = ubyte_f32<0>(lo), b0 = ubyte_f32<0>(hi);
         const float a1 = ubyte_f32<1>(lo), b1 = ubyte_f32<1>(hi);
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(256) void mfma_grouped_kernel(
             p = p * 4 < units_ * B ? p : 0;                                                     \
             RB[i] = *(const u32x4_t*)(codes + (size_t)wrow(r) * row_dw + (size_t)(kin_ / 32) * B + p * 4); \
         });                                                                                     \
-        {                                                                                       \
+        if constexpr (Code<B>::affine) {                                                        \
             const int qs = tid < SBN ? tid : SBN - 1;                                           \
             const int r = qs / kGPC;                                                            \
             int gg = qs - r * kGPC;                                                             \
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(256) void mfma_grouped_kernel(
                 *(u32x4_t*)(&S_.codes[r][p * 4]) = RB[i];                                       \
             }                                                                                   \
         });                                                                                     \
-        if (tid < SBN) S_.sb[tid / kGPC][tid % kGPC] = RS;                                      \
+        if (Code<B>::affine && tid < SBN) S_.sb[tid / kGPC][tid % kGPC] = RS;                   \
         static_for<APT>([&](auto I_) {                                                          \
             constexpr int i = decltype(I_)::value;                                              \
             const int q = tid + 256 * i;                                                        \
@@ -274,21 +281,30 @@ __global__ __launch_bounds__(256) void mfma_grouped_kernel(
                 const int r = nb * 64 + wave * 16 + c16;                                        \
                 bw[nb][0] = lds_pairs<B>(&S.codes[r][(2 * G2) * B], g);                         \
                 bw[nb][1] = lds_pairs<B>(&S.codes[r][(2 * G2 + 1) * B], g);                     \
-                const uint32_t s2 = S.sb[r][G2];                                                \
-                sc[nb] = half_bits_to_f32(s2 & 0xFFFFu);                                        \
-                zc[nb] = __builtin_fmaf(-off, sc[nb], half_bits_to_f32(s2 >> 16));              \
+                if constexpr (Code<B>::affine) {                                                \
+                    const uint32_t s2 = S.sb[r][G2];                                            \
+                    sc[nb] = half_bits_to_f32(s2 & 0xFFFFu);                                    \
+                    zc[nb] = __builtin_fmaf(-off, sc[nb], half_bits_to_f32(s2 >> 16));          \
+                }                                                                               \
             }                                                                                   \
             _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                                 \
                 if (mt < nmt) {                                                                 \
                     const u32x4_t a0 = *(const u32x4_t*)(&S.a[mt * 16 + c16][(2 * G2) * 32 + 8 * g]); \
                     const u32x4_t a1 = *(const u32x4_t*)(&S.a[mt * 16 + c16][(2 * G2 + 1) * 32 + 8 * g]); \
-                    f32x4_t tx = mfma(a0, ones, zero);                                          \
-                    tx = mfma(a1, ones, tx);                                                    \
-                    _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                         \
-                        f32x4_t t = mfma(a0, bw[nb][0], zero);                                  \
-                        t = mfma(a1, bw[nb][1], t);                                             \
-                        _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_)                        \
-                            acc[nb][mt][q_] = __builtin_fmaf(sc[nb], t[q_], __builtin_fmaf(zc[nb], tx[q_], acc[nb][mt][q_])); \
+                    if constexpr (Code<B>::affine) {                                            \
+                        f32x4_t tx = mfma(a0, ones, zero);                                      \
+                        tx = mfma(a1, ones, tx);                                                \
+                        _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                     \
+                            f32x4_t t = mfma(a0, bw[nb][0], zero);                              \
+                            t = mfma(a1, bw[nb][1], t);                                         \
+                            _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_)                    \
+                                acc[nb][mt][q_] = __builtin_fmaf(sc[nb], t[q_], __builtin_fmaf(zc[nb], tx[q_], acc[nb][mt][q_])); \
+                        }                                                                       \
+                    } else { /* bf16 weights: the matrix cores accumulate in place */            \
+                        _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                     \
+                            acc[nb][mt] = mfma(a0, bw[nb][0], acc[nb][mt]);                     \
+                            acc[nb][mt] = mfma(a1, bw[nb][1], acc[nb][mt]);                     \
+                        }                                                                       \
                     }                                                                           \
                 }                                                                               \
             }                                                                                   \
@@ -426,6 +442,7 @@ hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const Sor
     case 4: MOE_MG2(4); break;
     case 6: MOE_MG2(6); break;
     case 8: MOE_MG2(8); break;
+    case 16: MOE_MG2(16); break;
     default: return hipErrorInvalidValue;
     }
 #undef MOE_MG
@@ -451,6 +468,7 @@ hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, const int32
     case 4: MOE_MD2(4); break;
     case 6: MOE_MD2(6); break;
     case 8: MOE_MD2(8); break;
+    case 16: MOE_MD2(16); break;
     default: return hipErrorInvalidValue;
     }
 #undef MOE_MD

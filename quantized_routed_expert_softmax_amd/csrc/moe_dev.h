@@ -16,6 +16,9 @@
 // A bf16 dot2 then accumulates sum x*(off + c) exactly per product, and the
 // affine map is applied per group afterwards:
 //     sum_g s_g * sum x*c + z_g * sum x  =  s_g * acc + (z_g - off*s_g) * X_g.
+// Width 16 (unquantized bf16 weights) uses the same unit rule with the bf16 bit
+// patterns as codes: a unit is 16 words holding the 32 values in order, a pair
+// is taken straight from them, and there is no affine step.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,7 +36,8 @@ template <int B>
 struct Code {
     static constexpr uint32_t mask = (1u << B) - 1u;
     static constexpr uint32_t mask2 = mask * 0x10001u;
-    static constexpr float offset = (B == 8) ? 0.0f : 128.0f;  // bf16 value of code 0
+    static constexpr float offset = (B >= 8) ? 0.0f : 128.0f;  // bf16 value of code 0
+    static constexpr bool affine = B != 16;                       // width 16: bf16 weights
     static constexpr int per_t = 16 / B;                          // pairs from one window pair
 };
 
@@ -92,10 +96,17 @@ __device__ __forceinline__ uint32_t bytes02_to_bf16pair(uint32_t t)
     return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
 }
 
-// All 16 P16 pairs of one unit, as bf16 pairs of (offset + code).
+// All 16 P16 pairs of one unit, as bf16 pairs of (offset + code); width 16:
+// pair i = (value i, value i + 16), halves of words i/2 and 8 + i/2.
 template <int B>
 __device__ __forceinline__ void unit_pairs(const uint32_t (&w)[B], uint32_t (&pr)[16])
 {
+    if constexpr (B == 16) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            pr[i] = __builtin_amdgcn_perm(w[8 + (i >> 1)], w[i >> 1], (i & 1) ? 0x07060302u : 0x05040100u);
+        return;
+    }
     constexpr int S = Code<B>::per_t;
 #pragma unroll
     for (int i = 0; i < 16; i += S) {

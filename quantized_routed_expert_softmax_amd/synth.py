@@ -341,7 +341,8 @@ def tiny_problem() -> Problem:
 # --------------------------------------------------------------------------- #
 def fill_pool_device(pool, lay: Layout, slots, seed: int, layer: int):
     """Fill the given slots of a device pool tensor (uint8 [n_slots, slot_bytes])
-    with random codes and the scale/bias recipe of random_code_expert.
+    with random codes and the scale/bias recipe of random_code_expert (width 16:
+    bf16 weights N(0, 1/fan_in)).
 
     Codes are uniform random bytes (uniform codes for every width, since the
     code block is a plain bit stream).  Uses torch's seeded device generator; the
@@ -359,6 +360,11 @@ def fill_pool_device(pool, lay: Layout, slots, seed: int, layer: int):
         (lay.off_gu_codes, lay.gu_codes_bytes, lay.off_gu_sb, 2 * lay.I, lay.H, lay.bits_gu),
         (lay.off_d_codes, lay.d_codes_bytes, lay.off_d_sb, lay.H, lay.I, lay.bits_d),
     ):
+        if b == 16:  # unquantized: bf16 weights N(0, 1/fan_in), no scale/bias
+            w = torch.randn((n, R * C), device=dev, generator=g, dtype=torch.float32) / math.sqrt(C)
+            pool[slots_t, off_c:off_c + nbytes_c] = w.to(torch.bfloat16).view(torch.uint8)
+            del w
+            continue
         codes = torch.randint(0, 256, (n, nbytes_c), dtype=torch.uint8, device=dev, generator=g)
         pool[slots_t, off_c:off_c + nbytes_c] = codes
         del codes

@@ -200,6 +200,9 @@ SMALL = [
     (33, 256, 12, 128, 3, 3, 4),    # 2+ M-tiles for some experts, ragged
     (64, 128, 8, 64, 2, 8, 6),
     (1, 512, 16, 256, 4, 3, 3),
+    (16, 256, 8, 128, 2, 16, 16),   # unquantized bf16 experts
+    (5, 128, 6, 64, 3, 16, 4),      # bf16 gate/up, 4-bit down
+    (33, 256, 12, 128, 3, 4, 16),   # 4-bit gate/up, bf16 down, 2+ M-tiles
 ]
 
 
@@ -363,6 +366,40 @@ def test_forward_prefill_chunk_full_size():
     tokens = sorted(synth.rng_for(wl.seed, 9).choice(wl.T, 12, replace=False).tolist()) + [0, wl.T - 1]
     ref = oracle_on_rows(x, ids_o, w_o, table, pool, lay, wl.E, tokens)
     check_close(out[tokens], ref, "prefill sampled tokens")
+
+
+@pytest.mark.parametrize("T", [1, 1024])
+def test_forward_bf16_experts_full_size(T):
+    """Unquantized bf16 experts of the decode shape (H2048, E512, I512, top-10):
+    the GEMV path at batch 1, the MFMA path for a 1024-token chunk (sampled
+    tokens); the fused decode kernel has no bf16 variant, so AUTO takes GEMV."""
+    torch = _torch()
+    H, E, I, k = 2048, 512, 512, 10
+    lay = synth.Layout(H, I, 16, 16)
+    assert lay.slot_bytes == 6291456
+    table = synth.slot_table(synth.rng_for(6, 4, T), E, E)
+    pool = device_pool(lay, E, table, 6, T)
+    lg = synth.gen_logits(synth.rng_for(6, 3, T), T, E)
+    x = synth.gen_x(synth.rng_for(6, 1, T), T, H)
+    ids, w = B.moe_route_topk(to_dev(lg), k)
+    ids_o, w_o = oracle.route(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    tokens = [0] if T == 1 else sorted(synth.rng_for(6, 9).choice(T, 10, replace=False).tolist()) + [T - 1]
+    ref = oracle_on_rows(x, ids_o, w_o, table, pool, lay, E, tokens)
+    paths = (B.MOE_PATH_AUTO, B.MOE_PATH_GEMV3, B.MOE_PATH_MFMA) if T == 1 else (B.MOE_PATH_AUTO,)
+    for path in paths:
+        out, ew = forward_dev(dev_bf16(x), ids, w, E, to_dev(table), pool, lay, path)
+        assert ew == 0
+        assert bool(torch.isfinite(out.float()).all())
+        check_close(out[tokens], ref, f"bf16 experts T {T} path {path}")
+    if T == 1:  # router + experts entry point falls back to route + GEMV
+        desc = B.moe_size_class_init(H, I, 16, 16, pool.shape[0])
+        ew = err_word()
+        out, _, _ = B.moe_layer_forward(to_dev(lg), dev_bf16(x), to_dev(table), pool.view(-1), desc, k,
+                                        err_word=ew)
+        torch.cuda.synchronize()
+        assert int(ew.item()) == 0
+        check_close(out, ref, "bf16 experts moe_layer_forward")
 
 
 @pytest.mark.parametrize("T", [1, 8])
