@@ -40,6 +40,7 @@ def parse():
     p.add_argument("--prefill-reps", type=int, default=3)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-bf16", action="store_true", help="skip the unquantized bf16 expert lines")
     p.add_argument("--cpu-layers", type=int, default=12, help="oracle sample: decode layers")
     p.add_argument("--eager", action="store_true", help="no HIP graph (launch-bound)")
     p.add_argument("--replay", action="store_true",
@@ -352,6 +353,93 @@ def replay_main(args, torch, B, synth):
     print(json.dumps(result), flush=True)
 
 
+def bf16_lines(torch, B, synth, wl, dev, err):
+    """The decode layer shape with unquantized bf16 experts (6.29 MB each): decode
+    steps through 8 layer pools (25 GB, more than the 256 MB Infinity Cache can
+    hold, so experts stream from HBM), and one 1024-token prefill chunk."""
+    H, E, I, k = wl.H, wl.E, wl.I, wl.k
+    lay = synth.Layout(H, I, 16, 16)
+    n_pools = 8
+    desc = B.moe_size_class_init(H, I, 16, 16, E)
+    pools = []
+    for l in range(n_pools):
+        pool = torch.empty((E, lay.slot_bytes), dtype=torch.uint8, device=dev)
+        synth.fill_pool_device(pool, lay, np.arange(E), 7, l)
+        pools.append(pool.view(-1))
+    table = torch.arange(E, dtype=torch.int32, device=dev)
+    steps = 48
+    lg = torch.stack([torch.from_numpy(synth.gen_logits(
+        synth.rng_for(7, 3, s), 1, E, synth.zipf_bias(synth.rng_for(7, 2, s), E, wl.zipf_s))) for s in range(steps)]).to(dev)
+    x = torch.from_numpy(synth.gen_x(synth.rng_for(7, 1), 1, H).view(np.int16)).to(dev).view(torch.bfloat16)
+    ids = torch.empty((steps, 1, k), dtype=torch.int32, device=dev)
+    w = torch.empty((steps, 1, k), dtype=torch.float32, device=dev)
+    out = torch.empty((1, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(B.moe_forward_workspace_size(1, k, E, desc), dtype=torch.uint8, device=dev)
+
+    def dec():
+        for s_ in range(steps):
+            B.moe_layer_forward(lg[s_], x, table, pools[s_ % n_pools], desc, k, topk_ids=ids[s_], topk_w=w[s_],
+                                out=out, ws=ws, err_word=err)
+
+    dec()
+    torch.cuda.synchronize()
+    # the 48 layer-steps captured in one HIP graph, as the headline decode step is
+    graph = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(graph, stream=st):
+            dec()
+    torch.cuda.current_stream().wait_stream(st)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / (5 * steps)
+    ids_np = ids.cpu().numpy()
+    distinct = float(np.mean([len(set(ids_np[s_].reshape(-1).tolist())) for s_ in range(steps)]))
+    dec_bytes = distinct * lay.slot_bytes
+    # prefill chunk
+    pw = synth.WORKLOADS["prefill"]
+    T = pw.T
+    plg = torch.from_numpy(synth.gen_logits(synth.rng_for(7, 5), T, E)).to(dev)
+    px = torch.from_numpy(synth.gen_x(synth.rng_for(7, 6), T, H).view(np.int16)).to(dev).view(torch.bfloat16)
+    pids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    pwt = torch.empty((T, k), dtype=torch.float32, device=dev)
+    pout = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    pws = torch.zeros(B.moe_forward_workspace_size(T, k, E, desc), dtype=torch.uint8, device=dev)
+    run = lambda: B.moe_layer_forward(plg, px, table, pools[0], desc, k, topk_ids=pids, topk_w=pwt, out=pout,
+                                      ws=pws, err_word=err)
+    run()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    p_us = e0.elapsed_time(e1) * 1000.0 / 5
+    assert int(err.item()) == 0, f"device error word {int(err.item()):#x}"
+    flops = 2.0 * T * k * 3 * H * I
+    p_bytes = E * lay.slot_bytes
+    del pools
+    torch.cuda.empty_cache()
+    return {
+        "workload": "decode layer shape (H 2048, E 512, I 512, top-10) with bf16 experts, 6291456 B each",
+        "decode_us_per_layer": round(us, 2),
+        "decode_hbm_gbs": round(dec_bytes / (us * 1e-6) / 1e9, 1),
+        "decode_hbm_frac": round(dec_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_path": "router kernel + sort + GEMV gate/up + GEMV down (4 launches per layer, 48 layer-steps in one HIP graph)",
+        "prefill_chunk_us": round(p_us, 2),
+        "prefill_hbm_gbs": round(p_bytes / (p_us * 1e-6) / 1e9, 1),
+        "prefill_hbm_frac": round(p_bytes / (p_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "prefill_useful_tflops": round(flops / (p_us * 1e-6) / 1e12, 1),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -548,6 +636,10 @@ def main():
             "hbm_gbs": round(lc_bytes / (lc_ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(lc_bytes / (lc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         }
+
+    # ------------------------ unquantized bf16 experts ---------------------- #
+    if not args.no_bf16:
+        result["bf16_experts"] = bf16_lines(torch, B, synth, wl, dev, err)
 
     # ----------------------------- CPU oracle ------------------------------ #
     if not args.no_cpu:

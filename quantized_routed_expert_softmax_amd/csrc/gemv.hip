@@ -284,13 +284,13 @@ hipError_t down_b(int upl, dim3 grid, size_t lds, hipStream_t s, int T, int H, i
     hipLaunchKernelGGL((gemv_down_kernel<B, U, D>), grid, dim3(64), lds, s, T, H, I, k,           \
                        sv.offsets, sv.sorted_pairs, sv.pass_table, w, table, pool, c.n_slots,      \
                        c.slot_bytes, c.off_d_codes, c.off_d_sb, hbuf, out, err, lpr)
-    // experts prefetched per step: fewer for bf16 rows (16 words per unit)
-    constexpr int W = B == 16 ? 4 : 1;
+    // experts prefetched per step (bf16 rows hold 16 words per unit, so fewer)
+    constexpr bool W16 = B == 16;
     switch (upl) {
-    case 1: MOE_DN(1, 8 / W); break;
-    case 2: MOE_DN(2, (4 / W > 0 ? 4 / W : 1)); break;
-    case 3: MOE_DN(3, (2 / W > 0 ? 2 / W : 1)); break;
-    case 4: MOE_DN(4, (2 / W > 0 ? 2 / W : 1)); break;
+    case 1: MOE_DN(1, W16 ? 5 : 8); break;
+    case 2: MOE_DN(2, W16 ? 2 : 4); break;
+    case 3: MOE_DN(3, W16 ? 1 : 2); break;
+    case 4: MOE_DN(4, W16 ? 1 : 2); break;
     default: return hipErrorInvalidValue;
     }
 #undef MOE_DN

@@ -113,11 +113,17 @@ constexpr int kUPC = kKC / 32;    // pack units per stage
 constexpr int kGPC = kKC / 64;    // groups per stage
 constexpr int kAROW = kKC + 8;    // bf16 per staged activation row (padding: conflict-free reads)
 
+// Dwords of padding after each staged code row.  The 16 lanes of a lane group
+// read the same column of 16 consecutive rows; a row stride of 4 (mod 32) dwords
+// puts those rows on different banks.  Width 3 (stride 12) already spreads them.
+template <int B>
+constexpr int code_pad() { return B == 3 ? 0 : 4; }
+
 // One pipeline stage in LDS: raw codes and scale/bias of the workgroup's NB*64
 // weight rows for kKC inputs, and kKC activations of up to MT*16 rows.
 template <int B, int NB, int MT>
 struct Stage {
-    uint32_t codes[NB * 64][kUPC * B];
+    uint32_t codes[NB * 64][kUPC * B + code_pad<B>()];
     uint32_t sb[NB * 64][kGPC];
     uint16_t a[MT * 16][kAROW];
 };
