@@ -86,19 +86,20 @@ __device__ __forceinline__ u32x4_t lane_pairs(const uint32_t* __restrict__ unit,
         const int oh = ol + 16 * B - 16;       // window whose bit 16 is the first high code bit
         const int dl = ol >> 5, sl = ol & 31;
         const int dh = oh >> 5, sh = oh & 31;
-        const uint64_t lo64 = (uint64_t)unit[dl] | ((uint64_t)unit[dl + 1] << 32);
-        const uint64_t hi64 = (uint64_t)unit[dh] | ((uint64_t)unit[dh + 1] << 32);
         constexpr int S = Code<B>::per_t;  // 5 (B=3), 4 (B=4), 2 (B=6)
         constexpr uint32_t M2 = Code<B>::mask2;
         uint32_t p[4];
 #pragma unroll
         for (int q = 0; q < 4; q += S) {
-            const uint32_t wl = (uint32_t)(lo64 >> (sl + q * B));
-            const uint32_t wh = (uint32_t)(hi64 >> (sh + q * B));
-            const uint32_t t = (wl & 0xFFFFu) | (wh & 0xFFFF0000u);
+            // 32-bit funnel shifts of two adjacent words (the shift stays below 32:
+            // sl, sh < 32 and q * B + sl < 32 whenever q > 0 is reached)
+            const int ql = sl + q * B, qh = sh + q * B;
+            const uint32_t wl = __builtin_amdgcn_alignbit(unit[dl + 1 + (ql >> 5)], unit[dl + (ql >> 5)], ql & 31);
+            const uint32_t wh = __builtin_amdgcn_alignbit(unit[dh + 1 + (qh >> 5)], unit[dh + (qh >> 5)], qh & 31);
+            const uint32_t t = __builtin_amdgcn_perm(wh, wl, 0x07060100u);  // low half of wl, high half of wh
 #pragma unroll
             for (int m = 0; m < S; ++m)
-                if (q + m < 4) p[q + m] = ((t >> (B * m)) & M2) | MOE_MAGIC_PAIR;
+                if (q + m < 4) p[q + m] = bits_or_magic<M2>(t >> (B * m));
         }
         r.x = p[0];
         r.y = p[1];

@@ -81,6 +81,15 @@ __device__ __forceinline__ uint32_t pair_window(const uint32_t (&w)[B], int i)
     return (lo & 0xFFFFu) | (hi & 0xFFFF0000u);
 }
 
+// (x & M) | 0x43004300 in one gfx950 three-input bitwise op.  Truth table 0xEA:
+// output bit = (a & b) | c, indexed by (a << 2) | (b << 1) | c.
+template <uint32_t M>
+__device__ __forceinline__ uint32_t bits_or_magic(uint32_t x)
+{
+    static_assert((M & MOE_MAGIC_PAIR) == 0, "mask and magic overlap");
+    return __builtin_amdgcn_bitop3_b32(x, M, MOE_MAGIC_PAIR, 0xEA);
+}
+
 // Float of byte N of t (the compiler emits v_cvt_f32_ubyteN).
 template <int N>
 __device__ __forceinline__ float ubyte_f32(uint32_t t)
@@ -105,20 +114,20 @@ __device__ __forceinline__ void unit_pairs(const uint32_t (&w)[B], uint32_t (&pr
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             pr[i] = __builtin_amdgcn_perm(w[8 + (i >> 1)], w[i >> 1], (i & 1) ? 0x07060302u : 0x05040100u);
-        return;
-    }
-    constexpr int S = Code<B>::per_t;
+    } else {
+        constexpr int S = Code<B>::per_t;
 #pragma unroll
-    for (int i = 0; i < 16; i += S) {
-        const uint32_t t = pair_window<B>(w, i);
+        for (int i = 0; i < 16; i += S) {
+            const uint32_t t = pair_window<B>(w, i);
 #pragma unroll
-        for (int m = 0; m < S; ++m) {
-            if (i + m < 16) {
-                const uint32_t tm = t >> (B * m);
-                if constexpr (B == 8)
-                    pr[i + m] = bytes02_to_bf16pair(tm);
-                else
-                    pr[i + m] = (tm & Code<B>::mask2) | MOE_MAGIC_PAIR;
+            for (int m = 0; m < S; ++m) {
+                if (i + m < 16) {
+                    const uint32_t tm = t >> (B * m);
+                    if constexpr (B == 8)
+                        pr[i + m] = bytes02_to_bf16pair(tm);
+                    else
+                        pr[i + m] = bits_or_magic<Code<B>::mask2>(tm);
+                }
             }
         }
     }
