@@ -97,7 +97,7 @@ FwdLayout fwd_layout(int T, int k, int E, const moe_size_class_desc* d)
     L.xp = o;
     o = align_up(o + sizeof(uint16_t) * (size_t)T * d->H, 256);
     L.ybuf = o;
-    o = align_up(o + sizeof(float) * n * (size_t)d->H, 256);
+    o = align_up(o + sizeof(uint16_t) * n * (size_t)d->H, 256);  // y in bf16
     L.total = o;
     return L;
 }
@@ -274,7 +274,7 @@ int moe_experts_forward_ex(const void* x, int T, const int32_t* topk_ids, const 
         return MOE_OK;
     }
     uint16_t* xp = (uint16_t*)(w + L.xp);
-    float* ybuf = (float*)(w + L.ybuf);
+    uint16_t* ybuf = (uint16_t*)(w + L.ybuf);
     e = moe::launch_permute_x((const uint16_t*)x, T, c.H, xp, stream);
     if (e != hipSuccess) return hip_fail(e, "permute launch");
     e = moe::launch_mfma_gateup(xp, T, k, E, sv, slot_table, pool, c, hbuf, err_word, stream);

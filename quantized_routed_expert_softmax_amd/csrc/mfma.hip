@@ -27,7 +27,7 @@
 //
 // gate/up: SwiGLU in registers (a wave holds gate column n and up column I + n
 // in identical accumulator layouts), h written as bf16 in P16 order.
-// down: y per (pair, output) in fp32 to a workspace; a combine kernel adds the
+// down: y per (pair, output) in bf16 to a workspace; a combine kernel adds the
 // k contributions of each token in j order (deterministic).
 #include <utility>
 
@@ -156,14 +156,14 @@ __device__ __forceinline__ u32x4_t lds_pairs(const uint32_t* __restrict__ unit, 
 //               rows of the expert's pairs (via sorted_pairs); epilogue SwiGLU
 //               -> h (bf16, P16) at the pair's sorted position.
 //   GU = false: down.  Weight rows n0..n0+63 of the down matrix; A = h rows;
-//               epilogue y (fp32) at [pair id][n].
+//               epilogue y (bf16) at [pair id][n].
 template <int B, bool GU, int MT, int CBW>
 __global__ __launch_bounds__(256) void mfma_grouped_kernel(
     const uint16_t* __restrict__ act, int H, int I, int k, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table,
     const int32_t* __restrict__ table, const uint8_t* __restrict__ pool, int64_t n_slots,
     int64_t slot_bytes, int64_t off_codes, int64_t off_sb, uint16_t* __restrict__ hbuf,
-    float* __restrict__ ybuf, uint32_t* __restrict__ err)
+    uint16_t* __restrict__ ybuf, uint32_t* __restrict__ err)
 {
     constexpr int NB = GU ? 2 : 1;
     __shared__ Stage<B, NB, MT> st[2];
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(256) void mfma_grouped_kernel(
                                 const int pos = (n & ~31) | p16_pos(n & 31);
                                 hbuf[(size_t)(base + r) * I + pos] = f32_to_bf16(silu_mul(acc[0][mt][i], acc[1][mt][i]));
                             } else {
-                                ybuf[(size_t)sorted_pairs[base + r] * H + n] = acc[0][mt][i];
+                                ybuf[(size_t)sorted_pairs[base + r] * H + n] = f32_to_bf16(acc[0][mt][i]);
                             }
                         }
                     }
@@ -387,8 +387,10 @@ __global__ __launch_bounds__(256) void permute_x_kernel(const uint16_t* __restri
     xp[q] = (uint32_t)src[i] | ((uint32_t)src[i + 16] << 16);
 }
 
-// out[t, n] = bf16( sum_j w[t, j] * y[t*k + j, n] ), j ascending.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf,
+// out[t, n] = bf16( sum_j w[t, j] * y[t*k + j, n] ), j ascending, in fp32 (y is
+// stored in bf16, like h: the weighted sum of the k expert outputs is the only
+// place they meet).
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ ybuf,
                                                       const float* __restrict__ w, int T, int k,
                                                       int H, uint16_t* __restrict__ out)
 {
@@ -400,11 +402,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
     for (int j = 0; j < k; ++j) {
         const float wj = w[(size_t)t * k + j];
-        const float4 y = *(const float4*)(ybuf + ((size_t)t * k + j) * H + n4);
-        a0 += wj * y.x;
-        a1 += wj * y.y;
-        a2 += wj * y.z;
-        a3 += wj * y.w;
+        const uint2 y = *(const uint2*)(ybuf + ((size_t)t * k + j) * H + n4);
+        a0 += wj * bf16lo(y.x);
+        a1 += wj * bf16hi(y.x);
+        a2 += wj * bf16lo(y.y);
+        a3 += wj * bf16hi(y.y);
     }
     uint2 o;
     o.x = (uint32_t)f32_to_bf16(a0) | ((uint32_t)f32_to_bf16(a1) << 16);
@@ -459,7 +461,7 @@ hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const Sor
 
 hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, const int32_t* table,
                             const uint8_t* pool, const ClassView& c, const uint16_t* hbuf,
-                            float* ybuf, uint32_t* err, hipStream_t s)
+                            uint16_t* ybuf, uint32_t* err, hipStream_t s)
 {
     const int max_hit = (int64_t)T * k < E ? T * k : E;
     constexpr int CBW = 1;  // column blocks per workgroup
@@ -483,7 +485,7 @@ hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, const int32
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* ybuf, const float* topk_w, int T, int k, int H,
+hipError_t launch_combine(const uint16_t* ybuf, const float* topk_w, int T, int k, int H,
                           uint16_t* out, hipStream_t s)
 {
     const int64_t n = (int64_t)T * (H / 4);

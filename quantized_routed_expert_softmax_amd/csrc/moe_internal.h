@@ -56,15 +56,16 @@ hipError_t launch_decode_fused(const float* logits, int mode, float L, const int
                                const ClassView& c, uint16_t* out, void* reserved, uint32_t* err,
                                hipStream_t s);
 
-// Prefill path: P16-permuted x, MFMA gate/up + SwiGLU, MFMA down, combine.
+// Prefill path: P16-permuted x, MFMA gate/up + SwiGLU, MFMA down (y in bf16),
+// combine (fp32 sum in j order).
 hipError_t launch_permute_x(const uint16_t* x, int T, int H, uint16_t* xp, hipStream_t s);
 hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const SortView& sv,
                               const int32_t* table, const uint8_t* pool, const ClassView& c,
                               uint16_t* hbuf, uint32_t* err, hipStream_t s);
 hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, const int32_t* table,
                             const uint8_t* pool, const ClassView& c, const uint16_t* hbuf,
-                            float* ybuf, uint32_t* err, hipStream_t s);
-hipError_t launch_combine(const float* ybuf, const float* topk_w, int T, int k, int H,
+                            uint16_t* ybuf, uint32_t* err, hipStream_t s);
+hipError_t launch_combine(const uint16_t* ybuf, const float* topk_w, int T, int k, int H,
                           uint16_t* out, hipStream_t s);
 
 }  // namespace moe

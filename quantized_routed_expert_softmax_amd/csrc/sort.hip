@@ -11,9 +11,9 @@
 // a pair's place is offsets[e] + (pairs of e in earlier tiles) + (pairs of e
 // earlier in its own tile), which is the stable order by pair id.
 //   n <= 1024 : one block does everything (decode and small batches).
-//   n >  1024 : tile kernel (per-tile counts and in-tile ranks), then one block
-//               scans the counts, writes offsets and the pass table, and places
-//               every pair.
+//   n >  1024 : tile kernel (per-tile counts and in-tile ranks), one block that
+//               turns the counts into per-tile bases, offsets and the pass table,
+//               and a scatter kernel with one thread per pair.
 #include "../../include/moe.h"
 #include "moe_internal.h"
 
@@ -23,21 +23,34 @@ namespace {
 constexpr int kTile = 256;
 constexpr int kSmallMax = 1024;
 
-// Exclusive scan of s[0..E) in place over a 1024-thread block; returns the total.
+// Inclusive scan over the 64 lanes of a wave (shuffles; integer, exact).
+__device__ inline int wave_inclusive_scan(int v, int lane)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(v, off, 64);
+        if (lane >= off) v += u;
+    }
+    return v;
+}
+
+// Exclusive scan of s[0..E) in place over a 1024-thread block (16 waves): scan
+// within waves, then the 16 wave totals; returns the total.  s_tmp needs 16 ints.
 __device__ int block_exclusive_scan(int* s, int E, int* s_tmp)
 {
-    const int tid = threadIdx.x;
-    int v = tid < E ? s[tid] : 0;
-    s_tmp[tid] = v;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int v = tid < E ? s[tid] : 0;
+    const int inc = wave_inclusive_scan(v, lane);
+    if (lane == 63) s_tmp[wave] = inc;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        int add = tid >= off ? s_tmp[tid - off] : 0;
-        __syncthreads();
-        s_tmp[tid] += add;
-        __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        const int t = s_tmp[w];
+        before += w < wave ? t : 0;
+        total += t;
     }
-    int total = s_tmp[1023];
-    if (tid < E) s[tid] = s_tmp[tid] - v;
+    if (tid < E) s[tid] = before + inc - v;
     __syncthreads();
     return total;
 }
@@ -135,14 +148,12 @@ __global__ __launch_bounds__(kTile) void sort_tile_kernel(const int32_t* __restr
     for (int i = tid; i < E; i += kTile) tc[i] = s_cnt[i];
 }
 
-// One block: per-expert running sums over tiles, offsets, pass table, placement.
-__global__ __launch_bounds__(1024) void sort_place_kernel(const int32_t* __restrict__ ids, int n,
-                                                          int E, int P, int n_tiles,
-                                                          int32_t* __restrict__ tile_counts,
-                                                          const int32_t* __restrict__ rank_in,
-                                                          int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ sorted_pairs,
-                                                          int32_t* __restrict__ pass_table)
+// One block: per-expert running sums over tiles (tile_counts becomes the base of
+// each expert within each tile), offsets and the pass table.
+__global__ __launch_bounds__(1024) void sort_scan_kernel(int E, int P, int n_tiles,
+                                                         int32_t* __restrict__ tile_counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ pass_table)
 {
     __shared__ int s_cnt[1024];
     __shared__ int s_tmp[1024];
@@ -168,28 +179,21 @@ __global__ __launch_bounds__(1024) void sort_place_kernel(const int32_t* __restr
     }
     __syncthreads();
     write_offsets_and_passes(s_cnt, s_tmp, s_hit, E, P, offsets, pass_table);
-    __syncthreads();
-    // placement, 8 pairs per thread per round (independent loads first)
-    for (int p0 = tid; p0 < n; p0 += 1024 * 8) {
-        int e[8], r[8], tb[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int p = p0 + 1024 * j;
-            e[j] = p < n ? ids[p] : -1;
-            r[j] = p < n ? rank_in[p] : 0;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int p = p0 + 1024 * j;
-            const bool ok = e[j] >= 0 && e[j] < E;
-            tb[j] = ok ? tile_counts[(size_t)(p / kTile) * E + e[j]] : 0;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int p = p0 + 1024 * j;
-            if (e[j] >= 0 && e[j] < E) sorted_pairs[s_cnt[e[j]] + tb[j] + r[j]] = p;
-        }
-    }
+}
+
+// One thread per pair: place = offsets[e] + base of e in the pair's tile + rank in tile.
+__global__ __launch_bounds__(kTile) void sort_scatter_kernel(const int32_t* __restrict__ ids, int n, int E,
+                                                             const int32_t* __restrict__ tile_base,
+                                                             const int32_t* __restrict__ rank_in,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted_pairs)
+{
+    const int p = blockIdx.x * kTile + threadIdx.x;
+    if (p >= n) return;
+    const int e = ids[p];
+    if (e < 0 || e >= E) return;  // flagged by the tile kernel
+    const int r = rank_in[p];
+    sorted_pairs[offsets[e] + tile_base[(size_t)blockIdx.x * E + e] + r] = p;
 }
 
 }  // namespace
@@ -219,8 +223,12 @@ hipError_t launch_sort(const int32_t* ids, int T, int k, int E, int P, int32_t* 
                        ranks, err);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sort_place_kernel, dim3(1), dim3(1024), 0, s, ids, n, E, P, tiles,
-                       tile_counts, ranks, offsets, sorted_pairs, pass_table);
+    hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), 0, s, E, P, tiles, tile_counts, offsets,
+                       pass_table);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sort_scatter_kernel, dim3(tiles), dim3(kTile), 0, s, ids, n, E, tile_counts, ranks,
+                       offsets, sorted_pairs);
     return hipGetLastError();
 }
 
