@@ -573,24 +573,6 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
         // words never waits for the weights.
         poll(tid);
         issue_p2(pre, 0);
-        // a second look at the first words a little later, without waiting for the
-        // first: a word published just after the first poll then costs no extra
-        // round trip
-        uint64_t hv2[R];
-        __builtin_amdgcn_s_sleep(8);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int q = tid + kThreads * r;
-            hv2[r] = q < nh ? __hip_atomic_load(&P.xw[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag_hi;
-        }
-        bool stale = false;
-#pragma unroll
-        for (int r = 0; r < R; ++r) stale = stale || (uint32_t)(hv[r] >> 32) != tag;
-        if (stale) {
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-                if ((uint32_t)(hv[r] >> 32) != tag) hv[r] = hv2[r];
-        }
         for (int q0 = tid; q0 < nh; q0 += kThreads * R) {
             if (q0 != tid) poll(q0);
             unsigned spins = 0;
