@@ -465,6 +465,7 @@ struct alignas(16) RouteWgScratch {
     float top[64 + 4];  // per-wave top keys (wave w: [w*r, w*r + r)), padded for vector reads
     float red[3][W];    // per-wave max of the logits, max and min of p
     int bad[W];
+    float tau;
     int count;          // candidates placed so far
     float v[64 * W];    // e_i by expert
 };
@@ -497,9 +498,6 @@ __device__ bool route_token_wg(const float* __restrict__ lr, int E, int k, int m
         ws->bad[wave] = anybad ? 1 : 0;
     }
     __syncthreads();
-    // every wave is past the previous call here (it read that call's count before
-    // this barrier), so the candidate counter can be reset for this one
-    if (threadIdx.x == 0) ws->count = 0;
     float m = -INFINITY;
     int nb = 0;
 #pragma unroll
@@ -555,11 +553,8 @@ __device__ bool route_token_wg(const float* __restrict__ lr, int E, int k, int m
         }
     }
     __syncthreads();
-    // tau = k-th largest of the listed keys (equal keys ranked by list position).
-    // Every wave finds it itself: the ranks are distinct, so exactly one lane holds
-    // rank k - 1, and no barrier is needed before the candidates are placed.
-    float tau;
-    {
+    // tau = k-th largest of the listed keys (equal keys ranked by list position)
+    if (wave == 0) {
         const float tv = lane < nt ? ws->top[lane] : -INFINITY;
         int rank = 0;
         for (int q = 0; q < nt; q += 4) {
@@ -569,9 +564,11 @@ __device__ bool route_token_wg(const float* __restrict__ lr, int E, int k, int m
             rank += (int)((q + 2 < nt) & ((t4.z > tv) | ((t4.z == tv) & (q + 2 < lane))));
             rank += (int)((q + 3 < nt) & ((t4.w > tv) | ((t4.w == tv) & (q + 3 < lane))));
         }
-        const unsigned long long hm = __ballot(lane < nt && rank == k - 1);
-        tau = __shfl(tv, __ffsll((long long)hm) - 1, 64);
+        if (lane < nt && rank == k - 1) ws->tau = tv;
+        if (lane == 0) ws->count = 0;
     }
+    __syncthreads();
+    const float tau = ws->tau;
     const bool cand = valid && key >= tau;
     const unsigned long long cm = __ballot(cand);
     int base = 0;
