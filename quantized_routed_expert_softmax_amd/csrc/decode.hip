@@ -227,6 +227,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     __shared__ int32_t s_hit[kMaxPairs];
     __shared__ int32_t s_base[kMaxPairs + 1];
     __shared__ int32_t s_slot[kMaxPairs];  // slot of each hit (-1: not resident, skipped)
+    __shared__ int s_hstate[kMaxPairs];    // h of a hit in LDS: 0 not yet, 1 being staged, 2 ready
     __shared__ int32_t s_cnt[2];  // n_hit, n_valid
     __shared__ unsigned s_gen;
     __shared__ RouteScratch s_rsc[kWaves];
@@ -393,6 +394,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
             s_base[nh] = __popcll(vm);
         }
     }
+    if (tid < kMaxPairs) s_hstate[tid] = 0;
     __syncthreads();
     const int n_hit = s_cnt[0];
 
@@ -552,70 +554,84 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     }
 
 
-    // ---- stage h of every valid pair (P16, unit-contiguous: layout swz),
-    //      polling each tagged word until it carries this call's tag.  Consecutive
-    //      lanes poll consecutive words (one request per 64 bytes). ----
-    const int n_valid = s_cnt[1];
-    {
-        constexpr int R = 8;
-        const int nh = n_valid * (I / 2);
-        uint64_t hv[R];
-        auto poll = [&](int q0) {
+    // ---- h of each hit, staged when a wave first needs it: the wave that claims
+    //      a hit polls the tagged words of its pairs (P16, unit-contiguous layout
+    //      swz) until they carry this call's tag, adds their unit sums, and marks
+    //      the hit ready; a wave that needs a hit claimed by another waits for that
+    //      mark in LDS.  A wave so waits only for the experts of its own items, not
+    //      for the slowest expert of the layer. ----
+    issue_p2(pre, 0);  // the phase-2 weights stream in while h is exchanged
+    float* s_part = (float*)(s_dyn + P.part_dw);  // [wave][row][t]
+    float* part = s_part + wave * P.rows_per_wg * T;
+    for (int q = lane; q < P.rows_per_wg * T; q += 64) part[q] = 0.0f;  // this wave's rows only
+    auto ensure_hit = [&](int hh) {
+        if (__hip_atomic_load(&s_hstate[hh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 2) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+            return;
+        }
+        int claim = 0;
+        if (lane == 0) claim = atomicCAS(&s_hstate[hh], 0, 1) == 0 ? 1 : 0;
+        claim = __builtin_amdgcn_readfirstlane(claim);
+        if (claim) {
+            constexpr int R = 8;
+            const int q_end = s_base[hh + 1] * (I / 2);
+            for (int q0 = s_base[hh] * (I / 2) + lane; q0 < q_end; q0 += 64 * R) {
+                uint64_t hv[R];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int q = q0 + kThreads * r;
-                hv[r] = q < nh ? __hip_atomic_load(&P.xw[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag_hi;
+                for (int r = 0; r < R; ++r) {
+                    const int q = q0 + 64 * r;
+                    hv[r] = q < q_end ? __hip_atomic_load(&P.xw[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag_hi;
+                }
+                unsigned spins = 0;
+                for (;;) {
+                    bool ready = true;
+#pragma unroll
+                    for (int r = 0; r < R; ++r) ready = ready && (uint32_t)(hv[r] >> 32) == tag;
+                    if (ready) break;
+                    if (++spins > P.spin_limit) {
+                        flag(P.err, MOE_ERRW_TIMEOUT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const int q = q0 + 64 * r;
+                        if ((uint32_t)(hv[r] >> 32) != tag)
+                            hv[r] = __hip_atomic_load(&P.xw[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int q = q0 + 64 * r;
+                    if (q < q_end) {
+                        const int pos = q / (I / 2);
+                        const int rr = q - pos * (I / 2);
+                        s_h2[pos * (I / 2) + swz(rr >> 4, rr & 15)] = (uint32_t)hv[r];
+                    }
+                }
             }
-        };
-        // First poll, then the phase-2 weight loads (they do not depend on h and
-        // stream in during the exchange).  Loads complete in issue order as far
-        // as the wait counter is concerned, so the poll goes first: reading its
-        // words never waits for the weights.
-        poll(tid);
-        issue_p2(pre, 0);
-        for (int q0 = tid; q0 < nh; q0 += kThreads * R) {
-            if (q0 != tid) poll(q0);
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            for (int c = s_base[hh] * Ud + lane; c < s_base[hh + 1] * Ud; c += 64) {
+                const int pos = c / Ud, u = c - pos * Ud;
+                s_xs2[c] = unit_sum(s_h2 + pos * (I / 2), u);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            if (lane == 0) __hip_atomic_store(&s_hstate[hh], 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        } else {
             unsigned spins = 0;
-            for (;;) {
-                bool ready = true;
-#pragma unroll
-                for (int r = 0; r < R; ++r) ready = ready && (uint32_t)(hv[r] >> 32) == tag;
-                if (ready) break;
+            while (__hip_atomic_load(&s_hstate[hh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 2) {
                 if (++spins > P.spin_limit) {
                     flag(P.err, MOE_ERRW_TIMEOUT);
                     break;
                 }
-                __builtin_amdgcn_s_sleep(2);
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int q = q0 + kThreads * r;
-                    if ((uint32_t)(hv[r] >> 32) != tag)
-                        hv[r] = __hip_atomic_load(&P.xw[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
+                __builtin_amdgcn_s_sleep(1);
             }
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int q = q0 + kThreads * r;
-                if (q < nh) {
-                    const int pos = q / (I / 2);
-                    const int rr = q - pos * (I / 2);
-                    s_h2[pos * (I / 2) + swz(rr >> 4, rr & 15)] = (uint32_t)hv[r];
-                }
-            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         }
-    }
-    __syncthreads();
-    // per-unit sums of h (read by phase 2)
-    for (int c = tid; c < n_valid * Ud; c += kThreads) {
-        const int pos = c / Ud, u = c - pos * Ud;
-        s_xs2[c] = unit_sum(s_h2 + pos * (I / 2), u);
-    }
-    float* s_part = (float*)(s_dyn + P.part_dw);  // [wave][row][t]
-    for (int q = tid; q < kWaves * P.rows_per_wg * T; q += kThreads) s_part[q] = 0.0f;
-    __syncthreads();
+    };
 
     // ---- phase 2: down + weighted combine ----
-    float* part = s_part + wave * P.rows_per_wg * T;
     for (int d0 = 0; d0 < n_items2; d0 += D2) {
         if (d0 > 0) issue_p2(pre, d0);
         RowLoad<BD, UD>* cur = pre;
@@ -627,6 +643,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
             const int lrow = rg * rpp_d + rloc_d;
             const int nrow = row0 + lrow;
             if (s_slot[h] < 0) continue;
+            ensure_hit(h);
             const int pend = s_base[h + 1];
             for (int pos = s_base[h]; pos < pend; ++pos) {
                 const int pair = s_sorted[pos];
