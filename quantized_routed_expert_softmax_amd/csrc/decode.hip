@@ -232,6 +232,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     __shared__ unsigned s_gen;
     __shared__ RouteScratch s_rsc[kWaves];
     __shared__ RouteWgScratch<kWaves> s_rwg;
+    __shared__ RouteSelScratch s_rsel;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = gridDim.x;
@@ -317,14 +318,53 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
         s_xs1[q] = unit_sum(s_act + t * (H / 2), u);
     }
 
+    if (tid < kMaxPairs) s_hstate[tid] = 0;  // read in phase 2, after the barriers below
+
     // ---- routing from LDS (one wave per token), identical to the router kernel ----
     // (few tokens: all waves route each token together; more: one wave per token)
+    bool presorted = false;  // one routed token: the routing wave also sorts its pairs
     if (P.logits) {
         if (T <= 3 && E >= 64) {
-            for (int t = 0; t < T; ++t) {
-                const bool ok = route_token_wg<kWaves>(s_logit + t * E, E, k, P.mode, P.L, s_table,
-                                                       s_ids + t * k, s_w + t * k, &s_rsc[0], &s_rwg);
+            // plain mode: by logit order (one barrier); else by selection key
+            const bool by_logit = P.mode == MOE_ROUTE_PLAIN && k <= 15 && E <= 64 * (kWaves < 8 ? kWaves : 8);
+            // (one token without a loop: the loop's hoisted set-up costs more than the routing)
+            if (by_logit && T == 1) {
+                const bool ok = route_token_sel<kWaves>(s_logit, E, k, s_ids, s_w, &s_rsc[0], &s_rsel, 0);
                 if (!ok && wg0 && tid == 0) flag(P.err, MOE_ERRW_NONFINITE);
+                if (wave == route_sel_wave<kWaves>(E)) {
+                    // the k experts of one token are distinct: pair j goes to the rank of
+                    // its expert, which is also its hit index (one pair per hit)
+                    const int e = lane < k ? s_ids[lane] : 0x7fffffff;
+                    int rank = 0;
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) rank += __builtin_amdgcn_readlane(e, q) < e ? 1 : 0;
+                    if (lane < k) {
+                        s_sorted[rank] = lane;
+                        s_hit[rank] = e;
+                        s_base[rank] = rank;
+                        int32_t slot = s_table[e];
+                        if (slot < 0 || slot >= P.n_slots) {
+                            if (wg0) flag(P.err, slot < 0 ? MOE_ERRW_NOT_RESIDENT : MOE_ERRW_BAD_SLOT);
+                            slot = -1;
+                        }
+                        s_slot[rank] = slot;
+                    }
+                    if (lane == 0) {
+                        s_cnt[0] = k;
+                        s_cnt[1] = k;
+                        s_base[k] = k;
+                    }
+                }
+                presorted = true;
+            } else {
+                for (int t = 0; t < T; ++t) {
+                    const bool ok =
+                        by_logit ? route_token_sel<kWaves>(s_logit + t * E, E, k, s_ids + t * k, s_w + t * k,
+                                                           &s_rsc[0], &s_rsel, t & 1)
+                                 : route_token_wg<kWaves>(s_logit + t * E, E, k, P.mode, P.L, s_table, s_ids + t * k,
+                                                          s_w + t * k, &s_rsc[0], &s_rwg);
+                    if (!ok && wg0 && tid == 0) flag(P.err, MOE_ERRW_NONFINITE);
+                }
             }
         } else {
             for (int t = wave; t < T; t += kWaves) {
@@ -345,7 +385,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     // dup = earlier pairs with the same expert.  Sorted position = |lt| + dup;
     // hit index = first occurrences among lt.  Experts are read back from LDS
     // four at a time (broadcast reads); pairs past n hold the sentinel.
-    if (wave == 0) {
+    if (!presorted && wave == 0) {
         int e = 0x7fffffff;  // invalid pairs sort after every expert and are dropped
         if (lane < n) {
             e = s_ids[lane];
@@ -394,8 +434,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
             s_base[nh] = __popcll(vm);
         }
     }
-    if (tid < kMaxPairs) s_hstate[tid] = 0;
-    __syncthreads();
+    if (!presorted) __syncthreads();  // (presorted: the routing's barrier ordered the sort)
     const int n_hit = s_cnt[0];
 
     // ---- weight loads: phase 1 rows now, the phase-2 rows once phase 1 is done
@@ -779,7 +818,7 @@ bool decode_fused_supported(int T, int k, int E, const ClassView& c)
     if ((size_t)n * (c.I / 2) > (size_t)MOE_WS_XWORDS) return false;  // tagged h words
     if (c.slot_bytes >= ((int64_t)1 << 31)) return false;                // 32-bit offsets in a slot
     const size_t static_lds = sizeof(int32_t) * (kMaxE + 8 * kMaxPairs) + sizeof(RouteScratch) * v->w +
-                              sizeof(RouteWgScratch<10>) + 64;
+                              sizeof(RouteWgScratch<10>) + sizeof(RouteSelScratch) + 64;
     return lds_layout(T, k, E, c.H, c.I, rows, v->w).bytes + static_lds <= di.lds_per_block;
 }
 

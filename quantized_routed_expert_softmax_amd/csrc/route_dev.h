@@ -590,6 +590,230 @@ __device__ bool route_token_wg(const float* __restrict__ lr, int E, int k, int m
     return true;
 }
 
+// ---------------------------------------------------------------------------
+// Plain-mode workgroup routing by logit order (64 <= E <= 512, k <= 15).
+//
+// p_i is a function of logit_i alone once m and Z are fixed, and that function
+// rises with the logit except within rounding: if l_a < l_b - 2^-10 and
+// l_b - m >= -64, the contract's arithmetic gives p_a < p_b.  (The rounded
+// l - m is within 2^-18 of the exact difference for |l - m| < 128; exp_c is
+// within a few ulp of e^x; e^(-2^-10 + 2^-17) < 1 - 2^-11, far more than those
+// errors, and dividing both by the same Z keeps a gap of 2^-11 relative, far
+// more than one ulp of a normal p.)  So when every logit outside a set of k
+// experts is at least 2^-9 below every logit inside it, and those are at least
+// m - 64, the set holds exactly the k experts of largest p, whatever the ties
+// elsewhere; their order is then taken from their exact p (ties: smaller id
+// first).  Otherwise (near-ties at the boundary, far underflow) the token is
+// routed by the single-wave routine.  Either way the result is the contract's.
+//
+// The set is found on 32-bit keys: the logit's bits mapped to an unsigned
+// integer that orders like the value, its low 9 bits replaced by 511 - id, so
+// keys are distinct and a key bounds its logit to a bucket of 512 neighbouring
+// floats.  Waves 0..nl-1 (nl = ceil(E/64)) each sort their 64 keys (bitonic,
+// lane moves and min/max) and list their 16 largest; wave zw computes m and Z
+// meanwhile.  After one barrier wave zw merges the lists into the 16 largest
+// keys overall, c_0 > c_1 > ...; the chosen set is c_0..c_(k-1), every other
+// logit is at most the top of c_k's bucket, every chosen one at least the
+// bottom of c_(k-1)'s, and the test above is made on those two bounds.
+// ---------------------------------------------------------------------------
+struct alignas(16) RouteSelScratch {
+    uint32_t list[2][8][16];  // per token parity: per wave its 16 largest keys, descending
+    int bad[2][8];            // per token parity: wave saw a non-finite logit
+};
+
+__device__ __forceinline__ uint32_t logit_order_bits(float l)
+{
+    const uint32_t u = __float_as_uint(l);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// inverse of logit_order_bits
+__device__ __forceinline__ float order_bits_logit(uint32_t v)
+{
+    return __uint_as_float((v & 0x80000000u) ? (v & 0x7fffffffu) : ~v);
+}
+__device__ __forceinline__ uint32_t logit_key32(float l, int id)
+{
+    return (logit_order_bits(l) & ~0x1ffu) | (uint32_t)(0x1ff - id);
+}
+constexpr uint32_t kPadKey32 = 0u;  // below every logit's key
+
+// (every lane reads a lane of its own row for the moves used with it, except the
+// row shifts of xor4_u32, whose out-of-row lanes are not selected)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+// lane i ^ 4 within a row: row shift right by 4 (lane i - 4) or left by 4 (lane i + 4)
+__device__ __forceinline__ uint32_t xor4_u32(uint32_t v, int lane)
+{
+    const uint32_t up = dpp_u32<0x114>(v), dn = dpp_u32<0x104>(v);
+    return (lane & 4) ? up : dn;
+}
+// lane i ^ 16 resp. i ^ 32: each swap returns this lane's value and its partner's
+// in some order, so the partner's is their xor with this lane's
+__device__ __forceinline__ uint32_t swap16_u32(uint32_t v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return r[0] ^ r[1] ^ v;
+}
+__device__ __forceinline__ uint32_t swap32_u32(uint32_t v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return r[0] ^ r[1] ^ v;
+}
+
+// One compare-exchange of a sorting network: the larger of this lane's key and
+// its partner's when keep_max, else the smaller.
+__device__ __forceinline__ uint32_t cx_u32(uint32_t own, uint32_t partner, bool keep_max)
+{
+    const uint32_t mx = own > partner ? own : partner, mn = own < partner ? own : partner;
+    return keep_max ? mx : mn;
+}
+
+// A row of 16 lanes holding a bitonic sequence -> sorted descending.
+__device__ __forceinline__ uint32_t row_clean_u32(uint32_t K, int lane)
+{
+    K = cx_u32(K, dpp_u32<0x128>(K), (lane & 8) == 0);  // row rotate by 8 = lane i ^ 8
+    K = cx_u32(K, xor4_u32(K, lane), (lane & 4) == 0);
+    K = cx_u32(K, dpp_u32<0x4E>(K), (lane & 2) == 0);
+    K = cx_u32(K, dpp_u32<0xB1>(K), (lane & 1) == 0);
+    return K;
+}
+
+// Every row of 16 lanes sorted descending: blocks of 2, 4, 8, 16 in turn, each
+// merged from its two sorted halves by comparing lane i with its mirror in the
+// block (the halves become bitonic) and cleaning the halves.
+__device__ __forceinline__ uint32_t row_sort_u32(uint32_t K, int lane)
+{
+    K = cx_u32(K, dpp_u32<0xB1>(K), (lane & 1) == 0);   // blocks of 2
+    K = cx_u32(K, dpp_u32<0x1B>(K), (lane & 2) == 0);   // blocks of 4: quad mirror
+    K = cx_u32(K, dpp_u32<0xB1>(K), (lane & 1) == 0);
+    K = cx_u32(K, dpp_u32<0x141>(K), (lane & 4) == 0);  // blocks of 8: half-row mirror
+    K = cx_u32(K, dpp_u32<0x4E>(K), (lane & 2) == 0);
+    K = cx_u32(K, dpp_u32<0xB1>(K), (lane & 1) == 0);
+    K = cx_u32(K, dpp_u32<0x140>(K), (lane & 8) == 0);  // the row: row mirror
+    K = cx_u32(K, xor4_u32(K, lane), (lane & 4) == 0);
+    K = cx_u32(K, dpp_u32<0x4E>(K), (lane & 2) == 0);
+    K = cx_u32(K, dpp_u32<0xB1>(K), (lane & 1) == 0);
+    return K;
+}
+
+// Rows holding descending runs A (this row) and B (`other`, the partner row's
+// run brought to this row): the 16 largest of both, descending.  max(A_i,
+// B_(15-i)) is those 16 as a bitonic sequence.
+__device__ __forceinline__ uint32_t row_merge_u32(uint32_t K, uint32_t other, int lane)
+{
+    const uint32_t b = dpp_u32<0x140>(other);
+    return row_clean_u32(K > b ? K : b, lane);
+}
+
+// The wave of route_token_sel that writes the result.
+template <int W>
+__device__ __forceinline__ int route_sel_wave(int E)
+{
+    return ((E + 63) >> 6) < W ? W - 1 : 0;
+}
+
+template <int W>
+__device__ __forceinline__ bool route_token_sel(const float* __restrict__ lr, int E, int k, int32_t* ids, float* w,
+                                                RouteScratch* sc, RouteSelScratch* rs, int par)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nl = (E + 63) >> 6;
+    const int zw = route_sel_wave<W>(E);  // computes m and Z, merges, writes the result
+    if (wave < nl) {
+        const int e = wave * 64 + lane;
+        const bool valid = e < E;
+        const float l = valid ? lr[e] : 0.0f;
+        const bool bad = __any(valid && !isfinite(l));
+        uint32_t K = valid ? logit_key32(l, e) : kPadKey32;
+        K = row_sort_u32(K, lane);
+        K = row_merge_u32(K, swap16_u32(K), lane);  // rows 0 and 2: 16 largest of rows 0-1, 2-3
+        K = row_merge_u32(K, swap32_u32(K), lane);  // row 0: 16 largest of the wave
+        if (lane < 16) rs->list[par][wave][lane] = K;
+        if (lane == 0) rs->bad[par][wave] = bad ? 1 : 0;
+    }
+    float m = -INFINITY, Z = 0.0f;
+    if (wave == zw) {
+        // m and Z exactly as the single-wave routine: lane l holds experts l + 64j
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int i = lane + 64 * j;
+            v[j] = lr[i < E ? i : E - 1];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (lane + 64 * j < E) m = fmaxf(m, v[j]);
+        m = wave_max_f(m);
+        float S = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float ej = (lane + 64 * j < E) ? exp_contract(v[j] - m) : 0.0f;
+            S = S + ej;
+        }
+        Z = tree_sum_lane0(S);
+    }
+    __syncthreads();
+    int nb = 0;
+    for (int i = 0; i < nl; ++i) nb |= rs->bad[par][i];
+    if (nb) {
+        if (wave == zw && lane < k) {
+            ids[lane] = lane;
+            w[lane] = 0.0f;
+        }
+        return false;
+    }
+    if (wave != zw) return true;
+
+    // merge the lists: lists 0-3 in rows 0-3, lists 4-7 under them
+    const int r = lane >> 4;
+    const uint32_t A = r < nl ? rs->list[par][r][lane & 15] : kPadKey32;
+    const uint32_t Bv = r + 4 < nl ? rs->list[par][r + 4][lane & 15] : kPadKey32;
+    uint32_t K = row_merge_u32(A, Bv, lane);
+    K = row_merge_u32(K, swap16_u32(K), lane);
+    K = row_merge_u32(K, swap32_u32(K), lane);  // row 0: the 16 largest keys, descending
+
+    const int id = 0x1ff - (int)(K & 0x1ffu);
+    const float lx = lane < k ? lr[id] : 0.0f;  // exact logit of a chosen expert
+    const uint32_t c_last = (uint32_t)__builtin_amdgcn_readlane((int)K, k - 1);
+    const uint32_t c_next = (uint32_t)__builtin_amdgcn_readlane((int)K, k);
+    const float lo_in = order_bits_logit(c_last & ~0x1ffu);                         // every chosen logit >=
+    const float hi_out = c_next == kPadKey32 ? -INFINITY : order_bits_logit(c_next | 0x1ffu);  // every other <=
+    if (!(lo_in - m >= -64.0f && lo_in - hi_out >= 0x1p-9f))
+        return route_token_512(lr, E, k, MOE_ROUTE_PLAIN, 0.0f, nullptr, lane, ids, w, sc);
+
+    // exact p of the chosen k, ordered by (p desc, id asc)
+    const float p = lane < k ? __fdiv_rn(exp_contract(lx - m), Z) : 0.0f;
+    uint64_t P = lane < k ? (((uint64_t)__float_as_uint(p) << 32) | (uint32_t)~id) : 0ull;
+    const uint64_t next = ((uint64_t)dpp_u32<0x101>((uint32_t)(P >> 32)) << 32) | dpp_u32<0x101>((uint32_t)P);
+    if (__ballot(lane + 1 < k && !(P > next))) {
+        // rare (p rounds equal or out of logit order): sort the 16 lanes of row 0
+        // by (p, ~id) with the 64-bit keys, two words per step
+#pragma unroll
+        for (int st = 0; st < 16; ++st) {
+            // odd-even transposition sort, 16 rounds over 16 lanes (row shifts by 1)
+            const uint32_t dh = (st & 1) == (lane & 1) ? dpp_u32<0x101>((uint32_t)(P >> 32)) : dpp_u32<0x111>((uint32_t)(P >> 32));
+            const uint32_t dl = (st & 1) == (lane & 1) ? dpp_u32<0x101>((uint32_t)P) : dpp_u32<0x111>((uint32_t)P);
+            const uint64_t Q = ((uint64_t)dh << 32) | dl;
+            const bool lower = (st & 1) == (lane & 1);  // this lane is the left one of its pair
+            const bool edge = lower ? (lane & 15) == 15 : (lane & 15) == 0;
+            if (!edge) P = lower ? (P > Q ? P : Q) : (P < Q ? P : Q);
+        }
+    }
+    const float ps = __uint_as_float((uint32_t)(P >> 32));
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)  // lanes past k hold p = +0, which leaves the sum unchanged
+        s = s + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ps), q));
+    if (lane < k) {
+        ids[lane] = (int)~(uint32_t)P;
+        w[lane] = __fdiv_rn(ps, s);
+    }
+    return true;
+}
+
 __device__ __forceinline__ bool route_token(const float* __restrict__ lr, int E, int k, int mode,
                                             float L, const int32_t* __restrict__ table, int lane,
                                             int32_t* ids, float* w, RouteScratch* sc)

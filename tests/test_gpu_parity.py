@@ -567,6 +567,91 @@ def test_layer_forward_workgroup_routing(T, E, k, mode, kind, seed):
         check_close(out, ref, f"wg routing {T} {E} {k}")
 
 
+def _boundary_rows(E, k, seed):
+    """Logit rows that drive the plain-mode routing by logit order through each of
+    its branches: a clear gap after the k-th largest logit (taken by logit order),
+    the (k+1)-th one ulp below or equal to the k-th (near-tie: routed by key
+    instead), chosen logits one ulp apart with the larger one on the larger id (p
+    may round equal, then the smaller id goes first), the k-th far below the max
+    (p underflows: routed by key), large magnitudes, and coarse values (ties)."""
+    rng = synth.rng_for(seed, 700)
+    rows = []
+    base = synth.gen_logits(rng, 1, E)[0]
+    rows.append(base.copy())
+    order = np.argsort(-base, kind="stable")
+    kk = min(k, E - 1)
+    r = base.copy()
+    r[order[kk]] = np.nextafter(r[order[kk - 1]], np.float32(-np.inf))
+    rows.append(r)
+    r = base.copy()
+    r[order[kk]] = r[order[kk - 1]]
+    rows.append(r)
+    r = base.copy()
+    hi = np.sort(rng.choice(E, size=min(2 * kk, E), replace=False))
+    for a, b in zip(hi[0::2], hi[1::2]):  # b > a: the larger logit on the larger id
+        r[a] = np.float32(3.0)
+        r[b] = np.nextafter(np.float32(3.0), np.float32(np.inf))
+    rows.append(r)
+    r = np.full(E, -80.0, np.float32) + rng.standard_normal(E).astype(np.float32)
+    r[rng.integers(E)] = 0.0
+    rows.append(r)
+    rows.append((base * 3000.0).astype(np.float32))
+    rows.append((np.round(base * 2.0) / 2.0).astype(np.float32))
+    r = base.copy()
+    r[order[:kk]] += np.float32(1.0)
+    r[order[kk]] = r[order[kk - 1]] - np.float32(2.0 ** -9)  # just at the gap bound
+    rows.append(r.astype(np.float32))
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("E,k", [(512, 10), (512, 15), (512, 16), (512, 1), (320, 8), (100, 7), (64, 15)])
+def test_layer_forward_logit_order_routing(E, k):
+    """Plain-mode routing inside the fused kernel (T <= 3, 64 <= E <= 512, k <= 15
+    by logit order; k = 16 by key): ids and weights equal the oracle's bit for bit
+    on rows built to reach every branch, one, two and three tokens per call."""
+    torch = _torch()
+    H, I = 128, 64
+    rows = _boundary_rows(E, k, 710 + E + k)
+    pr = synth.make_problem(711, 3, H, E, I, k, 4, 4, n_slots=E, gaussian=False)
+    desc = B.moe_size_class_init(H, I, 4, 4, E)
+    x, table, pool = dev_bf16(pr.x), to_dev(pr.table), to_dev(pr.pool.reshape(-1))
+    for T in (1, 2, 3):
+        for i in range(0, rows.shape[0], T):
+            lg = rows[i:i + T]
+            if lg.shape[0] < T:
+                lg = np.concatenate([lg, rows[:T - lg.shape[0]]])
+            ew = err_word()
+            _, ids, w = B.moe_layer_forward(to_dev(lg), x[:T], table, pool, desc, k, err_word=ew)
+            torch.cuda.synchronize()
+            ids_o, w_o = oracle.route(lg, k)
+            assert np.array_equal(ids.cpu().numpy(), ids_o), (T, i)
+            assert np.array_equal(w.cpu().numpy().view(np.uint32), w_o.view(np.uint32)), (T, i)
+            assert int(ew.item()) == 0
+
+
+def test_layer_forward_routing_nonfinite():
+    """A non-finite logit in the fused kernel's routing: error bit set, that
+    token's ids 0..k-1 with weight 0 (as the router kernel), the other tokens
+    routed as usual."""
+    torch = _torch()
+    H, I, E, k = 128, 64, 512, 10
+    pr = synth.make_problem(712, 3, H, E, I, k, 4, 4, n_slots=E, gaussian=False)
+    desc = B.moe_size_class_init(H, I, 4, 4, E)
+    for bad in (np.nan, np.inf, -np.inf):
+        lg = pr.logits.copy()
+        lg[1, 333] = bad
+        ew = err_word()
+        _, ids, w = B.moe_layer_forward(to_dev(lg), dev_bf16(pr.x), to_dev(pr.table),
+                                        to_dev(pr.pool.reshape(-1)), desc, k, err_word=ew)
+        torch.cuda.synchronize()
+        assert int(ew.item()) & B.MOE_ERRW_NONFINITE
+        ids, w = ids.cpu().numpy(), w.cpu().numpy()
+        assert np.array_equal(ids[1], np.arange(k)) and not w[1].any()
+        ids_o, w_o = oracle.route(lg[[0, 2]], k)
+        assert np.array_equal(ids[[0, 2]], ids_o)
+        assert np.array_equal(w[[0, 2]].view(np.uint32), w_o.view(np.uint32))
+
+
 def test_fused_decode_repeated_calls_and_graph_replay():
     """The fused kernel's h exchange lives in the workspace's reserved prefix:
     1024 call-tag counters (dwords 64..1087, all equal to the number of fused
