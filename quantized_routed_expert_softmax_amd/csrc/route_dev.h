@@ -39,6 +39,27 @@ __device__ __forceinline__ float exp_contract(float x)
     return p * __uint_as_float((uint32_t)(ni + 127) << 23);
 }
 
+// exp_contract without a branch, so that independent calls interleave: the same
+// arithmetic for x >= -86 (the clamp does not touch those), 0 below.  For
+// finite x only (a NaN gives a finite value here).
+__device__ __forceinline__ float exp_contract_nb(float x)
+{
+    const float xc = fmaxf(x, -87.0f);
+    const float n = __builtin_rintf(xc * 1.44269502f);
+    float r = __builtin_fmaf(-n, __uint_as_float(0x3f317218u), xc);
+    r = __builtin_fmaf(-n, __uint_as_float(0xb102e308u), r);
+    float p = (float)(1.0 / 5040.0);
+    p = __builtin_fmaf(p, r, (float)(1.0 / 720.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 120.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 24.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 6.0));
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    const float y = p * __uint_as_float((uint32_t)((int)n + 127) << 23);
+    return x < -86.0f ? 0.0f : y;
+}
+
 // Max / min over the wave, every lane gets the result: DPP moves within rows of
 // 16 (quad xor 1, quad xor 2, half-row mirror, row mirror), then the gfx950 row
 // swaps for lane i ^ 16 and i ^ 32 (each swap returns the lane's own value and
@@ -744,15 +765,17 @@ __device__ __forceinline__ bool route_token_sel(const float* __restrict__ lr, in
             v[j] = lr[i < E ? i : E - 1];
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (lane + 64 * j < E) m = fmaxf(m, v[j]);
+        for (int j = 0; j < 8; ++j) v[j] = lane + 64 * j < E ? v[j] : -INFINITY;
+        m = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
         m = wave_max_f(m);
+        // (a non-finite logit makes the token's result be discarded below, so the
+        // branch-free exp may see only finite values that matter; -inf gives 0)
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = lane + 64 * j < E ? exp_contract_nb(v[j] - m) : 0.0f;
         float S = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float ej = (lane + 64 * j < E) ? exp_contract(v[j] - m) : 0.0f;
-            S = S + ej;
-        }
+        for (int j = 0; j < 8; ++j) S = S + e[j];
         Z = tree_sum_lane0(S);
     }
     __syncthreads();
@@ -785,7 +808,7 @@ __device__ __forceinline__ bool route_token_sel(const float* __restrict__ lr, in
         return route_token_512(lr, E, k, MOE_ROUTE_PLAIN, 0.0f, nullptr, lane, ids, w, sc);
 
     // exact p of the chosen k, ordered by (p desc, id asc)
-    const float p = lane < k ? __fdiv_rn(exp_contract(lx - m), Z) : 0.0f;
+    const float p = lane < k ? __fdiv_rn(exp_contract_nb(lx - m), Z) : 0.0f;
     uint64_t P = lane < k ? (((uint64_t)__float_as_uint(p) << 32) | (uint32_t)~id) : 0ull;
     const uint64_t next = ((uint64_t)dpp_u32<0x101>((uint32_t)(P >> 32)) << 32) | dpp_u32<0x101>((uint32_t)P);
     if (__ballot(lane + 1 < k && !(P > next))) {
