@@ -196,3 +196,93 @@ def test_substitution_selection_is_top_k_of_biased_score():
         assert sorted(ids[t].tolist()) == sorted(order[:k].tolist())
         moved += len(set(ids[t].tolist()) - set(np.argsort(-p[t], kind="stable")[:k].tolist()))
     assert moved > 0  # the mode does change some choices at L = 0.15
+
+
+# --------------------------------------------------------------------------- #
+# The logit-order shortcut of the decode kernel's routing (plain mode):       #
+# a model of its selection rule, checked against the oracle's top-k.          #
+# --------------------------------------------------------------------------- #
+def _order_bits(l):
+    u = np.asarray(l, np.float32).view(np.uint32)
+    return np.where(u & 0x80000000, ~u, u | 0x80000000).astype(np.uint32)
+
+
+def _order_bits_logit(v):
+    v = np.asarray(v, np.uint32)
+    return np.where(v & 0x80000000, v & 0x7FFFFFFF, ~v).astype(np.uint32).view(np.float32)
+
+
+def _logit_order_choice(row, k):
+    """The 32-bit keys (order bits, low 9 bits = 511 - id), the k largest as the
+    chosen set, and the gap test on the bucket bounds of the k-th and (k+1)-th
+    keys; returns (test passed, chosen ids)."""
+    E = row.shape[0]
+    ids = np.arange(E, dtype=np.uint32)
+    keys = (_order_bits(row) & np.uint32(0xFFFFFE00)) | (np.uint32(511) - ids)
+    c = np.sort(keys)[::-1]
+    chosen = (np.uint32(511) - (c[:k] & np.uint32(0x1FF))).astype(np.int64)
+    lo_in = _order_bits_logit(c[k - 1] & np.uint32(0xFFFFFE00))
+    hi_out = _order_bits_logit(c[k] | np.uint32(0x1FF))
+    m = np.float32(row.max())
+    ok = (np.float32(lo_in - m) >= np.float32(-64.0)) and (np.float32(lo_in - hi_out) >= np.float32(2.0 ** -9))
+    return bool(ok), chosen
+
+
+def _shortcut_rows(rng, E, k):
+    rows = [synth.gen_logits(rng, 1, E)[0] for _ in range(40)]
+    rows += [(synth.gen_logits(rng, 1, E)[0] * s).astype(np.float32) for s in (1e-3, 0.05, 30.0, 3000.0)]
+    rows += [(np.round(synth.gen_logits(rng, 1, E)[0] * q) / q).astype(np.float32) for q in (2.0, 64.0, 4096.0)]
+    base = synth.gen_logits(rng, 1, E)[0]
+    order = np.argsort(-base, kind="stable")
+    for d in (0.0, 1e-7, 2.0 ** -10, 2.0 ** -9, 2.0 ** -9 + 1e-6, 3e-3):
+        r = base.copy()
+        r[order[:k]] += np.float32(4.0)
+        r[order[k]] = np.float32(r[order[:k]].min() - np.float32(d))
+        rows.append(r.astype(np.float32))
+    r = np.full(E, -70.0, np.float32) + rng.standard_normal(E).astype(np.float32)
+    r[3] = 0.0
+    rows.append(r)
+    r = np.zeros(E, np.float32)
+    rows.append(r)
+    return rows
+
+
+@pytest.mark.parametrize("E,k", [(512, 10), (512, 15), (512, 1), (300, 8), (64, 15)])
+def test_logit_order_shortcut_matches_contract_top_k(E, k):
+    """Where the gap test passes, the k largest logit keys are exactly the
+    contract's top-k set (computed by the oracle from p); the test must pass on
+    ordinary logits and fail on near-ties at the boundary and far underflow."""
+    rng = synth.rng_for(4242, E, k)
+    passed = 0
+    for row in _shortcut_rows(rng, E, k):
+        ok, chosen = _logit_order_choice(row, k)
+        ids_o, _ = oracle.route(row[None, :], k)
+        if ok:
+            passed += 1
+            assert set(chosen.tolist()) == set(ids_o[0].tolist())
+    assert passed >= 30  # ordinary rows take the shortcut
+    # boundary cases: an exact tie and a 1e-7 gap must fail the test
+    base = synth.gen_logits(rng, 1, E)[0]
+    order = np.argsort(-base, kind="stable")
+    for d in (0.0, 1e-7):
+        r = base.copy()
+        r[order[k]] = np.float32(r[order[k - 1]] - np.float32(d))
+        assert not _logit_order_choice(r, k)[0]
+
+
+def test_logit_order_gap_bound_holds_for_exp_c():
+    """The bound the shortcut rests on: logits 2^-10 apart (and at least m - 64)
+    give strictly ordered p under the contract's arithmetic, near every exp_c
+    range-reduction boundary (n ln 2 for integer n) and at random points."""
+    rng = synth.rng_for(4243)
+    m = np.float32(0.0)
+    lb = np.concatenate([(-np.arange(0, 93) * np.log(2)).astype(np.float32),
+                         -rng.uniform(0, 64, 4000).astype(np.float32)])
+    lb = lb[lb >= -64.0]
+    la = (lb - np.float32(2.0 ** -10)).astype(np.float32)
+    eb = oracle.exp_c((lb - m).astype(np.float32))
+    ea = oracle.exp_c((la - m).astype(np.float32))
+    for Z in (np.float32(1.0), np.float32(3.7), np.float32(511.25)):
+        pb = (eb / Z).astype(np.float32)
+        pa = (ea / Z).astype(np.float32)
+        assert np.all(pa < pb)
