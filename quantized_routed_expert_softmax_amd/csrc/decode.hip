@@ -249,6 +249,11 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     uint32_t* s_h2 = s_dyn + P.h2_dw;           // h of every valid pair (P16, layout swz)
     float* s_xs2 = (float*)(s_dyn + P.xs2_dw);  // [pos][unit] sums of h
     if (tid == 0) s_gen = __hip_atomic_load(&P.gen[kGenBase + blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // one routed token in plain mode: routed by logit order, its lists and m, Z
+    // computed from registers before the staging barrier
+    const bool fast1 = P.logits && T == 1 && P.mode == MOE_ROUTE_PLAIN && E >= 64 && k <= 15 &&
+                       E <= 64 * (kWaves < 8 ? kWaves : 8);
+    float r_m = 0.0f, r_Z = 0.0f;
     {
         // all loads of this round are issued before any LDS store
         constexpr int R = 4;
@@ -282,8 +287,16 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
             const int i = tid + kThreads * r;
             tb[r] = P.table[i < E ? i : E - 1];
         }
+        float own = 0.0f, zv[8];
+        if (fast1) {
+            own = P.logits[tid < E ? tid : E - 1];
+            if (wave == route_sel_wave<kWaves>(E)) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) zv[j] = P.logits[lane + 64 * j < E ? lane + 64 * j : E - 1];
+            }
+        }
         float lgv[R];
-        const int nl = P.logits ? T * E : 0;
+        const int nl = (P.logits && !fast1) ? T * E : 0;
         for (int q0 = tid; q0 < nl; q0 += kThreads * R) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -304,6 +317,10 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
         for (int r = 0; r < RT; ++r) {
             const int i = tid + kThreads * r;
             if (i < E) s_table[i] = tb[r];
+        }
+        if (fast1) {
+            if (tid < E) s_logit[tid] = own;
+            route_sel_lists<kWaves>(own, zv, E, &s_rsel, 0, r_m, r_Z);
         }
     }
     __syncthreads();
@@ -328,8 +345,8 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
             // plain mode: by logit order (one barrier); else by selection key
             const bool by_logit = P.mode == MOE_ROUTE_PLAIN && k <= 15 && E <= 64 * (kWaves < 8 ? kWaves : 8);
             // (one token without a loop: the loop's hoisted set-up costs more than the routing)
-            if (by_logit && T == 1) {
-                const bool ok = route_token_sel<kWaves>(s_logit, E, k, s_ids, s_w, &s_rsc[0], &s_rsel, 0);
+            if (fast1) {
+                const bool ok = route_sel_finish<kWaves>(s_logit, E, k, r_m, r_Z, s_ids, s_w, &s_rsc[0], &s_rsel, 0);
                 if (!ok && wg0 && tid == 0) flag(P.err, MOE_ERRW_NONFINITE);
                 if (wave == route_sel_wave<kWaves>(E)) {
                     // the k experts of one token are distinct: pair j goes to the rank of
@@ -631,7 +648,6 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
                         flag(P.err, MOE_ERRW_TIMEOUT);
                         break;
                     }
-                    __builtin_amdgcn_s_sleep(2);
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
                         const int q = q0 + 64 * r;

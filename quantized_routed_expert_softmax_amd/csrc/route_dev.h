@@ -736,17 +736,19 @@ __device__ __forceinline__ int route_sel_wave(int E)
     return ((E + 63) >> 6) < W ? W - 1 : 0;
 }
 
+// Before the barrier: waves 0..nl-1 list their 16 largest keys (own = this
+// thread's logit, expert 64 * wave + lane); wave zw computes m and Z from v[j] =
+// logit of expert lane + 64j (entries past E ignored).  No barrier inside.
 template <int W>
-__device__ __forceinline__ bool route_token_sel(const float* __restrict__ lr, int E, int k, int32_t* ids, float* w,
-                                                RouteScratch* sc, RouteSelScratch* rs, int par)
+__device__ __forceinline__ void route_sel_lists(float own, const float (&v_in)[8], int E, RouteSelScratch* rs,
+                                                int par, float& m, float& Z)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nl = (E + 63) >> 6;
-    const int zw = route_sel_wave<W>(E);  // computes m and Z, merges, writes the result
     if (wave < nl) {
         const int e = wave * 64 + lane;
         const bool valid = e < E;
-        const float l = valid ? lr[e] : 0.0f;
+        const float l = valid ? own : 0.0f;
         const bool bad = __any(valid && !isfinite(l));
         uint32_t K = valid ? logit_key32(l, e) : kPadKey32;
         K = row_sort_u32(K, lane);
@@ -755,20 +757,16 @@ __device__ __forceinline__ bool route_token_sel(const float* __restrict__ lr, in
         if (lane < 16) rs->list[par][wave][lane] = K;
         if (lane == 0) rs->bad[par][wave] = bad ? 1 : 0;
     }
-    float m = -INFINITY, Z = 0.0f;
-    if (wave == zw) {
+    m = -INFINITY;
+    Z = 0.0f;
+    if (wave == route_sel_wave<W>(E)) {
         // m and Z exactly as the single-wave routine: lane l holds experts l + 64j
         float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int i = lane + 64 * j;
-            v[j] = lr[i < E ? i : E - 1];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = lane + 64 * j < E ? v[j] : -INFINITY;
+        for (int j = 0; j < 8; ++j) v[j] = lane + 64 * j < E ? v_in[j] : -INFINITY;
         m = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
         m = wave_max_f(m);
-        // (a non-finite logit makes the token's result be discarded below, so the
+        // (a non-finite logit makes the token's result be discarded, so the
         // branch-free exp may see only finite values that matter; -inf gives 0)
         float e[8];
 #pragma unroll
@@ -778,7 +776,19 @@ __device__ __forceinline__ bool route_token_sel(const float* __restrict__ lr, in
         for (int j = 0; j < 8; ++j) S = S + e[j];
         Z = tree_sum_lane0(S);
     }
-    __syncthreads();
+}
+
+// After the barrier that follows route_sel_lists (lists and logits lr in LDS):
+// every thread returns false if a logit is not finite (wave zw then writes ids
+// 0..k-1 with weight 0), else true; wave zw writes ids and w.
+template <int W>
+__device__ __forceinline__ bool route_sel_finish(const float* __restrict__ lr, int E, int k, float m, float Z,
+                                                 int32_t* ids, float* w, RouteScratch* sc, RouteSelScratch* rs,
+                                                 int par)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nl = (E + 63) >> 6;
+    const int zw = route_sel_wave<W>(E);
     int nb = 0;
     for (int i = 0; i < nl; ++i) nb |= rs->bad[par][i];
     if (nb) {
@@ -835,6 +845,26 @@ __device__ __forceinline__ bool route_token_sel(const float* __restrict__ lr, in
         w[lane] = __fdiv_rn(ps, s);
     }
     return true;
+}
+
+// One token by logit order with all W waves (logits lr in LDS); contains one barrier.
+template <int W>
+__device__ __forceinline__ bool route_token_sel(const float* __restrict__ lr, int E, int k, int32_t* ids, float* w,
+                                                RouteScratch* sc, RouteSelScratch* rs, int par)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int i = lane + 64 * j;
+        v[j] = lr[i < E ? i : E - 1];
+    }
+    const int e = wave * 64 + lane;
+    const float own = lr[e < E ? e : E - 1];
+    float m, Z;
+    route_sel_lists<W>(own, v, E, rs, par, m, Z);
+    __syncthreads();
+    return route_sel_finish<W>(lr, E, k, m, Z, ids, w, sc, rs, par);
 }
 
 __device__ __forceinline__ bool route_token(const float* __restrict__ lr, int E, int k, int mode,
