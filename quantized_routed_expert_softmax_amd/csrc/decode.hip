@@ -149,6 +149,13 @@ __device__ __forceinline__ int pair_row(int j) { return (j & ~31) | ((j >> 1) & 
 // distinct banks.  Dword i of unit u sits at swz(u, i).
 __device__ __forceinline__ int swz(int u, int i) { return 16 * u + ((((i >> 2) ^ (u >> 2)) & 3) << 2) + (i & 3); }
 
+// a / b for a >= 0, b > 0: a shift when b is a power of two (the usual case for
+// the layer's sizes; a general integer division costs tens of instructions)
+__device__ __forceinline__ int udiv(int a, int b)
+{
+    return (b & (b - 1)) == 0 ? (a >> __builtin_ctz(b)) : a / b;
+}
+
 // The 16 dwords of unit u, in order, with four 16-byte LDS reads.
 __device__ __forceinline__ void load_unit_act(const uint32_t* __restrict__ row, int u, uint32_t (&a)[16])
 {
@@ -264,7 +271,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
             for (int r = 0; r < R; ++r) {
                 const int q = q0 + kThreads * r;
                 const int qq = q < nx ? q : nx - 1;
-                const int t = qq / (H / 2);
+                const int t = T == 1 ? 0 : qq / (H / 2);
                 const int rr = qq - t * (H / 2);
                 const uint16_t* src = P.x + (size_t)t * H + 32 * (rr >> 4) + (rr & 15);
                 lo[r] = src[0];
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
             for (int r = 0; r < R; ++r) {
                 const int q = q0 + kThreads * r;
                 if (q < nx) {
-                    const int t = q / (H / 2);
+                    const int t = T == 1 ? 0 : q / (H / 2);
                     const int rr = q - t * (H / 2);
                     s_act[t * (H / 2) + swz(rr >> 4, rr & 15)] = lo[r] | (hi[r] << 16);
                 }
@@ -331,7 +338,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
         __hip_atomic_store(&P.gen[kGenBase + j], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // per-unit sums of x (read by phase 1, after the sort's barrier)
     for (int q = tid; q < T * Ug; q += kThreads) {
-        const int t = q / Ug, u = q - t * Ug;
+        const int t = T == 1 ? 0 : q / Ug, u = q - t * Ug;
         s_xs1[q] = unit_sum(s_act + t * (H / 2), u);
     }
 
@@ -460,11 +467,11 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     // phase-1 item is RW = max(rpp, 2) consecutive indices -- whole pairs -- so the
     // wave that computes it publishes its h words itself.  Wave gw takes items
     // gw, gw + NW, ...; (hit, item in hit) advance by (nw_q, nw_r) per step.
-    const int lpr = P.lpr_gu, rpp = 64 / lpr;
-    const int seg = lane & (lpr - 1), rloc = lane / lpr;
+    const int lpr = P.lpr_gu, rpp = udiv(64, lpr);
+    const int seg = lane & (lpr - 1), rloc = udiv(lane, lpr);
     const int RW = rpp > 1 ? rpp : 2;  // pair-order indices per item
     const int nsub = rpp > 1 ? 1 : 2;  // rows per lane per item
-    const int n_ipr = I / RW;          // items per hit
+    const int n_ipr = udiv(I, RW);     // items per hit
     const int n_items = n_hit * n_ipr;
     const int gw = blockIdx.x * kWaves + wave, NW = G * kWaves;
     const size_t g_row_dw = (size_t)H * BG / 32;
@@ -472,7 +479,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     RowLoad<BG, UG> gr[D1][2], ur[D1][2];
     int ih[D1], iii[D1], islot[D1];
     const uint32_t g_row_b = (uint32_t)(g_row_dw * 4), g_sb_b = (uint32_t)(H / 16);  // bytes per row
-    int h_next = gw / n_ipr, ii_next = gw - (gw / n_ipr) * n_ipr;  // item at it0
+    int h_next = udiv(gw, n_ipr), ii_next = gw - h_next * n_ipr;  // item at it0
     auto issue_p1 = [&](int it0) {
         int h = h_next, ii = ii_next;
 #pragma unroll
@@ -509,11 +516,11 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     };
     issue_p1(gw);
 
-    const int lpr_d = P.lpr_d, rpp_d = 64 / lpr_d;
-    const int seg_d = lane & (lpr_d - 1), rloc_d = lane / lpr_d;
+    const int lpr_d = P.lpr_d, rpp_d = udiv(64, lpr_d);
+    const int seg_d = lane & (lpr_d - 1), rloc_d = udiv(lane, lpr_d);
     const int Ud = I / 32;
     const int row0 = blockIdx.x * P.rows_per_wg;
-    const int n_rg = P.rows_per_wg / rpp_d;   // row groups of this workgroup
+    const int n_rg = udiv(P.rows_per_wg, rpp_d);  // row groups of this workgroup
     const uint32_t d_row_b = (uint32_t)(I * BD / 8), d_sb_b = (uint32_t)(I / 16);  // bytes per row
     constexpr int D2 = (64 / (UD * (BD + 1))) < 1 ? 1 : ((64 / (UD * (BD + 1))) > 4 ? 4 : (64 / (UD * (BD + 1))));
     // phase-2 items of the workgroup: (row group, hit), i = rg * n_hit + hit; wave w
@@ -522,7 +529,11 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     const int n_items2 = n_all2 > wave ? (n_all2 - wave + kWaves - 1) / kWaves : 0;
     RowLoad<BD, UD> pre[D2];
     int hh2[D2], rr2[D2];
-    int h2_next = n_hit > 0 ? wave % n_hit : 0, rg2_next = n_hit > 0 ? wave / n_hit : 0;
+    int h2_next = wave, rg2_next = 0;  // (wave / n_hit, wave % n_hit) without a division
+    while (h2_next >= n_hit && n_hit > 0) {
+        h2_next -= n_hit;
+        ++rg2_next;
+    }
     auto issue_p2 = [&](RowLoad<BD, UD>* dst, int d0) {
         int h = h2_next, rg = rg2_next;
 #pragma unroll
@@ -575,7 +586,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
                 continue;
             }
             for (int pos = pb; pos < pe; ++pos) {
-                const int t = s_sorted[pos] / k;
+                const int t = T == 1 ? 0 : s_sorted[pos] / k;
                 const uint32_t* act = s_act + t * (H / 2);
                 const float* xs = s_xs1 + t * Ug;
                 uint32_t hb[2] = {0u, 0u};
@@ -620,6 +631,9 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     float* s_part = (float*)(s_dyn + P.part_dw);  // [wave][row][t]
     float* part = s_part + wave * P.rows_per_wg * T;
     for (int q = lane; q < P.rows_per_wg * T; q += 64) part[q] = 0.0f;  // this wave's rows only
+    // (I / 2 words per pair, I / 32 units: shifts when I / 2 is a power of two)
+    const bool hw_pow2 = ((I / 2) & (I / 2 - 1)) == 0;
+    const int hw_sh = __builtin_ctz(I / 2);
     auto ensure_hit = [&](int hh) {
         if (__hip_atomic_load(&s_hstate[hh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 2) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -659,7 +673,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
                 for (int r = 0; r < R; ++r) {
                     const int q = q0 + 64 * r;
                     if (q < q_end) {
-                        const int pos = q / (I / 2);
+                        const int pos = hw_pow2 ? q >> hw_sh : q / (I / 2);
                         const int rr = q - pos * (I / 2);
                         s_h2[pos * (I / 2) + swz(rr >> 4, rr & 15)] = (uint32_t)hv[r];
                     }
@@ -668,7 +682,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             for (int c = s_base[hh] * Ud + lane; c < s_base[hh + 1] * Ud; c += 64) {
-                const int pos = c / Ud, u = c - pos * Ud;
+                const int pos = hw_pow2 ? c >> (hw_sh - 4) : c / Ud, u = c - pos * Ud;
                 s_xs2[c] = unit_sum(s_h2 + pos * (I / 2), u);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -698,22 +712,28 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
             const int lrow = rg * rpp_d + rloc_d;
             const int nrow = row0 + lrow;
             if (s_slot[h] < 0) continue;
+            // the first pair's id and weight are read before waiting for h
+            const int pb = s_base[h], pend = s_base[h + 1];
+            const int pair0 = s_sorted[pb];
+            const float w0 = s_w[pair0];
             ensure_hit(h);
-            const int pend = s_base[h + 1];
-            for (int pos = s_base[h]; pos < pend; ++pos) {
-                const int pair = s_sorted[pos];
+            for (int pos = pb; pos < pend; ++pos) {
+                const int pair = pos == pb ? pair0 : s_sorted[pos];
+                const float wp = pos == pb ? w0 : s_w[pair];
                 float y = row_dot_raw<BD, UD>(cur[d], s_h2 + pos * (I / 2), s_xs2 + pos * Ud, seg_d, lpr_d);
                 y = seg_sum(y, lpr_d);
                 if (seg_d == 0 && nrow < H) {
-                    const int t = pair / k;
-                    part[lrow * T + t] += s_w[pair] * y;
+                    const int t = T == 1 ? 0 : pair / k;
+                    // this wave's own partials: LDS add without a return value, applied
+                    // in the wave's program order
+                    atomicAdd(&part[lrow * T + t], wp * y);
                 }
             }
         }
     }
     __syncthreads();
     for (int q = tid; q < P.rows_per_wg * T; q += kThreads) {
-        const int lrow = q / T, t = q - lrow * T;
+        const int lrow = T == 1 ? q : q / T, t = q - lrow * T;
         const int nrow = row0 + lrow;
         if (nrow >= H) continue;
         float acc = s_part[q];
