@@ -631,9 +631,6 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     float* s_part = (float*)(s_dyn + P.part_dw);  // [wave][row][t]
     float* part = s_part + wave * P.rows_per_wg * T;
     for (int q = lane; q < P.rows_per_wg * T; q += 64) part[q] = 0.0f;  // this wave's rows only
-    // (I / 2 words per pair, I / 32 units: shifts when I / 2 is a power of two)
-    const bool hw_pow2 = ((I / 2) & (I / 2 - 1)) == 0;
-    const int hw_sh = __builtin_ctz(I / 2);
     auto ensure_hit = [&](int hh) {
         if (__hip_atomic_load(&s_hstate[hh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 2) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -643,48 +640,45 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
         if (lane == 0) claim = atomicCAS(&s_hstate[hh], 0, 1) == 0 ? 1 : 0;
         claim = __builtin_amdgcn_readfirstlane(claim);
         if (claim) {
-            constexpr int R = 8;
-            const int q_end = s_base[hh + 1] * (I / 2);
-            for (int q0 = s_base[hh] * (I / 2) + lane; q0 < q_end; q0 += 64 * R) {
-                uint64_t hv[R];
+            // pair by pair, word rr = w0 + lane + 64 r of the pair's I / 2 (no division)
+            constexpr int R = 4;
+            const int pb = s_base[hh], pe = s_base[hh + 1];
+            for (int pos = pb; pos < pe; ++pos) {
+                for (int w0 = 0; w0 < I / 2; w0 += 64 * R) {
+                    const uint64_t* src = P.xw + (size_t)pos * (I / 2) + w0 + lane;
+                    const int nv = I / 2 - w0 - lane;  // word r of this lane exists iff 64 r < nv
+                    uint64_t hv[R];
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int q = q0 + 64 * r;
-                    hv[r] = q < q_end ? __hip_atomic_load(&P.xw[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : tag_hi;
-                }
-                unsigned spins = 0;
-                for (;;) {
-                    bool ready = true;
+                    for (int r = 0; r < R; ++r)
+                        hv[r] = 64 * r < nv ? __hip_atomic_load(src + 64 * r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                            : tag_hi;
+                    unsigned spins = 0;
+                    for (;;) {
+                        bool ready = true;
 #pragma unroll
-                    for (int r = 0; r < R; ++r) ready = ready && (uint32_t)(hv[r] >> 32) == tag;
-                    if (ready) break;
-                    if (++spins > P.spin_limit) {
-                        flag(P.err, MOE_ERRW_TIMEOUT);
-                        break;
+                        for (int r = 0; r < R; ++r) ready = ready && (uint32_t)(hv[r] >> 32) == tag;
+                        if (ready) break;
+                        if (++spins > P.spin_limit) {
+                            flag(P.err, MOE_ERRW_TIMEOUT);
+                            break;
+                        }
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            if ((uint32_t)(hv[r] >> 32) != tag)
+                                hv[r] = __hip_atomic_load(src + 64 * r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
+                    uint32_t* dst = s_h2 + pos * (I / 2);
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
-                        const int q = q0 + 64 * r;
-                        if ((uint32_t)(hv[r] >> 32) != tag)
-                            hv[r] = __hip_atomic_load(&P.xw[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int q = q0 + 64 * r;
-                    if (q < q_end) {
-                        const int pos = hw_pow2 ? q >> hw_sh : q / (I / 2);
-                        const int rr = q - pos * (I / 2);
-                        s_h2[pos * (I / 2) + swz(rr >> 4, rr & 15)] = (uint32_t)hv[r];
+                        const int rr = w0 + lane + 64 * r;
+                        if (64 * r < nv) dst[swz(rr >> 4, rr & 15)] = (uint32_t)hv[r];
                     }
                 }
             }
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            for (int c = s_base[hh] * Ud + lane; c < s_base[hh + 1] * Ud; c += 64) {
-                const int pos = hw_pow2 ? c >> (hw_sh - 4) : c / Ud, u = c - pos * Ud;
-                s_xs2[c] = unit_sum(s_h2 + pos * (I / 2), u);
-            }
+            for (int pos = pb; pos < pe; ++pos)
+                for (int u = lane; u < Ud; u += 64) s_xs2[pos * Ud + u] = unit_sum(s_h2 + pos * (I / 2), u);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             if (lane == 0) __hip_atomic_store(&s_hstate[hh], 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         } else {
