@@ -260,7 +260,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     // computed from registers before the staging barrier
     const bool fast1 = P.logits && T == 1 && P.mode == MOE_ROUTE_PLAIN && E >= 64 && k <= 15 &&
                        E <= 64 * (kWaves < 8 ? kWaves : 8);
-    float r_m = 0.0f, r_Z = 0.0f;
+    float r_m = 0.0f, r_Z = 0.0f;  // routing: max logit and Z
     {
         // all loads of this round are issued before any LDS store
         constexpr int R = 4;
@@ -295,8 +295,9 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
             tb[r] = P.table[i < E ? i : E - 1];
         }
         float own = 0.0f, zv[8];
+        const int own_e = (fast1 ? max(route_sel_list<kWaves>(wave, E), 0) : 0) * 64 + lane;  // own expert
         if (fast1) {
-            own = P.logits[tid < E ? tid : E - 1];
+            own = P.logits[own_e < E ? own_e : E - 1];
             if (wave == route_sel_wave<kWaves>(E)) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) zv[j] = P.logits[lane + 64 * j < E ? lane + 64 * j : E - 1];
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
             if (i < E) s_table[i] = tb[r];
         }
         if (fast1) {
-            if (tid < E) s_logit[tid] = own;
+            if (route_sel_list<kWaves>(wave, E) >= 0 && own_e < E) s_logit[own_e] = own;
             route_sel_lists<kWaves>(own, zv, E, &s_rsel, 0, r_m, r_Z);
         }
     }

@@ -729,24 +729,37 @@ __device__ __forceinline__ uint32_t row_merge_u32(uint32_t K, uint32_t other, in
     return row_clean_u32(K > b ? K : b, lane);
 }
 
-// The wave of route_token_sel that writes the result.
+// The wave of route_token_sel that computes m and Z and writes the result, and
+// the list (experts 64 L .. 64 L + 63) each wave sorts, -1 for none.  With a
+// spare wave the result wave is nl - 1 and list nl - 1 moves to wave nl: waves
+// go to the four SIMDs round-robin, so the result wave shares its SIMD with one
+// list wave instead of two (W = 10, nl = 8: SIMD 3 holds waves 3 and 7).
 template <int W>
 __device__ __forceinline__ int route_sel_wave(int E)
 {
-    return ((E + 63) >> 6) < W ? W - 1 : 0;
+    const int nl = (E + 63) >> 6;
+    return nl < W ? nl - 1 : 0;
+}
+template <int W>
+__device__ __forceinline__ int route_sel_list(int wave, int E)
+{
+    const int nl = (E + 63) >> 6;
+    if (nl >= W) return wave < nl ? wave : -1;
+    return wave < nl - 1 ? wave : (wave == nl ? nl - 1 : -1);
 }
 
-// Before the barrier: waves 0..nl-1 list their 16 largest keys (own = this
-// thread's logit, expert 64 * wave + lane); wave zw computes m and Z from v[j] =
-// logit of expert lane + 64j (entries past E ignored).  No barrier inside.
+// Before the barrier: the list waves list their 16 largest keys (own = this
+// thread's logit, expert 64 * route_sel_list + lane); wave zw computes m and Z
+// from v[j] = logit of expert lane + 64j (entries past E ignored).  No barrier
+// inside.
 template <int W>
 __device__ __forceinline__ void route_sel_lists(float own, const float (&v_in)[8], int E, RouteSelScratch* rs,
                                                 int par, float& m, float& Z)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nl = (E + 63) >> 6;
-    if (wave < nl) {
-        const int e = wave * 64 + lane;
+    const int li = route_sel_list<W>(wave, E);
+    if (li >= 0) {
+        const int e = li * 64 + lane;
         const bool valid = e < E;
         const float l = valid ? own : 0.0f;
         const bool bad = __any(valid && !isfinite(l));
@@ -754,8 +767,8 @@ __device__ __forceinline__ void route_sel_lists(float own, const float (&v_in)[8
         K = row_sort_u32(K, lane);
         K = row_merge_u32(K, swap16_u32(K), lane);  // rows 0 and 2: 16 largest of rows 0-1, 2-3
         K = row_merge_u32(K, swap32_u32(K), lane);  // row 0: 16 largest of the wave
-        if (lane < 16) rs->list[par][wave][lane] = K;
-        if (lane == 0) rs->bad[par][wave] = bad ? 1 : 0;
+        if (lane < 16) rs->list[par][li][lane] = K;
+        if (lane == 0) rs->bad[par][li] = bad ? 1 : 0;
     }
     m = -INFINITY;
     Z = 0.0f;
@@ -859,7 +872,8 @@ __device__ __forceinline__ bool route_token_sel(const float* __restrict__ lr, in
         const int i = lane + 64 * j;
         v[j] = lr[i < E ? i : E - 1];
     }
-    const int e = wave * 64 + lane;
+    const int li = route_sel_list<W>(wave, E);
+    const int e = (li < 0 ? 0 : li) * 64 + lane;
     const float own = lr[e < E ? e : E - 1];
     float m, Z;
     route_sel_lists<W>(own, v, E, rs, par, m, Z);
