@@ -261,6 +261,8 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     const bool fast1 = P.logits && T == 1 && P.mode == MOE_ROUTE_PLAIN && E >= 64 && k <= 15 &&
                        E <= 64 * (kWaves < 8 ? kWaves : 8);
     float r_m = 0.0f, r_Z = 0.0f;  // routing: max logit and Z
+    uint32_t r_K = 0;                // routing: the chosen keys (wave zw)
+    bool r_late = false;             // routing: weights and pair order still to come (wave zw)
     {
         // all loads of this round are issued before any LDS store
         constexpr int R = 4;
@@ -354,17 +356,22 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
             const bool by_logit = P.mode == MOE_ROUTE_PLAIN && k <= 15 && E <= 64 * (kWaves < 8 ? kWaves : 8);
             // (one token without a loop: the loop's hoisted set-up costs more than the routing)
             if (fast1) {
-                const bool ok = route_sel_finish<kWaves>(s_logit, E, k, r_m, r_Z, s_ids, s_w, &s_rsc[0], &s_rsel, 0);
+                // the chosen set now; with routing by logit order its weights and pair
+                // order come after the phase-1 loads are issued (they need the set only)
+                bool by_key;
+                const bool ok = route_sel_choose<kWaves>(s_logit, E, k, r_m, s_ids, s_w, &s_rsc[0], &s_rsel, 0, r_K,
+                                                         by_key);
                 if (!ok && wg0 && tid == 0) flag(P.err, MOE_ERRW_NONFINITE);
                 if (wave == route_sel_wave<kWaves>(E)) {
-                    // the k experts of one token are distinct: pair j goes to the rank of
-                    // its expert, which is also its hit index (one pair per hit)
-                    const int e = lane < k ? s_ids[lane] : 0x7fffffff;
+                    // the k experts of one token are distinct: hit index = rank of the
+                    // expert (one pair per hit); pair j is known now only if routed by key
+                    r_late = ok && !by_key;
+                    const int e = lane < k ? (r_late ? key32_id(r_K) : s_ids[lane]) : 0x7fffffff;
                     int rank = 0;
 #pragma unroll
                     for (int q = 0; q < 16; ++q) rank += __builtin_amdgcn_readlane(e, q) < e ? 1 : 0;
                     if (lane < k) {
-                        s_sorted[rank] = lane;
+                        if (!r_late) s_sorted[rank] = lane;
                         s_hit[rank] = e;
                         s_base[rank] = rank;
                         int32_t slot = s_table[e];
@@ -399,7 +406,7 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
             }
         }
         __syncthreads();
-        if (wg0 && P.ids_out && tid < n) {
+        if (!fast1 && wg0 && P.ids_out && tid < n) {
             P.ids_out[tid] = s_ids[tid];
             P.w_out[tid] = s_w[tid];
         }
@@ -516,6 +523,24 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
         }
     };
     issue_p1(gw);
+    if (fast1) {
+        // weights and pair order of the routed token (routing by logit order)
+        if (r_late) {
+            const int e = route_sel_weights(s_logit, k, r_m, r_Z, r_K, s_ids, s_w);  // expert of pair `lane`
+            int rank = 0;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int o = __builtin_amdgcn_readlane(e, q);
+                rank += (q < k && o < e) ? 1 : 0;
+            }
+            if (lane < k) s_sorted[rank] = lane;
+        }
+        __syncthreads();
+        if (wg0 && P.ids_out && tid < n) {
+            P.ids_out[tid] = s_ids[tid];
+            P.w_out[tid] = s_w[tid];
+        }
+    }
 
     const int lpr_d = P.lpr_d, rpp_d = udiv(64, lpr_d);
     const int seg_d = lane & (lpr_d - 1), rloc_d = udiv(lane, lpr_d);

@@ -791,17 +791,25 @@ __device__ __forceinline__ void route_sel_lists(float own, const float (&v_in)[8
     }
 }
 
-// After the barrier that follows route_sel_lists (lists and logits lr in LDS):
-// every thread returns false if a logit is not finite (wave zw then writes ids
-// 0..k-1 with weight 0), else true; wave zw writes ids and w.
+// After the barrier that follows route_sel_lists (lists and logits lr in LDS),
+// in two steps.
+//
+// route_sel_choose: every thread returns false if a logit is not finite (wave
+// zw then writes ids 0..k-1 with weight 0 to ids / w), else true.  Wave zw merges
+// the lists; if the gap test holds, K holds the 16 largest keys in lanes 0..15
+// (the chosen set: lanes 0..k-1) and *by_key = false; otherwise the token is
+// routed by key now (ids / w written) and *by_key = true.  The chosen set is
+// final after this step; only its order and weights come from route_sel_weights.
 template <int W>
-__device__ __forceinline__ bool route_sel_finish(const float* __restrict__ lr, int E, int k, float m, float Z,
-                                                 int32_t* ids, float* w, RouteScratch* sc, RouteSelScratch* rs,
-                                                 int par)
+__device__ __forceinline__ bool route_sel_choose(const float* __restrict__ lr, int E, int k, float m, int32_t* ids,
+                                                 float* w, RouteScratch* sc, RouteSelScratch* rs, int par,
+                                                 uint32_t& K, bool& by_key)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nl = (E + 63) >> 6;
     const int zw = route_sel_wave<W>(E);
+    by_key = true;
+    K = kPadKey32;
     int nb = 0;
     for (int i = 0; i < nl; ++i) nb |= rs->bad[par][i];
     if (nb) {
@@ -817,20 +825,34 @@ __device__ __forceinline__ bool route_sel_finish(const float* __restrict__ lr, i
     const int r = lane >> 4;
     const uint32_t A = r < nl ? rs->list[par][r][lane & 15] : kPadKey32;
     const uint32_t Bv = r + 4 < nl ? rs->list[par][r + 4][lane & 15] : kPadKey32;
-    uint32_t K = row_merge_u32(A, Bv, lane);
+    K = row_merge_u32(A, Bv, lane);
     K = row_merge_u32(K, swap16_u32(K), lane);
     K = row_merge_u32(K, swap32_u32(K), lane);  // row 0: the 16 largest keys, descending
 
-    const int id = 0x1ff - (int)(K & 0x1ffu);
-    const float lx = lane < k ? lr[id] : 0.0f;  // exact logit of a chosen expert
     const uint32_t c_last = (uint32_t)__builtin_amdgcn_readlane((int)K, k - 1);
     const uint32_t c_next = (uint32_t)__builtin_amdgcn_readlane((int)K, k);
     const float lo_in = order_bits_logit(c_last & ~0x1ffu);                         // every chosen logit >=
     const float hi_out = c_next == kPadKey32 ? -INFINITY : order_bits_logit(c_next | 0x1ffu);  // every other <=
-    if (!(lo_in - m >= -64.0f && lo_in - hi_out >= 0x1p-9f))
-        return route_token_512(lr, E, k, MOE_ROUTE_PLAIN, 0.0f, nullptr, lane, ids, w, sc);
+    if (!(lo_in - m >= -64.0f && lo_in - hi_out >= 0x1p-9f)) {
+        route_token_512(lr, E, k, MOE_ROUTE_PLAIN, 0.0f, nullptr, lane, ids, w, sc);
+        return true;
+    }
+    by_key = false;
+    return true;
+}
 
-    // exact p of the chosen k, ordered by (p desc, id asc)
+// The expert of a chosen key (lanes 0..k-1 of wave zw after route_sel_choose).
+__device__ __forceinline__ int key32_id(uint32_t K) { return 0x1ff - (int)(K & 0x1ffu); }
+
+// Wave zw, by_key false: exact p of the chosen k, ordered by (p desc, id asc),
+// weights p / (sum in that order, left to right); writes ids / w and returns
+// this lane's expert in that order (lanes 0..k-1).
+__device__ __forceinline__ int route_sel_weights(const float* __restrict__ lr, int k, float m, float Z, uint32_t K,
+                                                 int32_t* ids, float* w)
+{
+    const int lane = threadIdx.x & 63;
+    const int id = key32_id(K);
+    const float lx = lane < k ? lr[id] : 0.0f;  // exact logit of a chosen expert
     const float p = lane < k ? __fdiv_rn(exp_contract_nb(lx - m), Z) : 0.0f;
     uint64_t P = lane < k ? (((uint64_t)__float_as_uint(p) << 32) | (uint32_t)~id) : 0ull;
     const uint64_t next = ((uint64_t)dpp_u32<0x101>((uint32_t)(P >> 32)) << 32) | dpp_u32<0x101>((uint32_t)P);
@@ -853,11 +875,25 @@ __device__ __forceinline__ bool route_sel_finish(const float* __restrict__ lr, i
 #pragma unroll
     for (int q = 0; q < 16; ++q)  // lanes past k hold p = +0, which leaves the sum unchanged
         s = s + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ps), q));
+    const int out_id = (int)~(uint32_t)P;
     if (lane < k) {
-        ids[lane] = (int)~(uint32_t)P;
+        ids[lane] = out_id;
         w[lane] = __fdiv_rn(ps, s);
     }
-    return true;
+    return out_id;
+}
+
+// Both steps at once: returns as route_sel_choose; wave zw writes ids / w.
+template <int W>
+__device__ __forceinline__ bool route_sel_finish(const float* __restrict__ lr, int E, int k, float m, float Z,
+                                                 int32_t* ids, float* w, RouteScratch* sc, RouteSelScratch* rs,
+                                                 int par)
+{
+    uint32_t K;
+    bool by_key;
+    const bool ok = route_sel_choose<W>(lr, E, k, m, ids, w, sc, rs, par, K, by_key);
+    if (ok && (threadIdx.x >> 6) == route_sel_wave<W>(E) && !by_key) route_sel_weights(lr, k, m, Z, K, ids, w);
+    return ok;
 }
 
 // One token by logit order with all W waves (logits lr in LDS); contains one barrier.
