@@ -432,7 +432,7 @@ def bf16_lines(torch, B, synth, wl, dev, err):
         "decode_us_per_layer": round(us, 2),
         "decode_hbm_gbs": round(dec_bytes / (us * 1e-6) / 1e9, 1),
         "decode_hbm_frac": round(dec_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-        "decode_path": "router kernel + sort + GEMV gate/up + GEMV down (4 launches per layer, 48 layer-steps in one HIP graph)",
+        "decode_path": "fused decode kernel decode_layer_kernel<16,16,1,1,8>: routing, sort, gate/up + SwiGLU, down and combine in one launch per layer, 48 layer-steps in one HIP graph",
         "prefill_chunk_us": round(p_us, 2),
         "prefill_hbm_gbs": round(p_bytes / (p_us * 1e-6) / 1e9, 1),
         "prefill_hbm_frac": round(p_bytes / (p_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),

@@ -115,12 +115,18 @@ __device__ __forceinline__ void load_unit(uint32_t (&w)[B], const uint32_t* __re
         const u32x4a_t v = *(const u32x4a_t*)p;
         const u32x2a_t u = *(const u32x2a_t*)(p + 4);
         w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w; w[4] = u.x; w[5] = u.y;
-    } else {
-        static_assert(B == 8, "bits");
+    } else if constexpr (B == 8) {
         const u32x4a_t v = *(const u32x4a_t*)p;
         const u32x4a_t u = *(const u32x4a_t*)(p + 4);
         w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
         w[4] = u.x; w[5] = u.y; w[6] = u.z; w[7] = u.w;
+    } else {
+        static_assert(B == 16, "bits");
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4a_t v = *(const u32x4a_t*)(p + 4 * c);
+            w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
+        }
     }
 }
 
@@ -135,7 +141,8 @@ __device__ __forceinline__ void load_row(RowLoad<B, UPL>& r, const uint8_t* __re
     for (int j = 0; j < UPL; ++j) {
         const uint32_t u = (uint32_t)(seg + lpr * j);
         load_unit<B>(r.w[j], (const uint32_t*)(base + (codes + u * (uint32_t)(4 * B))));
-        r.sb[j] = *(const uint32_t*)(base + (sb + (u >> 1) * 4u));
+        if constexpr (Code<B>::affine) r.sb[j] = *(const uint32_t*)(base + (sb + (u >> 1) * 4u));
+        else r.sb[j] = 0u;  // width 16: bf16 weights, no scale/bias
     }
 }
 
@@ -186,12 +193,16 @@ __device__ __forceinline__ float row_dot_raw(const RowLoad<B, UPL>& r, const uin
         uint32_t av[16], cp[16];
         load_unit_act(act, u, av);
         unit_pairs<B>(r.w[j], cp);
-        const float s = half_bits_to_f32(r.sb[j] & 0xFFFFu);
-        const float z = __builtin_fmaf(-off, s, half_bits_to_f32(r.sb[j] >> 16));
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc = dot2(cp[i], av[i], acc);
-        y = __builtin_fmaf(s, acc, __builtin_fmaf(z, xs[u], y));
+        if constexpr (Code<B>::affine) {
+            const float s = half_bits_to_f32(r.sb[j] & 0xFFFFu);
+            const float z = __builtin_fmaf(-off, s, half_bits_to_f32(r.sb[j] >> 16));
+            y = __builtin_fmaf(s, acc, __builtin_fmaf(z, xs[u], y));
+        } else {
+            y += acc;  // width 16: the pairs are the weights themselves
+        }
     }
     return y;
 }
@@ -804,6 +815,7 @@ const Variant kVariants[] = {
     MOE_V(3, 3, 1, 1, 10), MOE_V(4, 4, 1, 1, 10), MOE_V(6, 6, 1, 1, 8), MOE_V(8, 8, 1, 1, 10),
     MOE_V(4, 6, 1, 1, 10), MOE_V(3, 3, 1, 3, 8), MOE_V(4, 4, 1, 3, 8), MOE_V(4, 6, 1, 3, 8),
     MOE_V(8, 8, 2, 1, 8), MOE_V(4, 4, 2, 1, 8), MOE_V(3, 3, 2, 1, 8), MOE_V(6, 6, 1, 3, 8),
+    MOE_V(16, 16, 1, 1, 8),
 };
 #undef MOE_V
 

@@ -371,8 +371,8 @@ def test_forward_prefill_chunk_full_size():
 @pytest.mark.parametrize("T", [1, 1024])
 def test_forward_bf16_experts_full_size(T):
     """Unquantized bf16 experts of the decode shape (H2048, E512, I512, top-10):
-    the GEMV path at batch 1, the MFMA path for a 1024-token chunk (sampled
-    tokens); the fused decode kernel has no bf16 variant, so AUTO takes GEMV."""
+    the fused decode kernel at batch 1 (AUTO), the three-launch GEMV and the MFMA
+    paths too; the MFMA path for a 1024-token chunk (sampled tokens)."""
     torch = _torch()
     H, E, I, k = 2048, 512, 512, 10
     lay = synth.Layout(H, I, 16, 16)
@@ -392,7 +392,7 @@ def test_forward_bf16_experts_full_size(T):
         assert ew == 0
         assert bool(torch.isfinite(out.float()).all())
         check_close(out[tokens], ref, f"bf16 experts T {T} path {path}")
-    if T == 1:  # router + experts entry point falls back to route + GEMV
+    if T == 1:  # router + experts entry point: the fused decode kernel routes too
         desc = B.moe_size_class_init(H, I, 16, 16, pool.shape[0])
         ew = err_word()
         out, _, _ = B.moe_layer_forward(to_dev(lg), dev_bf16(x), to_dev(table), pool.view(-1), desc, k,
