@@ -135,11 +135,13 @@ __device__ __forceinline__ void unit_pairs(const uint32_t (&w)[B], uint32_t (&pr
 
 // DPP lane moves within rows of 16 (gfx9 encodings): 0xB1 quad xor 1, 0x4E quad
 // xor 2, 0x141 half-row mirror (lane i <-> 7-i), 0x140 row mirror (i <-> 15-i).
+// A lane whose source lies outside its row reads 0; no caller uses such a lane's
+// result.  (No old value to keep, so the move folds into the instruction that
+// uses it: one v_add_f32_dpp instead of a copy, a move and an add.)
 template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v)
 {
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
-                                                      0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // v + (the same register of lane i ^ 16), resp. i ^ 32, via the gfx950 swaps.

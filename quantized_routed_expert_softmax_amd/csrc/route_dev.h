@@ -171,7 +171,7 @@ __device__ __forceinline__ float wave_kth_largest(float v, int k, int lane)
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v)
 {
-    return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v)
