@@ -39,6 +39,7 @@ namespace moe {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 // Calls f(std::integral_constant<int, i>) for i = 0..N-1 (indices known at compile time).
 template <class F, int... Is>
@@ -115,10 +116,14 @@ constexpr int kGPC = kKC / 64;    // groups per stage
 constexpr int kAROW = kKC + 8;    // bf16 per staged activation row (padding: conflict-free reads)
 
 // Dwords of padding after each staged code row.  The 16 lanes of a lane group
-// read the same column of 16 consecutive rows; a row stride of 4 (mod 32) dwords
-// puts those rows on different banks.  Width 3 (stride 12) already spreads them.
+// read one column of 16 consecutive rows, and the lane group that shares their
+// LDS cycle reads the same column or a neighbouring one (width 16: 64-bit reads,
+// columns two apart).  A row stride of 2 (mod 4) dwords puts the 16 rows on
+// distinct even banks (mod 32) and a column one dword over on the odd ones, so
+// no read conflicts; the unpadded widths put rows r and r + 8 (or more) on one
+// bank.  Rows stay 8-byte aligned.
 template <int B>
-constexpr int code_pad() { return B == 3 ? 0 : 4; }
+constexpr int code_pad() { return 2; }
 
 // One pipeline stage in LDS: raw codes and scale/bias of the workgroup's NB*64
 // weight rows for kKC inputs, and kKC activations of up to MT*16 rows.
@@ -157,8 +162,10 @@ __device__ __forceinline__ u32x4_t lds_pairs(const uint32_t* __restrict__ unit, 
 //               -> h (bf16, P16) at the pair's sorted position.
 //   GU = false: down.  Weight rows n0..n0+63 of the down matrix; A = h rows;
 //               epilogue y (bf16) at [pair id][n].
+// Narrow codes with 32-row sweeps fit 168 VGPRs: three waves per SIMD.
 template <int B, bool GU, int MT, int CBW>
-__global__ __launch_bounds__(256) void mfma_grouped_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B <= 4 && MT == 2 ? 3 : 1)))
+void mfma_grouped_kernel(
     const uint16_t* __restrict__ act, int H, int I, int k, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table,
     const int32_t* __restrict__ table, const uint8_t* __restrict__ pool, int64_t n_slots,
@@ -265,7 +272,8 @@ __global__ __launch_bounds__(256) void mfma_grouped_kernel(
             const int q = tid + 256 * i;                                                        \
             if (q < BPIECES) {                                                                  \
                 const int r = q / B, p = q - r * B;                                             \
-                *(u32x4_t*)(&S_.codes[r][p * 4]) = RB[i];                                       \
+                *(u32x2_t*)(&S_.codes[r][p * 4]) = u32x2_t{RB[i].x, RB[i].y};                   \
+                *(u32x2_t*)(&S_.codes[r][p * 4 + 2]) = u32x2_t{RB[i].z, RB[i].w};               \
             }                                                                                   \
         });                                                                                     \
         if (Code<B>::affine && tid < SBN) S_.sb[tid / kGPC][tid % kGPC] = RS;                   \
@@ -281,41 +289,7 @@ __global__ __launch_bounds__(256) void mfma_grouped_kernel(
         const int cbl = (C) / n_kc;                                                             \
         const int kin = ((C) - cbl * n_kc) * kKC;                                               \
         const int groups = (kin + kKC <= K) ? kGPC : (K - kin) / 64;                            \
-        for (int G2 = 0; G2 < groups; ++G2) {                                                   \
-            u32x4_t bw[NB][2];                                                                  \
-            float sc[NB], zc[NB];                                                               \
-            _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                                 \
-                const int r = nb * 64 + wave * 16 + c16;                                        \
-                bw[nb][0] = lds_pairs<B>(&S.codes[r][(2 * G2) * B], g);                         \
-                bw[nb][1] = lds_pairs<B>(&S.codes[r][(2 * G2 + 1) * B], g);                     \
-                if constexpr (Code<B>::affine) {                                                \
-                    const uint32_t s2 = S.sb[r][G2];                                            \
-                    sc[nb] = half_bits_to_f32(s2 & 0xFFFFu);                                    \
-                    zc[nb] = __builtin_fmaf(-off, sc[nb], half_bits_to_f32(s2 >> 16));          \
-                }                                                                               \
-            }                                                                                   \
-            _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                                 \
-                if (mt < nmt) {                                                                 \
-                    const u32x4_t a0 = *(const u32x4_t*)(&S.a[mt * 16 + c16][(2 * G2) * 32 + 8 * g]); \
-                    const u32x4_t a1 = *(const u32x4_t*)(&S.a[mt * 16 + c16][(2 * G2 + 1) * 32 + 8 * g]); \
-                    if constexpr (Code<B>::affine) {                                            \
-                        f32x4_t tx = mfma(a0, ones, zero);                                      \
-                        tx = mfma(a1, ones, tx);                                                \
-                        _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                     \
-                            f32x4_t t = mfma(a0, bw[nb][0], zero);                              \
-                            t = mfma(a1, bw[nb][1], t);                                         \
-                            _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_)                    \
-                                acc[nb][mt][q_] = __builtin_fmaf(sc[nb], t[q_], __builtin_fmaf(zc[nb], tx[q_], acc[nb][mt][q_])); \
-                        }                                                                       \
-                    } else { /* bf16 weights: the matrix cores accumulate in place */            \
-                        _Pragma("unroll") for (int nb = 0; nb < NB; ++nb) {                     \
-                            acc[nb][mt] = mfma(a0, bw[nb][0], acc[nb][mt]);                     \
-                            acc[nb][mt] = mfma(a1, bw[nb][1], acc[nb][mt]);                     \
-                        }                                                                       \
-                    }                                                                           \
-                }                                                                               \
-            }                                                                                   \
-        }                                                                                       \
+        for (int G2 = 0; G2 < groups; ++G2) compute_group(S, G2);                               \
         if (kin + kKC >= K) {                                                                   \
             epilogue((cb0 + cbl) * 64 + wave * 16 + c16);                                       \
             _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                   \
@@ -349,6 +323,48 @@ __global__ __launch_bounds__(256) void mfma_grouped_kernel(
             }
         };
 
+        // one group of 64 inputs of the stage in LDS: B operands, then the matrix cores
+        auto compute_group = [&](const Stage<B, NB, MT>& S, int G2) __attribute__((always_inline)) {
+            u32x4_t bw[NB][2];
+            float sc[NB], zc[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int r = nb * 64 + wave * 16 + c16;
+                bw[nb][0] = lds_pairs<B>(&S.codes[r][(2 * G2) * B], g);
+                bw[nb][1] = lds_pairs<B>(&S.codes[r][(2 * G2 + 1) * B], g);
+                if constexpr (Code<B>::affine) {
+                    const uint32_t s2 = S.sb[r][G2];
+                    sc[nb] = half_bits_to_f32(s2 & 0xFFFFu);
+                    zc[nb] = __builtin_fmaf(-off, sc[nb], half_bits_to_f32(s2 >> 16));
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                if (mt < nmt) {
+                    const u32x4_t a0 = *(const u32x4_t*)(&S.a[mt * 16 + c16][(2 * G2) * 32 + 8 * g]);
+                    const u32x4_t a1 = *(const u32x4_t*)(&S.a[mt * 16 + c16][(2 * G2 + 1) * 32 + 8 * g]);
+                    if constexpr (Code<B>::affine) {
+                        f32x4_t tx = mfma(a0, ones, zero);
+                        tx = mfma(a1, ones, tx);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) {
+                            f32x4_t t = mfma(a0, bw[nb][0], zero);
+                            t = mfma(a1, bw[nb][1], t);
+#pragma unroll
+                            for (int q_ = 0; q_ < 4; ++q_)
+                                acc[nb][mt][q_] = __builtin_fmaf(sc[nb], t[q_], __builtin_fmaf(zc[nb], tx[q_], acc[nb][mt][q_]));
+                        }
+                    } else {  // bf16 weights: the matrix cores accumulate in place
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) {
+                            acc[nb][mt] = mfma(a0, bw[nb][0], acc[nb][mt]);
+                            acc[nb][mt] = mfma(a1, bw[nb][1], acc[nb][mt]);
+                        }
+                    }
+                }
+            }
+        };
+
         // prologue: stages 0 and 1 in flight, stage 0 into LDS
         MOE_LOAD_STAGE(0, rb0, rs0, ra0)
         if (n_stages > 1) MOE_LOAD_STAGE(1, rb1, rs1, ra1)
@@ -373,6 +389,221 @@ __global__ __launch_bounds__(256) void mfma_grouped_kernel(
 
     }
 #undef wrow
+}
+
+// Width 3: the same grouped GEMM with the stages moved from global memory
+// straight into LDS (global_load_lds_dwordx4 / _dword: lane i of a load writes
+// 16 or 4 bytes at the wave's LDS base + 16 i or 4 i).  No staging registers
+// and no VALU copies into LDS: gate/up spends the registers saved on both
+// groups of a stage in flight at once, down runs five waves per SIMD.  Two LDS
+// buffers: stage c + 1 lands while stage c is consumed.  Layouts in a buffer:
+//   codes  row r at dwords [12 r, 12 r + 12): the row's 3 pieces of 16 bytes
+//   sb     row r at dwords 2 r, 2 r + 1
+//   a      row m at dwords [64 m, 64 m + 64); its 16-byte chunk c sits in slot
+//          c ^ (m & 15), so the 16 rows read by one lane group spread over the banks
+template <int NB, int MT>
+struct DmaStage {
+    uint32_t codes[NB * 64 * 12];
+    uint32_t sb[NB * 64 * kGPC];
+    uint32_t a[MT * 16 * (kKC / 2)];
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base)
+{
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds_wave_base)
+{
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 4, 0, 0);
+}
+
+template <bool GU, int MT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 2 ? (GU ? 3 : 5) : 1)))
+void mfma_dma3_kernel(
+    const uint16_t* __restrict__ act, int H, int I, int k, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table,
+    const int32_t* __restrict__ table, const uint8_t* __restrict__ pool, int64_t n_slots,
+    int64_t slot_bytes, int64_t off_codes, int64_t off_sb, uint16_t* __restrict__ hbuf,
+    uint16_t* __restrict__ ybuf, uint32_t* __restrict__ err)
+{
+    constexpr int B = 3;
+    constexpr int NB = GU ? 2 : 1;
+    constexpr int ROWS = NB * 64;
+    __shared__ DmaStage<NB, MT> st[2];
+    // tile order as in mfma_grouped_kernel (one column block per workgroup)
+    const int ncb = (GU ? I : H) / 64;
+    const int L = blockIdx.x, r8 = L >> 3;
+    const int cb0 = r8 % ncb;
+    const int hit = (r8 / ncb) * 8 + (L & 7);
+    if (hit >= pass_table[0]) return;
+    const int e = pass_table[2 + hit];
+    const int32_t slot = table[e];
+    if (slot < 0 || slot >= n_slots) {
+        if (threadIdx.x == 0 && err) atomicOr(err, slot < 0 ? MOE_ERRW_NOT_RESIDENT : MOE_ERRW_BAD_SLOT);
+        return;
+    }
+    const int base = offsets[e], cnt = offsets[e + 1] - base;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int K = GU ? H : I;
+    const int NC = K / kKC;
+    const bool tail = (K % kKC) != 0;
+    const int n_stages = NC + (tail ? 1 : 0);
+    const int n0 = cb0 * 64;
+
+    const uint8_t* rowb = pool + (size_t)slot * (size_t)slot_bytes;
+    const size_t row_dw = (size_t)K * B / 32;
+    const uint32_t* codes = (const uint32_t*)(rowb + off_codes);
+    const uint32_t* sbg = (const uint32_t*)(rowb + off_sb);
+    constexpr float off = Code<B>::offset;
+    const u32x4_t ones = {MOE_ONES_PAIR, MOE_ONES_PAIR, MOE_ONES_PAIR, MOE_ONES_PAIR};
+    const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+    auto wrow = [&](int r) { return GU ? (r < 64 ? n0 + r : I + n0 + (r - 64)) : n0 + r; };
+
+    // loads of one stage: code pieces q = 256 i + tid (row q / 3, piece q % 3),
+    // sb dwords q = tid (row q / 2, group q % 2), activation pieces q = 256 i + tid
+    constexpr int BPIECES = ROWS * B;                    // 16-byte code pieces per stage
+    constexpr int BPT = (BPIECES + 255) / 256;
+    constexpr int SBN = ROWS * kGPC;                     // sb dwords per stage
+    constexpr int APT = MT * 16 * (kKC / 8) / 256;      // 16-byte activation pieces per thread
+    static_assert(BPIECES % 64 == 0 && SBN % 64 == 0, "whole waves per load");
+    const uint32_t* bsrc[BPT];
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        const int q = min(256 * i + tid, BPIECES - 1);
+        const int r = q / B;
+        bsrc[i] = codes + (size_t)wrow(r) * row_dw + (q - r * B) * 4;
+    }
+    const uint32_t* ssrc = sbg + (size_t)wrow(min(tid, SBN - 1) >> 1) * (K / 64) + (tid & 1);
+    const uint16_t* arow_[APT];  // activation row of each A piece, set per sweep
+    // stage kin: piece p of a code row is clamped to 0 past the tail's units (the
+    // copy lands in LDS but is never read), likewise the sb group and A chunk
+    auto issue = [&](int c, int buf) {
+        const int kin = c * kKC;
+        const int units = (kin + kKC <= K) ? kUPC : (K - kin) / 32;
+        DmaStage<NB, MT>& S = st[buf];
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            if (256 * i + wave * 64 < BPIECES) {  // wave-uniform
+                const int q = 256 * i + tid;
+                const int p = q % B;
+                const uint32_t* src = bsrc[i] + (size_t)(kin / 32) * B;
+                dma16(p * 4 < units * B ? src : src - p * 4, &S.codes[(256 * i + wave * 64) * 4]);
+            }
+        }
+        if (wave * 64 < SBN) {
+            const int gg = tid & 1;
+            dma4(ssrc + kin / 64 - (gg * 64 < units * 32 ? 0 : gg), &S.sb[wave * 64]);
+        }
+#pragma unroll
+        for (int i = 0; i < APT; ++i) {
+            const int q = 256 * i + tid;
+            const int m = q >> 4;
+            int ch = (q & 15) ^ (m & 15);       // global chunk held by this slot
+            ch = ch * 8 < units * 32 ? ch : 0;
+            dma16(arow_[i] + kin + ch * 8, &S.a[(256 * i + wave * 64) * 4]);
+        }
+    };
+
+    for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
+        const int rows = min(16 * MT, cnt - m0);
+        const int nmt = (rows + 15) >> 4;
+        // rows past the expert's last pair re-read its last row (results discarded)
+#pragma unroll
+        for (int i = 0; i < APT; ++i) {
+            const int m = min((256 * i + tid) >> 4, rows - 1);
+            if (GU) arow_[i] = act + (size_t)(sorted_pairs[base + m0 + m] / k) * H;
+            else arow_[i] = act + (size_t)(base + m0 + m) * I;
+        }
+        f32x4_t acc[NB][MT];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = zero;
+
+        // one group of 64 inputs of the stage in LDS: B operands, then the matrix cores
+        auto compute_group = [&](const DmaStage<NB, MT>& S, int G2) __attribute__((always_inline)) {
+            u32x4_t bw[NB][2];
+            float sc[NB], zc[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int r = nb * 64 + wave * 16 + c16;
+                bw[nb][0] = lds_pairs<B>(&S.codes[r * 12 + (2 * G2) * B], g);
+                bw[nb][1] = lds_pairs<B>(&S.codes[r * 12 + (2 * G2 + 1) * B], g);
+                const uint32_t s2 = S.sb[r * 2 + G2];
+                sc[nb] = half_bits_to_f32(s2 & 0xFFFFu);
+                zc[nb] = __builtin_fmaf(-off, sc[nb], half_bits_to_f32(s2 >> 16));
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                if (mt < nmt) {
+                    const int m = mt * 16 + c16;  // m & 15 == c16
+                    const u32x4_t a0 = *(const u32x4_t*)(&S.a[m * 64 + (((8 * G2 + g) ^ c16) * 4)]);
+                    const u32x4_t a1 = *(const u32x4_t*)(&S.a[m * 64 + (((8 * G2 + 4 + g) ^ c16) * 4)]);
+                    f32x4_t tx = mfma(a0, ones, zero);
+                    tx = mfma(a1, ones, tx);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        f32x4_t t = mfma(a0, bw[nb][0], zero);
+                        t = mfma(a1, bw[nb][1], t);
+#pragma unroll
+                        for (int q_ = 0; q_ < 4; ++q_)
+                            acc[nb][mt][q_] = __builtin_fmaf(sc[nb], t[q_], __builtin_fmaf(zc[nb], tx[q_], acc[nb][mt][q_]));
+                    }
+                }
+            }
+        };
+        auto compute_stage = [&](const DmaStage<NB, MT>& S, int c) __attribute__((always_inline)) {
+            const int kin = c * kKC;
+            const int groups = (kin + kKC <= K) ? kGPC : (K - kin) / 64;
+            if (GU && groups == kGPC) {  // gate/up: both groups in one block for the scheduler
+#pragma unroll
+                for (int G2 = 0; G2 < kGPC; ++G2) compute_group(S, G2);
+            } else {
+                for (int G2 = 0; G2 < groups; ++G2) compute_group(S, G2);
+            }
+        };
+
+        // stage c + 1 lands in the other buffer while stage c is consumed; each
+        // wave waits for its own loads, the barrier for everyone's (and for the
+        // reads of the buffer the next loads overwrite)
+        issue(0, 0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        lds_barrier();
+        for (int c = 0; c < n_stages; c += 2) {
+            if (c + 1 < n_stages) issue(c + 1, 1);
+            compute_stage(st[0], c);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            lds_barrier();
+            if (c + 1 >= n_stages) break;
+            if (c + 2 < n_stages) issue(c + 2, 0);
+            compute_stage(st[1], c + 1);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            lds_barrier();
+        }
+
+        // results of this lane's column n for the sweep's rows
+        const int n = n0 + wave * 16 + c16;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if (mt < nmt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = m0 + mt * 16 + 4 * g + i;
+                    if (r < cnt) {
+                        if constexpr (GU) {
+                            const int pos = (n & ~31) | p16_pos(n & 31);
+                            hbuf[(size_t)(base + r) * I + pos] = f32_to_bf16(silu_mul(acc[0][mt][i], acc[1][mt][i]));
+                        } else {
+                            ybuf[(size_t)sorted_pairs[base + r] * H + n] = f32_to_bf16(acc[0][mt][i]);
+                        }
+                    }
+                }
+            }
+        }
+    }
 }
 
 // x [T, H] bf16 -> P16 layout: within each 32-chunk, position 2i+h holds input i+16h.
@@ -446,8 +677,13 @@ hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const Sor
                        sv.offsets, sv.sorted_pairs, sv.pass_table, table, pool, c.n_slots,         \
                        c.slot_bytes, c.off_gu_codes, c.off_gu_sb, hbuf, nullptr, err)
 #define MOE_MG2(BB) { if (mt == 4) MOE_MG(BB, 4); else MOE_MG(BB, 2); }
+#define MOE_MG3(MM)                                                                                \
+    hipLaunchKernelGGL((mfma_dma3_kernel<true, MM>), dim3((unsigned)((c.I / 64) * ((max_hit + 7) / 8) * 8)), \
+                       dim3(256), 0, s, xp, c.H, c.I, k, sv.offsets, sv.sorted_pairs, sv.pass_table, \
+                       table, pool, c.n_slots, c.slot_bytes, c.off_gu_codes, c.off_gu_sb, hbuf,    \
+                       nullptr, err)
     switch (c.bits_gu) {
-    case 3: MOE_MG2(3); break;
+    case 3: if (mt == 4) MOE_MG3(4); else MOE_MG3(2); break;
     case 4: MOE_MG2(4); break;
     case 6: MOE_MG2(6); break;
     case 8: MOE_MG2(8); break;
@@ -456,6 +692,7 @@ hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const Sor
     }
 #undef MOE_MG
 #undef MOE_MG2
+#undef MOE_MG3
     return hipGetLastError();
 }
 
@@ -472,8 +709,13 @@ hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, const int32
                        k, sv.offsets, sv.sorted_pairs, sv.pass_table, table, pool, c.n_slots,      \
                        c.slot_bytes, c.off_d_codes, c.off_d_sb, nullptr, ybuf, err)
 #define MOE_MD2(BB) { if (mt == 4) MOE_MD(BB, 4); else MOE_MD(BB, 2); }
+#define MOE_MD3(MM)                                                                                \
+    hipLaunchKernelGGL((mfma_dma3_kernel<false, MM>), dim3((unsigned)((c.H / 64) * ((max_hit + 7) / 8) * 8)), \
+                       dim3(256), 0, s, hbuf, c.H, c.I, k, sv.offsets, sv.sorted_pairs, sv.pass_table, \
+                       table, pool, c.n_slots, c.slot_bytes, c.off_d_codes, c.off_d_sb, nullptr,  \
+                       ybuf, err)
     switch (c.bits_d) {
-    case 3: MOE_MD2(3); break;
+    case 3: if (mt == 4) MOE_MD3(4); else MOE_MD3(2); break;
     case 4: MOE_MD2(4); break;
     case 6: MOE_MD2(6); break;
     case 8: MOE_MD2(8); break;
@@ -482,6 +724,7 @@ hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, const int32
     }
 #undef MOE_MD
 #undef MOE_MD2
+#undef MOE_MD3
     return hipGetLastError();
 }
 

@@ -218,16 +218,35 @@ def test_forward_small(shape, path):
     check_close(out, ref, f"{shape} path {path}")
 
 
-def test_forward_many_rows_per_expert_mfma():
-    """One expert takes 150 rows: several K sweeps of 4 M-tiles plus a ragged tile."""
+@pytest.mark.parametrize("bits", [4, 3])
+def test_forward_many_rows_per_expert_mfma(bits):
+    """One expert takes 150 rows: several K sweeps of 4 M-tiles plus a ragged tile
+    (width 3 runs the kernel that loads its stages straight into LDS)."""
     T, H, E, I, k = 150, 128, 4, 64, 2
-    pr = synth.make_problem(301, T, H, E, I, k, 4, 4)
+    pr = synth.make_problem(301, T, H, E, I, k, bits, bits)
     ids = np.stack([np.array([1, (t % 3) + (t % 3 >= 1)], dtype=np.int32) for t in range(T)])
     w = np.full((T, k), 0.5, dtype=np.float32)
     out, ew = run_forward(pr, ids, w, B.MOE_PATH_MFMA)
     assert ew == 0
-    ref = oracle.layer(pr.x, ids, w, pr.table, pr.pool, H, I, 4, 4, E, threads=THREADS)
-    check_close(out, ref, "skewed")
+    ref = oracle.layer(pr.x, ids, w, pr.table, pr.pool, H, I, bits, bits, E, threads=THREADS)
+    check_close(out, ref, f"skewed {bits}-bit")
+
+
+@pytest.mark.parametrize("shape", [
+    # (T, H, E, I, k): K = 320 and 448 end in a half stage of 64 inputs after an
+    # odd / even number of full stages; the two LDS buffers alternate through it
+    (9, 320, 6, 448, 2),
+    (5, 192, 4, 320, 3),
+    (40, 448, 3, 64, 2),
+])
+def test_forward_mfma_width3_k_tails(shape):
+    T, H, E, I, k = shape
+    pr = synth.make_problem(900 + T + H, T, H, E, I, k, 3, 3, n_slots=E + 1)
+    ids, w = oracle.route(pr.logits, k)
+    out, ew = run_forward(pr, ids, w, B.MOE_PATH_MFMA)
+    assert ew == 0
+    ref = oracle.layer(pr.x, ids, w, pr.table, pr.pool, H, I, 3, 3, E, threads=THREADS)
+    check_close(out, ref, f"{shape} width 3")
 
 
 @pytest.mark.parametrize("path", [B.MOE_PATH_GEMV, B.MOE_PATH_GEMV3, B.MOE_PATH_MFMA])
