@@ -113,7 +113,12 @@ __device__ __forceinline__ u32x4_t lane_pairs(const uint32_t* __restrict__ unit,
 constexpr int kKC = 128;          // K per pipeline stage
 constexpr int kUPC = kKC / 32;    // pack units per stage
 constexpr int kGPC = kKC / 64;    // groups per stage
-constexpr int kAROW = kKC + 8;    // bf16 per staged activation row (padding: conflict-free reads)
+
+// K per pipeline stage of the register-staged kernel: 128 inputs, 64 for width 16
+// (its code rows are four times wider: 128 inputs would take 87 KB of LDS per
+// gate/up workgroup, one workgroup per CU).
+template <int B>
+constexpr int stage_k() { return B == 16 ? 64 : kKC; }
 
 // Dwords of padding after each staged code row.  The 16 lanes of a lane group
 // read one column of 16 consecutive rows, and the lane group that shares their
@@ -126,12 +131,13 @@ template <int B>
 constexpr int code_pad() { return 2; }
 
 // One pipeline stage in LDS: raw codes and scale/bias of the workgroup's NB*64
-// weight rows for kKC inputs, and kKC activations of up to MT*16 rows.
+// weight rows for stage_k<B>() inputs, and as many activations of up to MT*16
+// rows (rows padded by 8 bf16: conflict-free reads).
 template <int B, int NB, int MT>
 struct Stage {
-    uint32_t codes[NB * 64][kUPC * B + code_pad<B>()];
-    uint32_t sb[NB * 64][kGPC];
-    uint16_t a[MT * 16][kAROW];
+    uint32_t codes[NB * 64][stage_k<B>() / 32 * B + code_pad<B>()];
+    uint32_t sb[NB * 64][stage_k<B>() / 64];
+    uint16_t a[MT * 16][stage_k<B>() + 8];
 };
 
 // Workgroup barrier that orders LDS only: global loads in flight stay in flight.
@@ -155,16 +161,17 @@ __device__ __forceinline__ u32x4_t lds_pairs(const uint32_t* __restrict__ unit, 
 }
 
 // Grouped dequantizing GEMM for one hit expert and 64 output columns per
-// workgroup (16 per wave), pipelined through registers and LDS in stages of kKC
+// workgroup (16 per wave), pipelined through registers and LDS in stages of KC
 // inputs (see the top of this file).
 //   GU = true : gate/up.  Weight rows: gate n0..n0+63 and up I+n0..; A = P16 x
 //               rows of the expert's pairs (via sorted_pairs); epilogue SwiGLU
 //               -> h (bf16, P16) at the pair's sorted position.
 //   GU = false: down.  Weight rows n0..n0+63 of the down matrix; A = h rows;
 //               epilogue y (bf16) at [pair id][n].
-// Narrow codes with 32-row sweeps fit 168 VGPRs: three waves per SIMD.
+// 32-row sweeps of narrow codes (and of width 16, with its 64-input stages) fit
+// 168 VGPRs: three waves per SIMD.
 template <int B, bool GU, int MT, int CBW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B <= 4 && MT == 2 ? 3 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((B <= 4 || B == 16) && MT == 2 ? 3 : 1)))
 void mfma_grouped_kernel(
     const uint16_t* __restrict__ act, int H, int I, int k, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table,
@@ -173,6 +180,7 @@ void mfma_grouped_kernel(
     uint16_t* __restrict__ ybuf, uint32_t* __restrict__ err)
 {
     constexpr int NB = GU ? 2 : 1;
+    constexpr int KC = stage_k<B>(), UPC = KC / 32, GPC = KC / 64;
     __shared__ Stage<B, NB, MT> st[2];
     // XCD-aware tile order: workgroup L runs on XCD L % 8, so the workgroups of
     // one expert are given the same L % 8 -- they share one L2 and fetch the
@@ -195,8 +203,8 @@ void mfma_grouped_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const int K = GU ? H : I;            // reduction length
-    const int NC = K / kKC;              // full K stages per column block
-    const bool tail = (K % kKC) != 0;    // a last half stage of 64 inputs
+    const int NC = K / KC;              // full K stages per column block
+    const bool tail = (K % KC) != 0;    // a last half stage of 64 inputs
     const int n_kc = NC + (tail ? 1 : 0);
     const int n_stages = ncb_wg * n_kc;  // stage s: column block cb0 + s / n_kc, K chunk s % n_kc
 
@@ -212,10 +220,11 @@ void mfma_grouped_kernel(
 #define wrow(R) (GU ? ((R) < 64 ? n0_ + (R) : I + n0_ + ((R) - 64)) : n0_ + (R))
 
     // staging assignment: B pieces (16 B), sb dwords, A pieces (16 B)
-    constexpr int BPIECES = NB * 64 * B;                 // per stage (B pieces of 16 B per row)
+    constexpr int PPR = KC * B / 128;                    // 16-byte pieces per row per stage
+    constexpr int BPIECES = NB * 64 * PPR;               // per stage
     constexpr int BPT = (BPIECES + 255) / 256;
-    constexpr int SBN = NB * 64 * kGPC;                  // sb dwords per stage
-    constexpr int APT = MT * 16 * (kKC / 8) / 256;       // A pieces per thread
+    constexpr int SBN = NB * 64 * GPC;                  // sb dwords per stage
+    constexpr int APT = MT * 16 * (KC / 8) / 256;       // A pieces per thread
 
     for (int m0 = 0; m0 < cnt; m0 += 16 * MT) {
         const int rows = min(16 * MT, cnt - m0);
@@ -226,7 +235,7 @@ void mfma_grouped_kernel(
 #pragma unroll
         for (int i = 0; i < APT; ++i) {
             const int q = tid + 256 * i;
-            int m = q / (kKC / 8);
+            int m = q / (KC / 8);
             m = m < rows ? m : rows - 1;
             if (GU) arow[i] = act + (size_t)(sorted_pairs[base + m0 + m] / k) * H;
             else arow[i] = act + (size_t)(base + m0 + m) * I;
@@ -239,27 +248,27 @@ void mfma_grouped_kernel(
     {                                                                                           \
         const int cbl_ = (C) / n_kc;                                                            \
         const int n0_ = (cb0 + cbl_) * 64;                                                      \
-        const int kin_ = ((C) - cbl_ * n_kc) * kKC;                                             \
-        const int units_ = (kin_ + kKC <= K) ? kUPC : (K - kin_) / 32;                          \
+        const int kin_ = ((C) - cbl_ * n_kc) * KC;                                             \
+        const int units_ = (kin_ + KC <= K) ? UPC : (K - kin_) / 32;                          \
         static_for<BPT>([&](auto I_) {                                                          \
             constexpr int i = decltype(I_)::value;                                              \
             int q = tid + 256 * i;                                                              \
             q = q < BPIECES ? q : BPIECES - 1;                                                  \
-            const int r = q / B;                                                                \
-            int p = q - r * B;                                                                  \
+            const int r = q / PPR;                                                              \
+            int p = q - r * PPR;                                                                \
             p = p * 4 < units_ * B ? p : 0;                                                     \
             RB[i] = *(const u32x4_t*)(codes + (size_t)wrow(r) * row_dw + (size_t)(kin_ / 32) * B + p * 4); \
         });                                                                                     \
         if constexpr (Code<B>::affine) {                                                        \
             const int qs = tid < SBN ? tid : SBN - 1;                                           \
-            const int r = qs / kGPC;                                                            \
-            int gg = qs - r * kGPC;                                                             \
+            const int r = qs / GPC;                                                            \
+            int gg = qs - r * GPC;                                                             \
             gg = gg * 64 < units_ * 32 ? gg : 0;                                                \
             RS = sbg[(size_t)wrow(r) * (K / 64) + kin_ / 64 + gg];                              \
         }                                                                                       \
         static_for<APT>([&](auto I_) {                                                          \
             constexpr int i = decltype(I_)::value;                                              \
-            int p = (tid + 256 * i) % (kKC / 8);                                                \
+            int p = (tid + 256 * i) % (KC / 8);                                                \
             p = p * 8 < units_ * 32 ? p : 0;                                                    \
             RA[i] = *(const u32x4_t*)(arow[i] + kin_ + p * 8);                                  \
         });                                                                                     \
@@ -271,26 +280,26 @@ void mfma_grouped_kernel(
             constexpr int i = decltype(I_)::value;                                              \
             const int q = tid + 256 * i;                                                        \
             if (q < BPIECES) {                                                                  \
-                const int r = q / B, p = q - r * B;                                             \
+                const int r = q / PPR, p = q - r * PPR;                                         \
                 *(u32x2_t*)(&S_.codes[r][p * 4]) = u32x2_t{RB[i].x, RB[i].y};                   \
                 *(u32x2_t*)(&S_.codes[r][p * 4 + 2]) = u32x2_t{RB[i].z, RB[i].w};               \
             }                                                                                   \
         });                                                                                     \
-        if (Code<B>::affine && tid < SBN) S_.sb[tid / kGPC][tid % kGPC] = RS;                   \
+        if (Code<B>::affine && tid < SBN) S_.sb[tid / GPC][tid % GPC] = RS;                   \
         static_for<APT>([&](auto I_) {                                                          \
             constexpr int i = decltype(I_)::value;                                              \
             const int q = tid + 256 * i;                                                        \
-            *(u32x4_t*)(&S_.a[q / (kKC / 8)][(q % (kKC / 8)) * 8]) = RA[i];                    \
+            *(u32x4_t*)(&S_.a[q / (KC / 8)][(q % (KC / 8)) * 8]) = RA[i];                    \
         });                                                                                     \
     }
 #define MOE_COMPUTE_STAGE(BUF, C)                                                               \
     {                                                                                           \
         const Stage<B, NB, MT>& S = st[(BUF)];                                                  \
         const int cbl = (C) / n_kc;                                                             \
-        const int kin = ((C) - cbl * n_kc) * kKC;                                               \
-        const int groups = (kin + kKC <= K) ? kGPC : (K - kin) / 64;                            \
+        const int kin = ((C) - cbl * n_kc) * KC;                                               \
+        const int groups = (kin + KC <= K) ? GPC : (K - kin) / 64;                            \
         for (int G2 = 0; G2 < groups; ++G2) compute_group(S, G2);                               \
-        if (kin + kKC >= K) {                                                                   \
+        if (kin + KC >= K) {                                                                   \
             epilogue((cb0 + cbl) * 64 + wave * 16 + c16);                                       \
             _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                   \
                 _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = zero;           \
