@@ -404,7 +404,9 @@ void mfma_grouped_kernel(
 // straight into LDS (global_load_lds_dwordx4 / _dword: lane i of a load writes
 // 16 or 4 bytes at the wave's LDS base + 16 i or 4 i).  No staging registers
 // and no VALU copies into LDS: gate/up spends the registers saved on both
-// groups of a stage in flight at once, down runs five waves per SIMD.  Two LDS
+// groups of a stage in flight at once.  Down takes two blocks of 64 columns per
+// workgroup (128 weight rows, like gate and up), so each wave carries two
+// independent chains and one staging of the h rows serves both.  Two LDS
 // buffers: stage c + 1 lands while stage c is consumed.  Layouts in a buffer:
 //   codes  row r at dwords [12 r, 12 r + 12): the row's 3 pieces of 16 bytes
 //   sb     row r at dwords 2 r, 2 r + 1
@@ -429,7 +431,7 @@ __device__ __forceinline__ void dma4(const void* g, void* lds_wave_base)
 }
 
 template <bool GU, int MT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 2 ? (GU ? 3 : 5) : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 2 ? (GU ? 3 : 4) : 1)))
 void mfma_dma3_kernel(
     const uint16_t* __restrict__ act, int H, int I, int k, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table,
@@ -438,11 +440,11 @@ void mfma_dma3_kernel(
     uint16_t* __restrict__ ybuf, uint32_t* __restrict__ err)
 {
     constexpr int B = 3;
-    constexpr int NB = GU ? 2 : 1;
+    constexpr int NB = 2;  // gate and up / two blocks of 64 down columns
     constexpr int ROWS = NB * 64;
     __shared__ DmaStage<NB, MT> st[2];
     // tile order as in mfma_grouped_kernel (one column block per workgroup)
-    const int ncb = (GU ? I : H) / 64;
+    const int ncb = GU ? I / 64 : (H / 64 + 1) / 2;
     const int L = blockIdx.x, r8 = L >> 3;
     const int cb0 = r8 % ncb;
     const int hit = (r8 / ncb) * 8 + (L & 7);
@@ -460,7 +462,7 @@ void mfma_dma3_kernel(
     const int NC = K / kKC;
     const bool tail = (K % kKC) != 0;
     const int n_stages = NC + (tail ? 1 : 0);
-    const int n0 = cb0 * 64;
+    const int n0 = cb0 * (GU ? 64 : 128);
 
     const uint8_t* rowb = pool + (size_t)slot * (size_t)slot_bytes;
     const size_t row_dw = (size_t)K * B / 32;
@@ -469,7 +471,7 @@ void mfma_dma3_kernel(
     constexpr float off = Code<B>::offset;
     const u32x4_t ones = {MOE_ONES_PAIR, MOE_ONES_PAIR, MOE_ONES_PAIR, MOE_ONES_PAIR};
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-    auto wrow = [&](int r) { return GU ? (r < 64 ? n0 + r : I + n0 + (r - 64)) : n0 + r; };
+    auto wrow = [&](int r) { return GU ? (r < 64 ? n0 + r : I + n0 + (r - 64)) : min(n0 + r, H - 1); };
 
     // loads of one stage: code pieces q = 256 i + tid (row q / 3, piece q % 3),
     // sb dwords q = tid (row q / 2, group q % 2), activation pieces q = 256 i + tid
@@ -606,7 +608,9 @@ void mfma_dma3_kernel(
                             const int pos = (n & ~31) | p16_pos(n & 31);
                             hbuf[(size_t)(base + r) * I + pos] = f32_to_bf16(silu_mul(acc[0][mt][i], acc[1][mt][i]));
                         } else {
-                            ybuf[(size_t)sorted_pairs[base + r] * H + n] = f32_to_bf16(acc[0][mt][i]);
+                            const size_t yr = (size_t)sorted_pairs[base + r] * H;
+                            ybuf[yr + n] = f32_to_bf16(acc[0][mt][i]);
+                            if (n + 64 < H) ybuf[yr + n + 64] = f32_to_bf16(acc[1][mt][i]);
                         }
                     }
                 }
@@ -719,7 +723,7 @@ hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, const int32
                        c.slot_bytes, c.off_d_codes, c.off_d_sb, nullptr, ybuf, err)
 #define MOE_MD2(BB) { if (mt == 4) MOE_MD(BB, 4); else MOE_MD(BB, 2); }
 #define MOE_MD3(MM)                                                                                \
-    hipLaunchKernelGGL((mfma_dma3_kernel<false, MM>), dim3((unsigned)((c.H / 64) * ((max_hit + 7) / 8) * 8)), \
+    hipLaunchKernelGGL((mfma_dma3_kernel<false, MM>), dim3((unsigned)(((c.H / 64 + 1) / 2) * ((max_hit + 7) / 8) * 8)), \
                        dim3(256), 0, s, hbuf, c.H, c.I, k, sv.offsets, sv.sorted_pairs, sv.pass_table, \
                        table, pool, c.n_slots, c.slot_bytes, c.off_d_codes, c.off_d_sb, nullptr,  \
                        ybuf, err)
