@@ -29,6 +29,11 @@
 // in identical accumulator layouts), h written as bf16 in P16 order.
 // down: y per (pair, output) in bf16 to a workspace; a combine kernel adds the
 // k contributions of each token in j order (deterministic).
+//
+// Width 3 runs mfma_dma3_kernel instead: the same arithmetic with each stage
+// loaded straight into LDS (no staging registers), and down with 128 output
+// columns per workgroup.  Width 16 stages 64 inputs at a time (its rows are
+// four times wider than 3-bit rows).
 #include <utility>
 
 #include "../../include/moe.h"
