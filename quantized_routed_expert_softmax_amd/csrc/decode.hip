@@ -546,11 +546,6 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
             }
             if (lane < k) s_sorted[rank] = lane;
         }
-        __syncthreads();
-        if (wg0 && P.ids_out && tid < n) {
-            P.ids_out[tid] = s_ids[tid];
-            P.w_out[tid] = s_w[tid];
-        }
     }
 
     const int lpr_d = P.lpr_d, rpp_d = udiv(64, lpr_d);
@@ -665,6 +660,17 @@ __global__ __launch_bounds__(64 * W) void decode_layer_kernel(DecodeParams P)
     //      mark in LDS.  A wave so waits only for the experts of its own items, not
     //      for the slowest expert of the layer. ----
     issue_p2(pre, 0);  // the phase-2 weights stream in while h is exchanged
+    // one token: phase 1 used only what the routing barrier published (hit list,
+    // slots, staged x), so the weights and pair order the routing wave wrote after
+    // its phase-1 loads are ordered here, before phase 2 reads them; phase 1 did
+    // not wait for them
+    if (fast1) {
+        __syncthreads();
+        if (wg0 && P.ids_out && tid < n) {
+            P.ids_out[tid] = s_ids[tid];
+            P.w_out[tid] = s_w[tid];
+        }
+    }
     float* s_part = (float*)(s_dyn + P.part_dw);  // [wave][row][t]
     float* part = s_part + wave * P.rows_per_wg * T;
     for (int q = lane; q < P.rows_per_wg * T; q += 64) part[q] = 0.0f;  // this wave's rows only
