@@ -284,6 +284,48 @@ int moe_layer_forward(const float* logits, int T, int E, int k, int mode, float 
                       uint32_t* err_word, hipStream_t stream);
 
 /*
+ * Prefill in passes.  A long prompt hits nearly every expert of a layer; its hit
+ * experts run, in ascending id, in passes of at most 64, so that only one pass's
+ * experts need to be resident at a time and the cache can be smaller than a
+ * layer ([RFC] "How the prototype works", Prefill bullet; [HF-PR] commit
+ * messages: sorted prefill, 64 experts at a time).  One layer is:
+ *   moe_prefill_sort    once: the stable sort of the T*k pairs by expert and the
+ *                       pass table (the layout of moe_sort_by_expert, P = 64) plus
+ *                       a permuted copy of x, all into ws;
+ *   moe_prefill_pass    for passes [pass_begin, pass_end) of that table: gate/up,
+ *                       SwiGLU and down of those passes' hit experts, each pair's
+ *                       expert output (bf16) kept in ws; only the slots of these
+ *                       experts are read, through `slot_table` as it is when the
+ *                       call's kernels run (so the table and pool may change
+ *                       between passes, ordered on the stream);
+ *   moe_prefill_combine once, after the last pass: out[t] = sum_j w[t,j] * y[t,j]
+ *                       in fp32, j ascending, bf16 round to nearest even.
+ * Passes are 0 .. ceil(E/64) - 1; passes past the hit count are empty no-ops.
+ * The three calls share one ws of moe_forward_workspace_size(T, k, E, d) bytes
+ * (256-byte aligned; same T, k, E and d in every call) and must be ordered on
+ * one stream or by events.  Running every pass in one call gives the same bits
+ * as moe_experts_forward on MOE_PATH_MFMA.  Host status: MOE_E_INVALID (ranges,
+ * NULL, alignment), MOE_E_WORKSPACE; device: as moe_experts_forward (an expert of
+ * the passes run with no slot sets MOE_ERRW_NOT_RESIDENT; its pairs' outputs are
+ * then unspecified).
+ *
+ * moe_pass_table_host: the same pass table computed on the host from host ids
+ * (int32 [T, k] in host memory) into host memory of moe_pass_table_size(E, P)
+ * int32: the hit experts of each pass, for the caller that makes a pass resident
+ * before running it.  MOE_E_INVALID for an id outside [0, E).
+ */
+int moe_pass_table_host(const int32_t* topk_ids, int T, int k, int E, int pass_experts,
+                        int32_t* pass_table);
+int moe_prefill_sort(const void* x, int T, const int32_t* topk_ids, int k, int E,
+                     const moe_size_class_desc* d, void* ws, size_t ws_bytes, uint32_t* err_word,
+                     hipStream_t stream);
+int moe_prefill_pass(int T, int k, int E, int pass_begin, int pass_end, const int32_t* slot_table,
+                     const void* slot_pool, const moe_size_class_desc* d, void* ws, size_t ws_bytes,
+                     uint32_t* err_word, hipStream_t stream);
+int moe_prefill_combine(int T, int k, int E, const float* topk_w, const moe_size_class_desc* d,
+                        void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Enqueue the copy of one expert row (d->slot_bytes bytes at `src`) into slot
  * `slot` of `slot_pool` on `copy_stream`, then record `done` (may be NULL) on it.
  * src_kind: MOE_SRC_HOST (pinned host memory) or MOE_SRC_DEVICE.  The copy is
@@ -450,6 +492,19 @@ int     moe_store_read(const moe_store* s, int layer, int expert, void* dst);
  * moe_pipeline_prefetch: guessed experts of `layer`: absent ones start installs
  *   in the background without pinning; resident or in-flight ones are skipped.
  *   Never waits.  Returns the number of installs started (>= 0) or an error.
+ * moe_pipeline_prefill: one layer of a prefill chunk run pass by pass through the
+ *   cache, so the layer's class may hold fewer slots than the chunk hits experts
+ *   (at least one pass: min(hit experts, 64)).  `ids_host` is the layer's routing
+ *   brought to the host (int32 [T, k], host memory); topk_ids / topk_w are the same
+ *   routing on the device; x, out, ws, err_word as moe_experts_forward (ws sized by
+ *   moe_forward_workspace_size for the layer's class).  Computes the pass table on
+ *   the host (moe_pass_table_host), enqueues moe_prefill_sort, then for each pass:
+ *   moe_pipeline_prepare(layer, the pass's hit experts, table_dev), moe_prefill_pass
+ *   of that pass on the layer's class pool, moe_pipeline_release(layer); finally
+ *   moe_prefill_combine, all on `compute`.  A pass's installs overlap the kernels
+ *   of the passes before it whenever their victims are not in use (a class with
+ *   two passes' worth of slots).  Returns the number of passes (>= 0) or a status
+ *   of the calls it makes.
  * moe_pipeline_drain: wait until every read and copy has finished.
  * moe_pipeline_stats_get: counters of one class (moe_pipeline_stats).
  * moe_pipeline_host_rows: host-tier rows of class `cls` (0 without a host tier).
@@ -486,6 +541,10 @@ int     moe_pipeline_prepare(moe_pipeline* p, int layer, const int32_t* ids, int
                              int32_t* table_dev, hipStream_t compute);
 int     moe_pipeline_release(moe_pipeline* p, int layer, hipStream_t compute);
 int     moe_pipeline_prefetch(moe_pipeline* p, int layer, const int32_t* ids, int n);
+int     moe_pipeline_prefill(moe_pipeline* p, int layer, const int32_t* ids_host, const void* x, int T,
+                             const int32_t* topk_ids, const float* topk_w, int k, int32_t* table_dev,
+                             void* out, void* ws, size_t ws_bytes, uint32_t* err_word,
+                             hipStream_t compute);
 int     moe_pipeline_drain(moe_pipeline* p);
 int     moe_pipeline_stats_get(const moe_pipeline* p, int cls, moe_pipeline_stats* out);
 int64_t moe_pipeline_host_rows(const moe_pipeline* p, int cls);

@@ -106,6 +106,10 @@ def lib() -> ctypes.CDLL:
                 "moe_experts_forward_ex": (I32, [P, I32, P, P, I32, I32, P, P, D, P, P, SZ, P, I32, P]),
                 "moe_forward_workspace_size": (SZ, [I32, I32, I32, D]),
                 "moe_layer_forward": (I32, [P, I32, I32, I32, I32, F32, P, P, P, D, P, P, P, P, SZ, P, P]),
+                "moe_pass_table_host": (I32, [P, I32, I32, I32, I32, P]),
+                "moe_prefill_sort": (I32, [P, I32, P, I32, I32, D, P, SZ, P, P]),
+                "moe_prefill_pass": (I32, [I32, I32, I32, I32, I32, P, P, D, P, SZ, P, P]),
+                "moe_prefill_combine": (I32, [I32, I32, I32, P, D, P, P, SZ, P]),
                 "moe_cache_install": (I32, [P, D, I64, P, I32, P, P]),
                 "moe_cache_create": (P, [D, I32, P, I32, I32]),
                 "moe_cache_create_ex": (P, [D, I32, P, I32, I32, I32, I32]),
@@ -135,6 +139,7 @@ def lib() -> ctypes.CDLL:
                 "moe_pipeline_prepare": (I32, [P, I32, P, I32, P, P]),
                 "moe_pipeline_release": (I32, [P, I32, P]),
                 "moe_pipeline_prefetch": (I32, [P, I32, P, I32]),
+                "moe_pipeline_prefill": (I32, [P, I32, P, P, I32, P, P, I32, P, P, P, SZ, P, P]),
                 "moe_pipeline_drain": (I32, [P]),
                 "moe_pipeline_stats_get": (I32, [P, I32, ctypes.POINTER(PipelineStats)]),
                 "moe_pipeline_host_rows": (I64, [P, I32]),
@@ -325,6 +330,64 @@ def moe_layer_forward(logits, x, slot_table, slot_pool, desc: SizeClassDesc, k: 
         _dev_ptr(ws, torch.uint8, "ws"), ws.numel(), _opt_ptr(err_word, torch.int32, "err_word"),
         _stream(stream)))
     return out, topk_ids, topk_w
+
+
+def moe_pass_table_host(topk_ids, E: int, pass_experts: int = PASS_EXPERTS):
+    """Pass table of host ids (int32 [T, k] numpy) computed on the host."""
+    import numpy as np
+    a = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    T, k = a.shape
+    pt = np.empty(moe_pass_table_size(E, pass_experts), dtype=np.int32)
+    _check(lib().moe_pass_table_host(ctypes.c_void_p(a.ctypes.data), T, k, E, pass_experts,
+                                     ctypes.c_void_p(pt.ctypes.data)))
+    return pt
+
+
+def _fwd_ws(T, k, E, desc, ws, dev):
+    torch = _torch()
+    if ws is None:
+        ws = torch.zeros(max(moe_forward_workspace_size(T, k, E, desc), 256), dtype=torch.uint8, device=dev)
+    return ws
+
+
+def moe_prefill_sort(x, topk_ids, E: int, desc: SizeClassDesc, ws=None, err_word=None, stream=None):
+    """Sort the pairs by expert and permute x into the forward workspace; returns ws."""
+    torch = _torch()
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    if H != desc.H:
+        raise ValueError(f"x has {H} columns, size class has H={desc.H}")
+    ws = _fwd_ws(T, k, E, desc, ws, x.device)
+    _check(lib().moe_prefill_sort(_dev_ptr(x, torch.bfloat16, "x", 2), T,
+                                  _dev_ptr(topk_ids, torch.int32, "topk_ids", 2), k, E, ctypes.byref(desc),
+                                  _dev_ptr(ws, torch.uint8, "ws"), ws.numel(),
+                                  _opt_ptr(err_word, torch.int32, "err_word"), _stream(stream)))
+    return ws
+
+
+def moe_prefill_pass(T: int, k: int, E: int, pass_begin: int, pass_end: int, slot_table, slot_pool,
+                     desc: SizeClassDesc, ws, err_word=None, stream=None):
+    """gate/up, SwiGLU and down of the hit experts of passes [pass_begin, pass_end)."""
+    torch = _torch()
+    if slot_pool.numel() < desc.n_slots * desc.slot_bytes:
+        raise ValueError("slot_pool smaller than n_slots * slot_bytes")
+    _check(lib().moe_prefill_pass(T, k, E, pass_begin, pass_end,
+                                  _dev_ptr(slot_table, torch.int32, "slot_table", 1),
+                                  _dev_ptr(slot_pool, torch.uint8, "slot_pool"), ctypes.byref(desc),
+                                  _dev_ptr(ws, torch.uint8, "ws"), ws.numel(),
+                                  _opt_ptr(err_word, torch.int32, "err_word"), _stream(stream)))
+
+
+def moe_prefill_combine(topk_w, E: int, desc: SizeClassDesc, ws, out=None, stream=None):
+    """out[t] = sum_j w[t, j] * y[t, j] after the last pass."""
+    torch = _torch()
+    T, k = topk_w.shape
+    if out is None:
+        out = torch.empty((T, desc.H), dtype=torch.bfloat16, device=topk_w.device)
+    _check(lib().moe_prefill_combine(T, k, E, _dev_ptr(topk_w, torch.float32, "topk_w", 2),
+                                     ctypes.byref(desc), _dev_ptr(out, torch.bfloat16, "out", 2),
+                                     _dev_ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
+    return out
 
 
 def moe_cache_install(slot_pool, desc: SizeClassDesc, slot: int, src, stream=None, event=None):
@@ -550,6 +613,33 @@ def moe_pipeline_prefetch(p: int, layer: int, ids) -> int:
     if rc < 0:
         raise MoeError(rc, moe_last_error())
     return rc
+
+
+def moe_pipeline_prefill(p: int, layer: int, ids_host, x, topk_ids, topk_w, table_dev, desc: SizeClassDesc,
+                         out=None, ws=None, err_word=None, stream=None) -> tuple:
+    """One prefill layer pass by pass through the cache; returns (out, passes run).
+    `desc` is the layer's size class (it sizes the workspace)."""
+    torch = _torch()
+    import numpy as np
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    E = table_dev.shape[0]
+    a = np.ascontiguousarray(ids_host, dtype=np.int32)
+    if a.shape != (T, k):
+        raise ValueError("ids_host must be [T, k]")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    ws = _fwd_ws(T, k, E, desc, ws, x.device)
+    rc = lib().moe_pipeline_prefill(p, layer, ctypes.c_void_p(a.ctypes.data),
+                                    _dev_ptr(x, torch.bfloat16, "x", 2), T,
+                                    _dev_ptr(topk_ids, torch.int32, "topk_ids", 2),
+                                    _dev_ptr(topk_w, torch.float32, "topk_w", 2), k,
+                                    _dev_ptr(table_dev, torch.int32, "table_dev", 1),
+                                    _dev_ptr(out, torch.bfloat16, "out", 2), _dev_ptr(ws, torch.uint8, "ws"),
+                                    ws.numel(), _opt_ptr(err_word, torch.int32, "err_word"), _stream(stream))
+    if rc < 0:
+        raise MoeError(rc, moe_last_error())
+    return out, rc
 
 
 def moe_pipeline_drain(p: int):

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/moe.h"
 #include "moe_internal.h"
@@ -38,7 +39,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-constexpr int kPassExperts = 64;  // experts per pass of the sorted prefill
+using moe::kPassExperts;
 
 int check_desc(const moe_size_class_desc* d)
 {
@@ -100,6 +101,43 @@ FwdLayout fwd_layout(int T, int k, int E, const moe_size_class_desc* d)
     o = align_up(o + sizeof(uint16_t) * n * (size_t)d->H, 256);  // y in bf16
     L.total = o;
     return L;
+}
+
+int n_pass_max(int E) { return (E + kPassExperts - 1) / kPassExperts; }
+
+// gate/up + SwiGLU and down of the hit experts of passes [p0, p1): h and y of
+// their pairs in the workspace (sort and permuted x already there).
+int run_passes(int T, int k, int E, int p0, int p1, const int32_t* slot_table, const uint8_t* pool,
+               const moe::ClassView& c, const FwdLayout& L, char* w, uint32_t* err_word,
+               hipStream_t stream)
+{
+    const moe::SortView sv{(const int32_t*)(w + L.offsets), (const int32_t*)(w + L.sorted),
+                           (const int32_t*)(w + L.pass)};
+    uint16_t* hbuf = (uint16_t*)(w + L.hbuf);
+    hipError_t e = moe::launch_mfma_gateup((const uint16_t*)(w + L.xp), T, k, E, sv, p0, p1, slot_table,
+                                           pool, c, hbuf, err_word, stream);
+    if (e != hipSuccess) return hip_fail(e, "mfma gate/up launch");
+    e = moe::launch_mfma_down(T, k, E, sv, p0, p1, slot_table, pool, c, hbuf, (uint16_t*)(w + L.ybuf),
+                              err_word, stream);
+    if (e != hipSuccess) return hip_fail(e, "mfma down launch");
+    return MOE_OK;
+}
+
+// Shared checks of the forward-shaped calls: T, E, k ranges and the workspace.
+int check_fwd(int T, int k, int E, const moe_size_class_desc* d, const void* ws, size_t ws_bytes,
+              FwdLayout* L)
+{
+    if (int rc = check_desc(d)) return rc;
+    if (T < 0) return fail(MOE_E_INVALID, "T < 0");
+    if (E < 1 || E > 1024) return fail(MOE_E_INVALID, "E must be in [1, 1024] (got %d)", E);
+    if (k < 1 || k > E || k > 32) return fail(MOE_E_INVALID, "k must be in [1, min(E, 32)] (got %d)", k);
+    if ((int64_t)T * k > (int64_t)1 << 26) return fail(MOE_E_INVALID, "T*k too large");
+    *L = fwd_layout(T, k, E, d);
+    if (T == 0) return MOE_OK;
+    if (!ws || !aligned(ws, 256)) return fail(MOE_E_INVALID, "ws must be a 256-byte aligned buffer");
+    if (ws_bytes < L->total)
+        return fail(MOE_E_WORKSPACE, "forward workspace %zu bytes < %zu", ws_bytes, L->total);
+    return MOE_OK;
 }
 
 }  // namespace
@@ -273,15 +311,12 @@ int moe_experts_forward_ex(const void* x, int T, const int32_t* topk_ids, const 
         if (e != hipSuccess) return hip_fail(e, "gemv down launch");
         return MOE_OK;
     }
-    uint16_t* xp = (uint16_t*)(w + L.xp);
-    uint16_t* ybuf = (uint16_t*)(w + L.ybuf);
-    e = moe::launch_permute_x((const uint16_t*)x, T, c.H, xp, stream);
+    // MFMA: every pass in one launch pair (the whole hit list is resident)
+    e = moe::launch_permute_x((const uint16_t*)x, T, c.H, (uint16_t*)(w + L.xp), stream);
     if (e != hipSuccess) return hip_fail(e, "permute launch");
-    e = moe::launch_mfma_gateup(xp, T, k, E, sv, slot_table, pool, c, hbuf, err_word, stream);
-    if (e != hipSuccess) return hip_fail(e, "mfma gate/up launch");
-    e = moe::launch_mfma_down(T, k, E, sv, slot_table, pool, c, hbuf, ybuf, err_word, stream);
-    if (e != hipSuccess) return hip_fail(e, "mfma down launch");
-    e = moe::launch_combine(ybuf, topk_w, T, k, c.H, (uint16_t*)out, stream);
+    if (int rc = run_passes(T, k, E, 0, n_pass_max(E), slot_table, pool, c, L, w, err_word, stream))
+        return rc;
+    e = moe::launch_combine((const uint16_t*)(w + L.ybuf), topk_w, T, k, c.H, (uint16_t*)out, stream);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return MOE_OK;
 }
@@ -330,6 +365,84 @@ int moe_experts_forward(const void* x, int T, const int32_t* topk_ids, const flo
 {
     return moe_experts_forward_ex(x, T, topk_ids, topk_w, k, E, slot_table, slot_pool, d, out, ws,
                                   ws_bytes, err_word, MOE_PATH_AUTO, stream);
+}
+
+int moe_pass_table_host(const int32_t* topk_ids, int T, int k, int E, int pass_experts,
+                        int32_t* pass_table)
+{
+    if (T < 0) return fail(MOE_E_INVALID, "T < 0");
+    if (E < 1 || E > 1024) return fail(MOE_E_INVALID, "E must be in [1, 1024] (got %d)", E);
+    if (k < 1 || k > E || k > 32) return fail(MOE_E_INVALID, "k must be in [1, min(E, 32)] (got %d)", k);
+    if (pass_experts < 1) return fail(MOE_E_INVALID, "pass_experts must be >= 1");
+    if (!pass_table || (T > 0 && !topk_ids)) return fail(MOE_E_INVALID, "NULL buffer");
+    std::vector<char> hit((size_t)E, 0);
+    for (int64_t p = 0; p < (int64_t)T * k; ++p) {
+        const int32_t e = topk_ids[p];
+        if (e < 0 || e >= E) return fail(MOE_E_INVALID, "expert id %d of pair %lld outside [0, %d)", e, (long long)p, E);
+        hit[(size_t)e] = 1;
+    }
+    int n_hit = 0;
+    for (int e = 0; e < E; ++e) {
+        pass_table[2 + e] = -1;
+        if (hit[(size_t)e]) pass_table[2 + n_hit++] = e;
+    }
+    const int n_max = (E + pass_experts - 1) / pass_experts;
+    pass_table[0] = n_hit;
+    pass_table[1] = (n_hit + pass_experts - 1) / pass_experts;
+    for (int q = 0; q <= n_max; ++q) {
+        const int64_t start = (int64_t)q * pass_experts;
+        pass_table[2 + E + q] = start < n_hit ? (int32_t)start : n_hit;
+    }
+    return MOE_OK;
+}
+
+int moe_prefill_sort(const void* x, int T, const int32_t* topk_ids, int k, int E,
+                     const moe_size_class_desc* d, void* ws, size_t ws_bytes, uint32_t* err_word,
+                     hipStream_t stream)
+{
+    FwdLayout L;
+    if (int rc = check_fwd(T, k, E, d, ws, ws_bytes, &L)) return rc;
+    if (T == 0) return MOE_OK;
+    if (!x || !topk_ids) return fail(MOE_E_INVALID, "NULL buffer");
+    if (!aligned(x, 16)) return fail(MOE_E_INVALID, "x needs 16-byte alignment");
+    char* w = (char*)ws;
+    hipError_t e = moe::launch_sort(topk_ids, T, k, E, kPassExperts, (int32_t*)(w + L.offsets),
+                                    (int32_t*)(w + L.sorted), (int32_t*)(w + L.pass), w + L.sort_ws,
+                                    err_word, stream);
+    if (e != hipSuccess) return hip_fail(e, "sort launch");
+    e = moe::launch_permute_x((const uint16_t*)x, T, d->H, (uint16_t*)(w + L.xp), stream);
+    if (e != hipSuccess) return hip_fail(e, "permute launch");
+    return MOE_OK;
+}
+
+int moe_prefill_pass(int T, int k, int E, int pass_begin, int pass_end, const int32_t* slot_table,
+                     const void* slot_pool, const moe_size_class_desc* d, void* ws, size_t ws_bytes,
+                     uint32_t* err_word, hipStream_t stream)
+{
+    FwdLayout L;
+    if (int rc = check_fwd(T, k, E, d, ws, ws_bytes, &L)) return rc;
+    const int nmax = n_pass_max(E);
+    if (pass_begin < 0 || pass_end > nmax || pass_begin > pass_end)
+        return fail(MOE_E_INVALID, "pass range [%d, %d) outside [0, %d]", pass_begin, pass_end, nmax);
+    if (T == 0 || pass_begin == pass_end) return MOE_OK;
+    if (!slot_table || !slot_pool) return fail(MOE_E_INVALID, "NULL buffer");
+    if (!aligned(slot_pool, 256)) return fail(MOE_E_INVALID, "slot_pool needs 256-byte alignment");
+    return run_passes(T, k, E, pass_begin, pass_end, slot_table, (const uint8_t*)slot_pool, view_of(d),
+                      L, (char*)ws, err_word, stream);
+}
+
+int moe_prefill_combine(int T, int k, int E, const float* topk_w, const moe_size_class_desc* d,
+                        void* out, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    FwdLayout L;
+    if (int rc = check_fwd(T, k, E, d, ws, ws_bytes, &L)) return rc;
+    if (T == 0) return MOE_OK;
+    if (!topk_w || !out) return fail(MOE_E_INVALID, "NULL buffer");
+    if (!aligned(out, 16)) return fail(MOE_E_INVALID, "out needs 16-byte alignment");
+    hipError_t e = moe::launch_combine((const uint16_t*)((char*)ws + L.ybuf), topk_w, T, k, d->H,
+                                       (uint16_t*)out, stream);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    return MOE_OK;
 }
 
 int moe_cache_install(void* slot_pool, const moe_size_class_desc* d, int64_t slot, const void* src,

@@ -179,10 +179,10 @@ template <int B, bool GU, int MT, int CBW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((B <= 4 || B == 16) && MT == 2 ? 3 : 1)))
 void mfma_grouped_kernel(
     const uint16_t* __restrict__ act, int H, int I, int k, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table,
-    const int32_t* __restrict__ table, const uint8_t* __restrict__ pool, int64_t n_slots,
-    int64_t slot_bytes, int64_t off_codes, int64_t off_sb, uint16_t* __restrict__ hbuf,
-    uint16_t* __restrict__ ybuf, uint32_t* __restrict__ err)
+    const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table, int E,
+    int pass_lo, int pass_hi, const int32_t* __restrict__ table, const uint8_t* __restrict__ pool,
+    int64_t n_slots, int64_t slot_bytes, int64_t off_codes, int64_t off_sb,
+    uint16_t* __restrict__ hbuf, uint16_t* __restrict__ ybuf, uint32_t* __restrict__ err)
 {
     constexpr int NB = GU ? 2 : 1;
     constexpr int KC = stage_k<B>(), UPC = KC / 32, GPC = KC / 64;
@@ -196,8 +196,9 @@ void mfma_grouped_kernel(
     const int L = blockIdx.x, r8 = L >> 3;
     const int cb0 = (r8 % nwg) * CBW;
     const int ncb_wg = min(CBW, ncb - cb0);     // column blocks of this workgroup
-    const int hit = (r8 / nwg) * 8 + (L & 7);
-    if (hit >= pass_table[0]) return;
+    // the hit experts of passes [pass_lo, pass_hi): a contiguous run of the hit list
+    const int hit = pass_table[2 + E + pass_lo] + (r8 / nwg) * 8 + (L & 7);
+    if (hit >= pass_table[2 + E + pass_hi]) return;
     const int e = pass_table[2 + hit];
     const int32_t slot = table[e];
     if (slot < 0 || slot >= n_slots) {
@@ -439,10 +440,10 @@ template <bool GU, int MT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 2 ? (GU ? 3 : 4) : 1)))
 void mfma_dma3_kernel(
     const uint16_t* __restrict__ act, int H, int I, int k, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table,
-    const int32_t* __restrict__ table, const uint8_t* __restrict__ pool, int64_t n_slots,
-    int64_t slot_bytes, int64_t off_codes, int64_t off_sb, uint16_t* __restrict__ hbuf,
-    uint16_t* __restrict__ ybuf, uint32_t* __restrict__ err)
+    const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table, int E,
+    int pass_lo, int pass_hi, const int32_t* __restrict__ table, const uint8_t* __restrict__ pool,
+    int64_t n_slots, int64_t slot_bytes, int64_t off_codes, int64_t off_sb,
+    uint16_t* __restrict__ hbuf, uint16_t* __restrict__ ybuf, uint32_t* __restrict__ err)
 {
     constexpr int B = 3;
     constexpr int NB = 2;  // gate and up / two blocks of 64 down columns
@@ -452,8 +453,8 @@ void mfma_dma3_kernel(
     const int ncb = GU ? I / 64 : (H / 64 + 1) / 2;
     const int L = blockIdx.x, r8 = L >> 3;
     const int cb0 = r8 % ncb;
-    const int hit = (r8 / ncb) * 8 + (L & 7);
-    if (hit >= pass_table[0]) return;
+    const int hit = pass_table[2 + E + pass_lo] + (r8 / ncb) * 8 + (L & 7);
+    if (hit >= pass_table[2 + E + pass_hi]) return;
     const int e = pass_table[2 + hit];
     const int32_t slot = table[e];
     if (slot < 0 || slot >= n_slots) {
@@ -674,6 +675,16 @@ hipError_t launch_permute_x(const uint16_t* x, int T, int H, uint16_t* xp, hipSt
     return hipGetLastError();
 }
 
+// Most hit experts passes [pass_lo, pass_hi) can hold: kPassExperts each, and no
+// more than the distinct experts the T*k pairs can reach.
+static int pass_hits_max(int T, int k, int E, int pass_lo, int pass_hi)
+{
+    int64_t m = (int64_t)T * k;
+    if (m > E) m = E;
+    const int64_t p = (int64_t)kPassExperts * (pass_hi - pass_lo);
+    return (int)(m < p ? m : p);
+}
+
 // M-tiles per sweep: 2 (32 rows) when experts average few rows, else 4.
 static int pick_mt(int T, int k, int E)
 {
@@ -683,22 +694,22 @@ static int pick_mt(int T, int k, int E)
 }
 
 hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const SortView& sv,
-                              const int32_t* table, const uint8_t* pool, const ClassView& c,
-                              uint16_t* hbuf, uint32_t* err, hipStream_t s)
+                              int pass_lo, int pass_hi, const int32_t* table, const uint8_t* pool,
+                              const ClassView& c, uint16_t* hbuf, uint32_t* err, hipStream_t s)
 {
-    const int max_hit = (int64_t)T * k < E ? T * k : E;
+    const int max_hit = pass_hits_max(T, k, E, pass_lo, pass_hi);
     constexpr int CBW = 1;  // column blocks per workgroup
     dim3 grid((unsigned)(((c.I / 64 + CBW - 1) / CBW) * ((max_hit + 7) / 8) * 8));  // see the kernel's tile order
     const int mt = pick_mt(T, k, E);
 #define MOE_MG(BB, MM)                                                                             \
     hipLaunchKernelGGL((mfma_grouped_kernel<BB, true, MM, CBW>), grid, dim3(256), 0, s, xp, c.H, c.I, k, \
-                       sv.offsets, sv.sorted_pairs, sv.pass_table, table, pool, c.n_slots,         \
+                       sv.offsets, sv.sorted_pairs, sv.pass_table, E, pass_lo, pass_hi, table, pool, c.n_slots,         \
                        c.slot_bytes, c.off_gu_codes, c.off_gu_sb, hbuf, nullptr, err)
 #define MOE_MG2(BB) { if (mt == 4) MOE_MG(BB, 4); else MOE_MG(BB, 2); }
 #define MOE_MG3(MM)                                                                                \
     hipLaunchKernelGGL((mfma_dma3_kernel<true, MM>), dim3((unsigned)((c.I / 64) * ((max_hit + 7) / 8) * 8)), \
                        dim3(256), 0, s, xp, c.H, c.I, k, sv.offsets, sv.sorted_pairs, sv.pass_table, \
-                       table, pool, c.n_slots, c.slot_bytes, c.off_gu_codes, c.off_gu_sb, hbuf,    \
+                       E, pass_lo, pass_hi, table, pool, c.n_slots, c.slot_bytes, c.off_gu_codes, c.off_gu_sb, hbuf,    \
                        nullptr, err)
     switch (c.bits_gu) {
     case 3: if (mt == 4) MOE_MG3(4); else MOE_MG3(2); break;
@@ -714,23 +725,23 @@ hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const Sor
     return hipGetLastError();
 }
 
-hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, const int32_t* table,
-                            const uint8_t* pool, const ClassView& c, const uint16_t* hbuf,
-                            uint16_t* ybuf, uint32_t* err, hipStream_t s)
+hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, int pass_lo, int pass_hi,
+                            const int32_t* table, const uint8_t* pool, const ClassView& c,
+                            const uint16_t* hbuf, uint16_t* ybuf, uint32_t* err, hipStream_t s)
 {
-    const int max_hit = (int64_t)T * k < E ? T * k : E;
+    const int max_hit = pass_hits_max(T, k, E, pass_lo, pass_hi);
     constexpr int CBW = 1;  // column blocks per workgroup
     dim3 grid((unsigned)(((c.H / 64 + CBW - 1) / CBW) * ((max_hit + 7) / 8) * 8));  // see the kernel's tile order
     const int mt = pick_mt(T, k, E);
 #define MOE_MD(BB, MM)                                                                             \
     hipLaunchKernelGGL((mfma_grouped_kernel<BB, false, MM, CBW>), grid, dim3(256), 0, s, hbuf, c.H, c.I, \
-                       k, sv.offsets, sv.sorted_pairs, sv.pass_table, table, pool, c.n_slots,      \
+                       k, sv.offsets, sv.sorted_pairs, sv.pass_table, E, pass_lo, pass_hi, table, pool, c.n_slots,      \
                        c.slot_bytes, c.off_d_codes, c.off_d_sb, nullptr, ybuf, err)
 #define MOE_MD2(BB) { if (mt == 4) MOE_MD(BB, 4); else MOE_MD(BB, 2); }
 #define MOE_MD3(MM)                                                                                \
     hipLaunchKernelGGL((mfma_dma3_kernel<false, MM>), dim3((unsigned)(((c.H / 64 + 1) / 2) * ((max_hit + 7) / 8) * 8)), \
                        dim3(256), 0, s, hbuf, c.H, c.I, k, sv.offsets, sv.sorted_pairs, sv.pass_table, \
-                       table, pool, c.n_slots, c.slot_bytes, c.off_d_codes, c.off_d_sb, nullptr,  \
+                       E, pass_lo, pass_hi, table, pool, c.n_slots, c.slot_bytes, c.off_d_codes, c.off_d_sb, nullptr,  \
                        ybuf, err)
     switch (c.bits_d) {
     case 3: if (mt == 4) MOE_MD3(4); else MOE_MD3(2); break;

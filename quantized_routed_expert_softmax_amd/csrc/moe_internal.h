@@ -8,6 +8,11 @@
 
 namespace moe {
 
+// Experts per pass of the sorted prefill: a long prompt's hit experts run in
+// passes of at most this many ("RFC: stream MoE experts from disk in
+// from_pretrained", How the prototype works, Prefill bullet).
+constexpr int kPassExperts = 64;
+
 // Record `msg` as this thread's moe_last_error() text; returns `code`.
 int set_error(int code, const char* msg);
 
@@ -59,12 +64,14 @@ hipError_t launch_decode_fused(const float* logits, int mode, float L, const int
 // Prefill path: P16-permuted x, MFMA gate/up + SwiGLU, MFMA down (y in bf16),
 // combine (fp32 sum in j order).
 hipError_t launch_permute_x(const uint16_t* x, int T, int H, uint16_t* xp, hipStream_t s);
+// Both run the hit experts of passes [pass_lo, pass_hi) of the pass table only
+// (0 and ceil(E / kPassExperts) for every hit expert).
 hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const SortView& sv,
-                              const int32_t* table, const uint8_t* pool, const ClassView& c,
-                              uint16_t* hbuf, uint32_t* err, hipStream_t s);
-hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, const int32_t* table,
-                            const uint8_t* pool, const ClassView& c, const uint16_t* hbuf,
-                            uint16_t* ybuf, uint32_t* err, hipStream_t s);
+                              int pass_lo, int pass_hi, const int32_t* table, const uint8_t* pool,
+                              const ClassView& c, uint16_t* hbuf, uint32_t* err, hipStream_t s);
+hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, int pass_lo, int pass_hi,
+                            const int32_t* table, const uint8_t* pool, const ClassView& c,
+                            const uint16_t* hbuf, uint16_t* ybuf, uint32_t* err, hipStream_t s);
 hipError_t launch_combine(const uint16_t* ybuf, const float* topk_w, int T, int k, int H,
                           uint16_t* out, hipStream_t s);
 

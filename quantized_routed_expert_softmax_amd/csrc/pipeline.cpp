@@ -40,6 +40,7 @@
 #include <sys/stat.h>
 #include <unistd.h>
 
+#include <algorithm>
 #include <cerrno>
 #include <condition_variable>
 #include <cstring>
@@ -894,6 +895,40 @@ int moe_pipeline_drain(moe_pipeline* p)
     std::lock_guard<std::mutex> g(p->mu);
     if (p->io_error) return pfail(p->io_error, "moe_pipeline_drain: an install failed");
     return MOE_OK;
+}
+
+int moe_pipeline_prefill(moe_pipeline* p, int layer, const int32_t* ids_host, const void* x, int T,
+                         const int32_t* topk_ids, const float* topk_w, int k, int32_t* table_dev,
+                         void* out, void* ws, size_t ws_bytes, uint32_t* err_word, hipStream_t compute)
+{
+    if (!p || layer < 0 || layer >= p->n_layers)
+        return pfail(MOE_E_INVALID, "moe_pipeline_prefill: bad arguments");
+    if (T == 0) return 0;
+    const int E = p->E;
+    const int cls = p->cls_of(layer);
+    const moe_size_class_desc* d = &p->desc[(size_t)cls];
+    std::vector<int32_t> pt((size_t)moe_pass_table_size(E, moe::kPassExperts));
+    if (pt.empty()) return pfail(MOE_E_INVALID, "moe_pipeline_prefill: bad E");
+    if (int rc = moe_pass_table_host(ids_host, T, k, E, moe::kPassExperts, pt.data())) return rc;
+    const int n_pass = pt[1];
+    if (n_pass > 0 && d->n_slots < std::min<int64_t>(pt[0], moe::kPassExperts))
+        return pfail(MOE_E_NO_SLOT, "moe_pipeline_prefill: the layer's class holds fewer slots than one pass");
+    if (int rc = moe_prefill_sort(x, T, topk_ids, k, E, d, ws, ws_bytes, err_word, compute)) return rc;
+    const int32_t* starts = pt.data() + 2 + E;
+    for (int q = 0; q < n_pass; ++q) {
+        // the pass's hit experts resident (their installs overlap the kernels of
+        // the passes already enqueued), its kernels, then the slots released
+        const int32_t* hits = pt.data() + 2 + starts[q];
+        if (int rc = moe_pipeline_prepare(p, layer, hits, starts[q + 1] - starts[q], table_dev, compute))
+            return rc;
+        const int rc = moe_prefill_pass(T, k, E, q, q + 1, table_dev, p->pools[(size_t)cls], d, ws, ws_bytes,
+                                        err_word, compute);
+        const int rr = moe_pipeline_release(p, layer, compute);
+        if (rc) return rc;
+        if (rr) return rr;
+    }
+    if (int rc = moe_prefill_combine(T, k, E, topk_w, d, out, ws, ws_bytes, compute)) return rc;
+    return n_pass;
 }
 
 int moe_pipeline_stats_get(const moe_pipeline* p, int cls, moe_pipeline_stats* out)

@@ -117,3 +117,69 @@ def test_workspace_sizes_cover_prefill():
     # per-pair y (bf16), per-pair h (bf16) and the permuted x (bf16)
     assert ws >= n * 2048 * 2 + n * 512 * 2 + 1024 * 2048 * 2
     assert B.moe_pass_table_size(512, 64) == 2 + 512 + 8 + 1
+
+
+@pytest.mark.parametrize("T,k,E,P,kind", [
+    (1024, 10, 512, 64, "uniform"),   # a prefill chunk: every expert hit, 8 passes
+    (256, 8, 128, 64, "uniform"),
+    (37, 8, 100, 64, "uniform"),      # E not a multiple of 64
+    (5, 3, 300, 64, "uniform"),       # fewer hit experts than one pass
+    (64, 32, 1024, 64, "uniform"),    # maximum E and k
+    (300, 7, 1000, 16, "uniform"),    # other pass sizes
+    (500, 2, 16, 4, "skew"),          # every pair on two experts
+    (1, 1, 1, 64, "uniform"),
+    (0, 4, 8, 64, "uniform"),         # no tokens: no hit expert, no pass
+])
+def test_pass_table_host_matches_oracle_sort(T, k, E, P, kind):
+    """The host pass table (what a caller makes resident before each pass) is the
+    oracle's pass table bit for bit."""
+    import oracle
+    rng = synth.rng_for(T, k, E, 990)
+    if kind == "skew":
+        ids = np.tile(np.array([[3, 11]], dtype=np.int32), (T, 1))
+    else:
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32) if T \
+            else np.zeros((0, k), np.int32)
+    pt = B.moe_pass_table_host(ids, E, P)
+    if T:
+        _, _, pt_o = oracle.sort(ids, E, P)
+        assert np.array_equal(pt, pt_o)
+    hit = sorted(set(ids.reshape(-1).tolist()))
+    assert pt[0] == len(hit) and pt[1] == (len(hit) + P - 1) // P
+    assert pt[2:2 + len(hit)].tolist() == hit and np.all(pt[2 + len(hit):2 + E] == -1)
+    starts = pt[2 + E:]
+    for q in range(len(starts) - 1):   # passes of at most P, in order, covering the hit list
+        assert 0 <= starts[q + 1] - starts[q] <= P
+    assert starts[0] == 0 and starts[-1] == len(hit)
+
+
+def test_pass_table_host_rejects_bad_ids():
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_pass_table_host(np.array([[0, 8]], np.int32), 8)
+    assert ei.value.code == B.MOE_E_INVALID
+    with pytest.raises(B.MoeError):
+        B.moe_pass_table_host(np.array([[-1, 2]], np.int32), 8)
+
+
+def test_prefill_argument_checks_on_host():
+    L = B.lib()
+    d = B.moe_size_class_init(256, 128, 4, 4, 8)
+    ws = B.moe_forward_workspace_size(16, 2, 100, d)
+    A = ctypes.c_void_p(0x100000)  # 256-aligned fake address, never dereferenced
+    D = ctypes.byref(d)
+    pas = L.moe_prefill_pass
+    assert pas(16, 2, 100, 0, 3, A, A, D, A, ws, None, None) == B.MOE_E_INVALID   # passes 0..1
+    assert pas(16, 2, 100, -1, 1, A, A, D, A, ws, None, None) == B.MOE_E_INVALID
+    assert pas(16, 2, 100, 1, 0, A, A, D, A, ws, None, None) == B.MOE_E_INVALID
+    assert pas(16, 2, 100, 0, 1, A, A, D, A, ws - 1, None, None) == B.MOE_E_WORKSPACE
+    assert pas(16, 2, 100, 0, 1, None, A, D, A, ws, None, None) == B.MOE_E_INVALID
+    assert pas(16, 2, 100, 1, 1, A, A, D, A, ws, None, None) == B.MOE_OK         # empty range
+    assert pas(16, 9, 8, 0, 1, A, A, D, A, ws, None, None) == B.MOE_E_INVALID    # k > E
+    srt = L.moe_prefill_sort
+    assert srt(A, 16, A, 2, 100, D, A, ws - 1, None, None) == B.MOE_E_WORKSPACE
+    assert srt(ctypes.c_void_p(0x100008), 16, A, 2, 100, D, ctypes.c_void_p(0x100008), ws, None,
+               None) == B.MOE_E_INVALID
+    assert srt(None, 0, None, 2, 100, D, None, 0, None, None) == B.MOE_OK        # T = 0
+    cmb = L.moe_prefill_combine
+    assert cmb(16, 2, 100, None, D, A, A, ws, None) == B.MOE_E_INVALID
+    assert cmb(16, 2, 100, A, D, A, A, ws - 256, None) == B.MOE_E_WORKSPACE
