@@ -284,6 +284,26 @@ int moe_layer_forward(const float* logits, int T, int E, int k, int mode, float 
                       uint32_t* err_word, hipStream_t stream);
 
 /*
+ * moe_layer_forward with no workspace argument and no allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, semantics and
+ * results as moe_layer_forward (bit-identical).  Its scratch is one array of
+ * MOE_STATIC_SCRATCH_BYTES in the library's device memory per GPU, held until
+ * the process ends; the first call on a device looks its address up and clears
+ * its reserved prefix with a small kernel on `stream`.  A layer whose workspace
+ * (moe_forward_workspace_size) exceeds MOE_STATIC_SCRATCH_BYTES is refused with
+ * MOE_E_WORKSPACE before anything is enqueued.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and give unspecified results; order them on one stream.
+ * Allocates nothing: no hipMalloc, no hipFree, no allocating library routine.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (8u << 20)
+int moe_layer_forward_static(const float* logits, int T, int E, int k, int mode, float L, const void* x,
+                             const int32_t* slot_table, const void* slot_pool,
+                             const moe_size_class_desc* d, int32_t* topk_ids, float* topk_w, void* out,
+                             uint32_t* err_word, hipStream_t stream);
+
+/*
  * Prefill in passes.  A long prompt hits nearly every expert of a layer; its hit
  * experts run, in ascending id, in passes of at most 64, so that only one pass's
  * experts need to be resident at a time and the cache can be smaller than a

@@ -106,6 +106,7 @@ def lib() -> ctypes.CDLL:
                 "moe_experts_forward_ex": (I32, [P, I32, P, P, I32, I32, P, P, D, P, P, SZ, P, I32, P]),
                 "moe_forward_workspace_size": (SZ, [I32, I32, I32, D]),
                 "moe_layer_forward": (I32, [P, I32, I32, I32, I32, F32, P, P, P, D, P, P, P, P, SZ, P, P]),
+                "moe_layer_forward_static": (I32, [P, I32, I32, I32, I32, F32, P, P, P, D, P, P, P, P, P]),
                 "moe_pass_table_host": (I32, [P, I32, I32, I32, I32, P]),
                 "moe_prefill_sort": (I32, [P, I32, P, I32, I32, D, P, SZ, P, P]),
                 "moe_prefill_pass": (I32, [I32, I32, I32, I32, I32, P, P, D, P, SZ, P, P]),
@@ -388,6 +389,37 @@ def moe_prefill_combine(topk_w, E: int, desc: SizeClassDesc, ws, out=None, strea
                                      ctypes.byref(desc), _dev_ptr(out, torch.bfloat16, "out", 2),
                                      _dev_ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)))
     return out
+
+
+MOE_STATIC_SCRATCH_BYTES = 8 << 20
+
+
+def moe_layer_forward_static(logits, x, slot_table, slot_pool, desc: SizeClassDesc, k: int,
+                             mode: int = MOE_ROUTE_PLAIN, L: float = 0.0, topk_ids=None, topk_w=None,
+                             out=None, err_word=None, stream=None):
+    """moe_layer_forward on the library's own scratch (no workspace argument; the
+    library allocates nothing).  Returns (out, topk_ids, topk_w)."""
+    torch = _torch()
+    T, E = logits.shape
+    H = x.shape[1]
+    if H != desc.H:
+        raise ValueError(f"x has {H} columns, size class has H={desc.H}")
+    if slot_pool.numel() < desc.n_slots * desc.slot_bytes:
+        raise ValueError("slot_pool smaller than n_slots * slot_bytes")
+    dev = x.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _check(lib().moe_layer_forward_static(
+        _dev_ptr(logits, torch.float32, "logits", 2), T, E, k, mode, L, _dev_ptr(x, torch.bfloat16, "x", 2),
+        _dev_ptr(slot_table, torch.int32, "slot_table", 1), _dev_ptr(slot_pool, torch.uint8, "slot_pool"),
+        ctypes.byref(desc), _dev_ptr(topk_ids, torch.int32, "topk_ids", 2),
+        _dev_ptr(topk_w, torch.float32, "topk_w", 2), _dev_ptr(out, torch.bfloat16, "out", 2),
+        _opt_ptr(err_word, torch.int32, "err_word"), _stream(stream)))
+    return out, topk_ids, topk_w
 
 
 def moe_cache_install(slot_pool, desc: SizeClassDesc, slot: int, src, stream=None, event=None):

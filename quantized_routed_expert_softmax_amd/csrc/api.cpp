@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -137,6 +138,52 @@ int check_fwd(int T, int k, int E, const moe_size_class_desc* d, const void* ws,
     if (!ws || !aligned(ws, 256)) return fail(MOE_E_INVALID, "ws must be a 256-byte aligned buffer");
     if (ws_bytes < L->total)
         return fail(MOE_E_WORKSPACE, "forward workspace %zu bytes < %zu", ws_bytes, L->total);
+    return MOE_OK;
+}
+
+}  // namespace
+
+// ---- the library-owned scratch of moe_layer_forward_static ------------------
+// One array per GPU the library runs on, held until the process ends.  Host code
+// never uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress once per device and is kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+__global__ void zero_dwords_kernel(uint32_t* __restrict__ p, size_t n)
+{
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// Device address of the current device's scratch; the first call on a device
+// looks it up and clears its reserved prefix (the fused decode kernel's call-tag
+// counters and tagged h words) with a fill kernel on `stream`.
+int static_scratch(hipStream_t stream, void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_E_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr || (uintptr_t)ptr % 256) return fail(MOE_E_HIP, "scratch has no 256-byte aligned device address");
+        const size_t n = MOE_WS_RESERVED_BYTES / 4;
+        hipLaunchKernelGGL(zero_dwords_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           (uint32_t*)ptr, n);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "scratch clear launch");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
     return MOE_OK;
 }
 
@@ -356,6 +403,27 @@ int moe_layer_forward(const float* logits, int T, int E, int k, int mode, float 
         return rc;
     return moe_experts_forward_ex(x, T, topk_ids, topk_w, k, E, slot_table, slot_pool, d, out, ws,
                                   ws_bytes, err_word, MOE_PATH_AUTO, stream);
+}
+
+int moe_layer_forward_static(const float* logits, int T, int E, int k, int mode, float L, const void* x,
+                             const int32_t* slot_table, const void* slot_pool,
+                             const moe_size_class_desc* d, int32_t* topk_ids, float* topk_w, void* out,
+                             uint32_t* err_word, hipStream_t stream)
+{
+    if (int rc = check_desc(d)) return rc;
+    if (T < 0) return fail(MOE_E_INVALID, "T < 0");
+    if (E < 1 || E > 1024) return fail(MOE_E_INVALID, "E must be in [1, 1024] (got %d)", E);
+    if (k < 1 || k > E || k > 32) return fail(MOE_E_INVALID, "k must be in [1, min(E, 32)] (got %d)", k);
+    if ((int64_t)T * k > (int64_t)1 << 26) return fail(MOE_E_INVALID, "T*k too large");
+    const size_t need = fwd_layout(T, k, E, d).total;
+    if (need > (size_t)MOE_STATIC_SCRATCH_BYTES)
+        return fail(MOE_E_WORKSPACE, "this layer needs %zu bytes of scratch, more than the library's %zu",
+                    need, (size_t)MOE_STATIC_SCRATCH_BYTES);
+    if (T == 0) return MOE_OK;
+    void* ws = nullptr;
+    if (int rc = static_scratch(stream, &ws)) return rc;
+    return moe_layer_forward(logits, T, E, k, mode, L, x, slot_table, slot_pool, d, topk_ids, topk_w, out,
+                             ws, (size_t)MOE_STATIC_SCRATCH_BYTES, err_word, stream);
 }
 
 int moe_experts_forward(const void* x, int T, const int32_t* topk_ids, const float* topk_w, int k,
