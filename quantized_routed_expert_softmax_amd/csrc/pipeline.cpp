@@ -233,6 +233,7 @@ struct Staging {
 struct SlotState {
     int use_ev = -1;       // use-ring entry of the last release that covered the slot
     int fill_ev = -1;      // fill-ring entry of the slot's last install
+    uint64_t fill_seq = 0; // order in which that install's copy was enqueued
     bool pending = false;  // install accepted, copy not yet enqueued
     bool failed = false;   // the store read of the last install failed
 };
@@ -284,6 +285,10 @@ struct moe_pipeline {
     int32_t* table_host = nullptr;  // pinned [kTableRing][E]
     int64_t fill_next[kMaxCopyStreams] = {};
     int64_t use_next = 0, table_next = 0;
+    uint64_t fill_count = 0;            // installs enqueued so far (fill_seq source)
+    uint64_t use_gen[kUseRing] = {};    // records made of each use-ring entry
+    int last_wait[kMaxCopyStreams] = {-1, -1, -1, -1};  // use-ring entry a copy stream last waited for ...
+    uint64_t last_wait_gen[kMaxCopyStreams] = {};  // ... and which record of it
 
     mutable std::mutex mu;  // everything above that threads share
     std::mutex copy_mu[kMaxCopyStreams];  // per copy stream: enqueue + fill-ring record
@@ -315,7 +320,16 @@ struct moe_pipeline {
     {
         std::lock_guard<std::mutex> g(copy_mu[q]);
         const hipStream_t st = copies[(size_t)q];
-        if (use_ev >= 0 && hipStreamWaitEvent(st, use_ring[use_ev], 0) != hipSuccess) return -1;
+        // a stream that already waits for this record of the use event (installs
+        // of one layer or pass share their victims' release) need not wait again
+        if (use_ev >= 0) {
+            const uint64_t gen = __atomic_load_n(&use_gen[use_ev], __ATOMIC_ACQUIRE);
+            if (last_wait[q] != use_ev || last_wait_gen[q] != gen) {
+                if (hipStreamWaitEvent(st, use_ring[use_ev], 0) != hipSuccess) return -1;
+                last_wait[q] = use_ev;
+                last_wait_gen[q] = gen;
+            }
+        }
         if (hipMemcpyAsync(slot_ptr(cls, s), src, (size_t)desc[cls].slot_bytes, hipMemcpyHostToDevice,
                            st) != hipSuccess)
             return -1;
@@ -374,6 +388,7 @@ struct moe_pipeline {
         ss.pending = false;
         ss.failed = ev < 0;
         ss.fill_ev = ev;
+        ss.fill_seq = ++fill_count;
         if (ev >= 0) {
             moe_cache_fill_done(cache, layer, expert, fill_ring[ev]);
         } else {
@@ -526,6 +541,37 @@ struct moe_pipeline {
         if (install_from_host(lk, layer, expert, cls, s, use_ev)) return;
         jobs.push_back(Job{kInstall, layer, expert, cls, s, use_ev, guess, -1});
         cv_jobs.notify_one();
+    }
+
+    // Every unpinned slot of class cls is being filled: wait for the oldest fill
+    // still in flight (the copies queued behind it keep the copy engines busy),
+    // or for a queued store read.  Caller holds mu (released while waiting).
+    // False when nothing of the class is in flight.
+    bool wait_oldest_fill(std::unique_lock<std::mutex>& lk, int cls)
+    {
+        int64_t best = -1;
+        bool pending = false;
+        for (size_t i = 0; i < slot[cls].size(); ++i) {
+            const SlotState& ss = slot[cls][i];
+            if (ss.pending) {
+                pending = true;
+                continue;
+            }
+            if (ss.fill_ev < 0 || event_done(fill_ring[ss.fill_ev])) continue;
+            if (best < 0 || ss.fill_seq < slot[cls][(size_t)best].fill_seq) best = (int64_t)i;
+        }
+        if (best >= 0) {
+            const hipEvent_t e = fill_ring[slot[cls][(size_t)best].fill_ev];
+            lk.unlock();
+            hipEventSynchronize(e);
+            lk.lock();
+            return true;
+        }
+        if (pending) {
+            cv_done.wait(lk);
+            return true;
+        }
+        return false;
     }
 
     void wait_idle(std::unique_lock<std::mutex>& lk)
@@ -761,18 +807,10 @@ int moe_pipeline_prepare(moe_pipeline* p, int layer, const int32_t* ids, int n, 
         int64_t s = -1;
         int needs_fill = 0;
         int rc = moe_cache_acquire(p->cache, layer, e, &s, &needs_fill);
-        if (rc == MOE_E_NO_SLOT) {
-            // installs still in flight (guesses among them) may hold every unpinned
-            // slot: let every enqueued read and copy finish, then try once more
-            lk.unlock();
-            {
-                std::unique_lock<std::mutex> l2(p->mu);
-                p->wait_idle(l2);
-            }
-            p->sync_copies();
-            lk.lock();
+        // installs still in flight (earlier passes' or guesses') may hold every
+        // unpinned slot: wait for them one at a time, oldest first
+        while (rc == MOE_E_NO_SLOT && p->wait_oldest_fill(lk, cls))
             rc = moe_cache_acquire(p->cache, layer, e, &s, &needs_fill);
-        }
         if (rc != MOE_OK && rc != MOE_E_BUSY) {
             lk.unlock();
             p->unpin_all(layer);
@@ -844,6 +882,9 @@ int moe_pipeline_release(moe_pipeline* p, int layer, hipStream_t compute)
         p->unpin_all(layer);
         return pfail(MOE_E_HIP, "moe_pipeline_release: event record failed");
     }
+    // counted after the record: a copy stream that saw this count has waited for
+    // this record or a later one
+    __atomic_add_fetch(&p->use_gen[u], 1, __ATOMIC_RELEASE);
     {
         std::lock_guard<std::mutex> g(p->mu);
         const int cls = p->cls_of(layer);
