@@ -251,7 +251,8 @@ int    moe_pass_table_size(int E, int pass_experts);
  *              MOE_ERRW_TIMEOUT.
  * `path` selects the kernels (MOE_PATH_*); moe_experts_forward uses AUTO: the
  * fused one-launch decode kernel when T*k <= 64 and the shape has a compiled
- * variant, the GEMV kernels for other small batches, MFMA otherwise.
+ * variant that fits the device's LDS, the three-launch GEMV kernels for other
+ * batches of at most 8 pairs, MFMA otherwise.
  * Sources: [HF-PR] PR description (experts run through gather_qmm on the cache);
  * [RFC] "How the prototype works" (Cache, Prefill and Quantized experts bullets).
  */

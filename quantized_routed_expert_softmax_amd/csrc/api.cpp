@@ -329,7 +329,15 @@ int moe_experts_forward_ex(const void* x, int T, const int32_t* topk_ids, const 
     const bool gemv_ok = moe::gemv_supported(T, k, c);
     if ((path == MOE_PATH_GEMV || path == MOE_PATH_GEMV3) && !gemv_ok)
         return fail(MOE_E_UNSUPPORTED, "GEMV path supports T <= 64 and H/32, I/32 with an odd part <= 4");
-    if (path == MOE_PATH_AUTO) path = (gemv_ok && (int64_t)T * k <= 128) ? MOE_PATH_GEMV : MOE_PATH_MFMA;
+    if (path == MOE_PATH_AUTO) {
+        // the one-launch decode kernel when it takes the shape; otherwise the
+        // three-launch GEMV only for a handful of pairs (measured: 8 pairs of the
+        // mixed layer 28 us GEMV vs 38 us MFMA, 16 pairs 48 vs 43, 64 pairs 155
+        // vs 72), the MFMA path above that
+        if (gemv_ok && (moe::decode1_supported(T, k, E, MOE_ROUTE_PLAIN, false, c) || moe::decode_fused_supported(T, k, E, c)))
+            path = MOE_PATH_GEMV;
+        else path = (gemv_ok && (int64_t)T * k <= 8) ? MOE_PATH_GEMV : MOE_PATH_MFMA;
+    }
 
     char* w = (char*)ws;
     int32_t* offsets = (int32_t*)(w + L.offsets);
@@ -338,6 +346,12 @@ int moe_experts_forward_ex(const void* x, int T, const int32_t* topk_ids, const 
     uint16_t* hbuf = (uint16_t*)(w + L.hbuf);
     const uint8_t* pool = (const uint8_t*)slot_pool;
     hipError_t e;
+    if (path == MOE_PATH_GEMV && moe::decode1_supported(T, k, E, MOE_ROUTE_PLAIN, false, c)) {
+        e = moe::launch_decode1(nullptr, topk_ids, topk_w, nullptr, nullptr, E, k, (const uint16_t*)x, slot_table,
+                                pool, c, (uint16_t*)out, w + L.reserved, err_word, stream);
+        if (e != hipSuccess) return hip_fail(e, "one-token decode launch");
+        return MOE_OK;
+    }
     if (path == MOE_PATH_GEMV && moe::decode_fused_supported(T, k, E, c)) {
         e = moe::launch_decode_fused(nullptr, MOE_ROUTE_PLAIN, 0.0f, topk_ids, topk_w, nullptr,
                                      nullptr, T, E, k, (const uint16_t*)x, slot_table, pool, c,
@@ -390,6 +404,13 @@ int moe_layer_forward(const float* logits, int T, int E, int k, int mode, float 
     const FwdLayout Lw = fwd_layout(T, k, E, d);
     if (ws_bytes < Lw.total) return fail(MOE_E_WORKSPACE, "forward workspace %zu bytes < %zu", ws_bytes, Lw.total);
     const moe::ClassView c = view_of(d);
+    if (moe::decode1_supported(T, k, E, mode, true, c)) {
+        hipError_t e = moe::launch_decode1(logits, nullptr, nullptr, topk_ids, topk_w, E, k, (const uint16_t*)x,
+                                           slot_table, (const uint8_t*)slot_pool, c, (uint16_t*)out,
+                                           (char*)ws + Lw.reserved, err_word, stream);
+        if (e != hipSuccess) return hip_fail(e, "one-token decode launch");
+        return MOE_OK;
+    }
     // in-kernel routing covers E <= 512; larger E routes with the router kernel first
     if (E <= 512 && moe::decode_fused_supported(T, k, E, c)) {
         char* w = (char*)ws;

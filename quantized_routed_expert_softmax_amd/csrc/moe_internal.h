@@ -13,6 +13,11 @@ namespace moe {
 // from_pretrained", How the prototype works, Prefill bullet).
 constexpr int kPassExperts = 64;
 
+// Reserved workspace region of the one-launch decode kernels: call-tag counter of
+// workgroup slot b at dword kGenBase + b (b < kMaxGrid), then the tagged h words.
+constexpr int kMaxGrid = 1024;
+constexpr int kGenBase = 64;
+
 // Record `msg` as this thread's moe_last_error() text; returns `code`.
 int set_error(int code, const char* msg);
 
@@ -60,6 +65,15 @@ hipError_t launch_decode_fused(const float* logits, int mode, float L, const int
                                int k, const uint16_t* x, const int32_t* table, const uint8_t* pool,
                                const ClassView& c, uint16_t* out, void* reserved, uint32_t* err,
                                hipStream_t s);
+
+// Decode path for one token: a leaner one-launch kernel (every wave routes in
+// registers, all weight rows are requested at once, each wave stages only its
+// own experts' h).  Plain routing only (logits != null) or given ids / weights.
+bool decode1_supported(int T, int k, int E, int mode, bool routes, const ClassView& c);
+hipError_t launch_decode1(const float* logits, const int32_t* ids_in, const float* w_in, int32_t* ids_out,
+                          float* w_out, int E, int k, const uint16_t* x, const int32_t* table,
+                          const uint8_t* pool, const ClassView& c, uint16_t* out, void* reserved,
+                          uint32_t* err, hipStream_t s);
 
 // Prefill path: P16-permuted x, MFMA gate/up + SwiGLU, MFMA down (y in bf16),
 // combine (fp32 sum in j order).

@@ -752,6 +752,22 @@ __device__ __forceinline__ int route_sel_list(int wave, int E)
 // thread's logit, expert 64 * route_sel_list + lane); wave zw computes m and Z
 // from v[j] = logit of expert lane + 64j (entries past E ignored).  No barrier
 // inside.
+// Z of the routing contract from v[j] = logit of expert lane + 64j (entries at
+// or past E ignored) and the largest logit m.  (A non-finite logit makes the
+// token's result be discarded, so the branch-free exp may see only finite values
+// that matter; -inf gives 0.)
+__device__ __forceinline__ float route_sel_z(const float (&v)[8], int E, float m)
+{
+    const int lane = threadIdx.x & 63;
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = lane + 64 * j < E ? exp_contract_nb(v[j] - m) : 0.0f;
+    float S = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) S = S + e[j];
+    return tree_sum_lane0(S);
+}
+
 template <int W>
 __device__ __forceinline__ void route_sel_lists(float own, const float (&v_in)[8], int E, RouteSelScratch* rs,
                                                 int par, float& m, float& Z)
@@ -779,15 +795,7 @@ __device__ __forceinline__ void route_sel_lists(float own, const float (&v_in)[8
         for (int j = 0; j < 8; ++j) v[j] = lane + 64 * j < E ? v_in[j] : -INFINITY;
         m = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
         m = wave_max_f(m);
-        // (a non-finite logit makes the token's result be discarded, so the
-        // branch-free exp may see only finite values that matter; -inf gives 0)
-        float e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = lane + 64 * j < E ? exp_contract_nb(v[j] - m) : 0.0f;
-        float S = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) S = S + e[j];
-        Z = tree_sum_lane0(S);
+        Z = route_sel_z(v, E, m);
     }
 }
 

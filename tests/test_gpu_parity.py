@@ -542,8 +542,8 @@ def test_layer_forward_matches_route_plus_forward(shape):
     assert np.array_equal(w.cpu().numpy().view(np.uint32), w_o.view(np.uint32))
     ref = oracle.layer(pr.x, ids_o, w_o, pr.table, pr.pool, H, I, bg, bd, E, threads=THREADS)
     check_close(out, ref, f"layer_forward {shape}")
-    # identical to the two-call form on the fused kernel
-    out2, _ = run_forward(pr, ids_o, w_o, B.MOE_PATH_GEMV)
+    # identical to the two-call form (route, then the experts on the AUTO path)
+    out2, _ = run_forward(pr, ids_o, w_o, B.MOE_PATH_AUTO)
     assert np.array_equal(out.view(torch.int16).cpu().numpy(), out2.view(torch.int16).cpu().numpy())
 
 
