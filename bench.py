@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the routed-expert MoE layer on one MI355X.
 
-Workload (the headline): decode of a 48-layer MoE with 512 experts per layer,
+Workload (the headline): decode through 48 MoE layers of 512 experts each,
 hidden 2048, expert intermediate 512, top-10, 3-bit group-64 experts, batch 1,
 a 2048-slot pool per layer with a random expert -> slot table, router logits
 N(0,1) plus a per-expert Zipf(1.1) bias.  One step = one decode token through
@@ -71,11 +71,12 @@ def parse():
 
 # Sources of the fused decode kernel; the measured HBM traffic recorded in the
 # profile summary below holds only while their hash matches.
-DECODE_SOURCES = ["quantized_routed_expert_softmax_amd/csrc/decode.hip",
+DECODE_SOURCES = ["quantized_routed_expert_softmax_amd/csrc/decode1.hip",
+                  "quantized_routed_expert_softmax_amd/csrc/decode_dev.h",
                   "quantized_routed_expert_softmax_amd/csrc/route_dev.h",
                   "quantized_routed_expert_softmax_amd/csrc/moe_dev.h",
                   "include/moe.h"]
-TRAFFIC_SUMMARY = "profiles/decode_layer_kernel_3_3_1_1-decode48.md"
+TRAFFIC_SUMMARY = "profiles/decode1_kernel_3_3_16_1_10-decode48.md"
 
 
 def decode_sources_sha256():
@@ -719,7 +720,8 @@ def mixed_lines(torch, B, mb, synth, dev, err, steps):
     res["workload"] = ("mixed: 48 layers x (hidden 2048, 128 experts, intermediate 768, top-8), 4-bit "
                        "experts, 6-bit down on layers l % 4 == 3 (two size classes: 2654208 and 3047424 B), "
                        "every expert resident, pre-norm residual chain, one HIP graph per step")
-    res["kernel"] = "decode_layer_kernel (moe_layer_forward, one launch per layer)"
+    res["kernel"] = ("moe_layer_forward, one launch per layer: batch 1 decode1_kernel<4,4,16,1,10> on the "
+                     "4-bit layers and decode_layer_kernel on the 4/6-bit layers; batch 8 routing + MFMA passes")
     res["frac_basis"] = "distinct routed experts' bytes per step / the 48 layer launches' time (graph of layer launches only)"
     return res
 
@@ -1035,7 +1037,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "decode_layer_kernel<3,3,1,1> (moe_layer_forward: route + sort + "
+                     "kernel": "decode1_kernel<3,3,16,1,10> (moe_layer_forward: route + hit list + "
                                "gate/up + SwiGLU + down + combine, one launch per layer)",
                      "avg_launch_us": round(fwd_ms_avg * 1000.0, 3),
                      "bytes_per_launch": int(bytes_per_launch)},

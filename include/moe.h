@@ -146,8 +146,8 @@ extern "C" {
 
 /*
  * Size class: every expert whose row has the same byte size shares one pool of
- * slots and one LRU ([CLASS] PR description: layers are grouped by the bytes one
- * expert needs, and each group has its own slots and LRU).  Filled by
+ * slots and one LRU ([CLASS] PR description: layers whose experts take the same
+ * number of bytes form a class, and a class owns a separate slot pool and LRU).  Filled by
  * moe_size_class_init; all offsets are bytes from the start of a slot row.
  */
 typedef struct moe_size_class_desc {
@@ -168,8 +168,9 @@ typedef struct moe_size_class_desc {
 /*
  * Fill `d` for an expert of the given shape and code widths.  group must be 64
  * and align 256 in this version.  Returns MOE_E_INVALID on bad arguments.
- * Source: [RFC] "How the prototype works" (one contiguous row per expert) and
- * [CLASS] PR description (bytes one expert needs = sum of its aligned windows).
+ * Source: [RFC] "How the prototype works" (each expert stored as a single
+ * unbroken row) and [CLASS] PR description (an expert's size is the total of its
+ * tensors' windows, each padded to the alignment).
  */
 int moe_size_class_init(moe_size_class_desc* d, int H, int I, int bits_gu, int bits_d,
                         int group, int align, int64_t n_slots);
@@ -181,8 +182,9 @@ int moe_size_class_init(moe_size_class_desc* d, int H, int I, int bits_gu, int b
  * logits: fp32 [n_mats, T, E] (device), fp32 sums of exact bf16 products.
  * These logits feed moe_route_topk to guess the experts the next layers will
  * ask for, before their hidden states exist.  Source: [RFC] "How the prototype
- * works", Reads bullet (the next two layers' experts are guessed by running
- * their routers on the current hidden states and read in the background).
+ * works", Reads bullet (the prediction for the two following layers applies
+ * their router weights to the present layer's hidden state, and the predicted
+ * experts are fetched while compute goes on).
  * Limits: H a positive multiple of 8, 1 <= E <= 1024, 1 <= n_mats <= 8, x and w
  * 16-byte aligned; T = 0 is a no-op.  Sized for decode batches (each four tokens
  * re-read the routers, from L2).
@@ -221,8 +223,8 @@ int moe_route_topk(const float* logits, int T, int E, int k, int mode, float L,
  *                  pass_experts (P) each; unused starts equal n_hit.
  *   ws             device scratch of moe_sort_workspace_size(T, k, E) bytes.
  *   err_word       MOE_ERRW_BAD_ID if an id is outside [0, E); such pairs are dropped.
- * Sources: [HF-PR] commit messages (sorted prefill runs 64 experts at a time);
- * [RFC] "How the prototype works", Prefill bullet (sorted gather in groups of 64).
+ * Sources: [HF-PR] commit messages (the sorted prefill's batches of 64 experts);
+ * [RFC] "How the prototype works", Prefill bullet (sorted gather, 64 experts per batch).
  */
 int moe_sort_by_expert(const int32_t* topk_ids, int T, int k, int E, int pass_experts,
                        int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pass_table,
@@ -249,11 +251,22 @@ int    moe_pass_table_size(int E, int pass_experts);
  *              in time (same stream, or ordered by events).
  *   err_word   MOE_ERRW_NOT_RESIDENT / MOE_ERRW_BAD_SLOT / MOE_ERRW_BAD_ID /
  *              MOE_ERRW_TIMEOUT.
- * `path` selects the kernels (MOE_PATH_*); moe_experts_forward uses AUTO: the
- * fused one-launch decode kernel when T*k <= 64 and the shape has a compiled
- * variant that fits the device's LDS, the three-launch GEMV kernels for other
- * batches of at most 8 pairs, MFMA otherwise.
- * Sources: [HF-PR] PR description (experts run through gather_qmm on the cache);
+ * `path` selects the kernels (MOE_PATH_*); moe_experts_forward uses AUTO: a
+ * one-launch decode kernel when the batch is one token (or T*k <= 64) and the
+ * shape has a compiled variant that fits the device's LDS, the three-launch GEMV
+ * kernels for other batches of at most 8 pairs, MFMA otherwise.
+ * Co-residency precondition of the one-launch kernels (AUTO / GEMV at decode
+ * sizes, and moe_layer_forward): their workgroups hand the SwiGLU activations to
+ * one another through the workspace inside the launch, so every workgroup of the
+ * grid must be running at the same time.  The grid is sized to at most one
+ * workgroup per compute unit and the host checks that the kernel's resources
+ * allow it, but a kernel on another stream or in another process that holds
+ * compute units for long can keep a workgroup from starting.  Every wait is
+ * bounded: when one expires the kernel sets MOE_ERRW_TIMEOUT, still ends, and
+ * the contents of `out` are unspecified (routing results written by
+ * moe_layer_forward are still exact).  MOE_PATH_GEMV3 and MOE_PATH_MFMA have no
+ * waits between workgroups and no such precondition.
+ * Sources: [HF-PR] PR description (the cached experts go through a gathered quantized matmul);
  * [RFC] "How the prototype works" (Cache, Prefill and Quantized experts bullets).
  */
 int moe_experts_forward(const void* x, int T, const int32_t* topk_ids, const float* topk_w,
@@ -309,7 +322,7 @@ int moe_layer_forward_static(const float* logits, int T, int E, int k, int mode,
  * experts run, in ascending id, in passes of at most 64, so that only one pass's
  * experts need to be resident at a time and the cache can be smaller than a
  * layer ([RFC] "How the prototype works", Prefill bullet; [HF-PR] commit
- * messages: sorted prefill, 64 experts at a time).  One layer is:
+ * messages: the sorted prefill's batches of 64 experts).  One layer is:
  *   moe_prefill_sort    once: the stable sort of the T*k pairs by expert and the
  *                       pass table (the layout of moe_sort_by_expert, P = 64) plus
  *                       a permuted copy of x, all into ws;
@@ -352,8 +365,8 @@ int moe_prefill_combine(int T, int k, int E, const float* topk_w, const moe_size
  * src_kind: MOE_SRC_HOST (pinned host memory) or MOE_SRC_DEVICE.  The copy is
  * asynchronous; the slot must not be read until `done` has completed (wait on it
  * from the compute stream).  Source: [RFC] "How the prototype works", Reads
- * bullet (one contiguous read and one non-blocking host-to-device copy per
- * expert); [HF-PR] host-tier commit message.
+ * bullet (a miss is a single read of the expert's row followed by a single
+ * asynchronous copy to the device); [HF-PR] host-tier commit message.
  */
 int moe_cache_install(void* slot_pool, const moe_size_class_desc* d, int64_t slot,
                       const void* src, int src_kind, hipStream_t copy_stream, hipEvent_t done);
@@ -361,10 +374,11 @@ int moe_cache_install(void* slot_pool, const moe_size_class_desc* d, int64_t slo
 /*
  * Host-side bounded expert cache: size classes, one LRU per class, per-layer
  * expert -> slot tables.  Source: [RFC] "How the prototype works", Cache bullet
- * (preallocated pool of slots, LRU, per-layer expert -> slot table on the host);
- * [CLASS] PR description and constructor (slots of a class are contiguous, slot
- * byte offsets are running sums, empty slots sit at the LRU's back and are taken
- * first; each class has its own LRU and budget never moves between classes).
+ * (a fixed pool of slots allocated up front, LRU eviction, each layer's map from
+ * expert to slot held on the host); [CLASS] PR description and constructor (a
+ * class's slots are adjacent, slot byte offsets accumulate, unused slots are
+ * queued at the LRU's tail so they are handed out before any eviction; every
+ * class evicts on its own and no class borrows another's budget).
  *
  * moe_cache_create: classes[n_classes] (n_slots of each is that class's budget);
  *   layer_class[n_layers] maps each layer to its class; E experts per layer.
@@ -392,7 +406,7 @@ moe_cache* moe_cache_create(const moe_size_class_desc* classes, int n_classes,
 /*
  * Eviction variants.  Sources: [RFC] "How the prototype works", Cache bullet (LRU,
  * optional LFU); [CLASS] PR description (one LRU per class, or one per layer with
- * --per-layer; every layer keeps the same share).
+ * --per-layer; each layer gets an equal fraction).
  * policy MOE_EVICT_LRU: the least recently used candidate goes.  MOE_EVICT_LFU:
  *   the candidate with the fewest acquires since it took its expert goes, ties to
  *   the least recently used.  A candidate is neither pinned nor in flight; empty
@@ -424,7 +438,7 @@ int  moe_cache_class_of(const moe_cache* c, int layer);
  * moe_cache_class_desc: copy of class `cls`'s descriptor.
  * moe_cache_class_stats: hits, misses, evictions of one class since creation;
  *   the per-class hit rate the size-class design reports ([CLASS] PR description:
- *   each class has its own slots and LRU, the measured replay gives its hit rate).
+ *   the hit rate is given per class, since each class evicts on its own).
  * moe_cache_abort_fill: drop an entry whose fill failed: it becomes absent and its
  *   slot empty at the LRU's back.  MOE_E_BUSY while the entry is pinned.
  */
@@ -439,9 +453,9 @@ int  moe_cache_abort_fill(moe_cache* c, int layer, int expert);
  * per (layer, expert) in the slot byte format, layer-major: the row of (l, e)
  * starts at base(l) + e * slot_bytes(class(l)), base(l) = sum over l' < l of
  * E * slot_bytes(class(l')).  Sources: [RFC] "How the prototype works", Quantized
- * experts bullet (a one-time conversion writes one contiguous row per expert) and
- * Reads bullet (one contiguous read per expert); [HF-PR] commit message (reads go
- * through one descriptor per shard).
+ * experts bullet (an offline conversion stores each expert as a single unbroken
+ * row) and Reads bullet (a miss is one read of that row); [HF-PR] commit message
+ * (one open file per shard serves every read).
  *
  * moe_store_open_file: a file at `path`, opened once read-only; every reader
  *   shares the descriptor (positioned reads).  It must hold at least
@@ -463,18 +477,18 @@ int     moe_store_read(const moe_store* s, int layer, int expert, void* dst);
 
 /*
  * Miss pipeline: fills a moe_cache's device pools from a moe_store, through an
- * optional tier of expert rows in pinned host memory.
- * Sources: [RFC] "How the prototype works", Reads bullet (each layer brings its
- * routing to the host once; misses are read on I/O threads into recycled pinned
- * buffers, one contiguous read and one non-blocking host-to-device copy per
- * expert; the next layers' experts are guessed and read in the background) and
- * Host tier bullet (pinned rows between storage and the device cache, so a device
- * miss costs one host-to-device copy; optional preload at load time); [HF-PR]
- * host-tier commit message (rows handed out stay reserved until the copy that
- * reads them has run) and mps_commit commit message (guessed reads still in
- * flight are skipped, never waited for); [RFC] Cache bullet (when every expert is
- * resident no layer waits for the host); [CLASS] PR description (every layer
- * keeps the same share).
+ * optional pinned-host copy of expert rows.
+ * Sources: [RFC] "How the prototype works", Reads bullet (the routing of a
+ * layer travels to the host once; worker threads fetch each missing expert
+ * with one read into a reused pinned staging buffer, then one asynchronous copy
+ * moves it to the device; predicted experts of later layers are fetched ahead)
+ * and Host tier bullet (a pinned host level under the device cache turns a
+ * device miss into just a host-to-device copy; it can be filled at load time);
+ * [HF-PR] host-tier commit message (a host row is not reused before the copy
+ * reading it has finished) and mps_commit commit message (a predicted read that
+ * has not landed is bypassed rather than awaited); [RFC] Cache bullet (a fully
+ * resident model never makes a layer wait on the host); [CLASS] PR description
+ * (each layer gets an equal fraction of its experts).
  *
  * moe_pipeline_config:
  *   host_tier_bytes  pinned host bytes for expert rows (0 = no host tier), split
@@ -484,7 +498,7 @@ int     moe_store_read(const moe_store* s, int layer, int expert, void* dst);
  *                    (layers ascending, experts ascending, until each class's rows
  *                    are full).
  *   io_threads       store readers, 1..64.
- *   staging_rows     recycled pinned buffers (largest row each) for store reads
+ *   staging_rows     reused pinned staging buffers (largest row each) for store reads
  *                    that do not land in a host row; io_threads..1024.
  *
  * moe_pipeline_create: `class_pools[c]` is class c's device pool (n_slots rows of

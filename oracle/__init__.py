@@ -115,7 +115,7 @@ def pass_table_size(E: int, P: int) -> int:
 
 def sort(ids: np.ndarray, E: int, P: int = 64):
     """Stable sort of pair ids by expert and the pass table ("POC: Experts
-    offload", commit messages: sorted prefill, 64 experts at a time)."""
+    offload", commit messages: the sorted prefill's batches of 64 experts)."""
     a = np.ascontiguousarray(ids, dtype=np.int32)
     T, k = a.shape
     off = np.empty(E + 1, dtype=np.int32)
@@ -171,8 +171,8 @@ def layer(x_bf16: np.ndarray, ids: np.ndarray, w: np.ndarray, slot_table: np.nda
 def router_logits(x_bf16: np.ndarray, w_bf16: np.ndarray) -> np.ndarray:
     """Router logits of consecutive layers on one set of hidden states, fp64:
     logits[m, t, e] = sum_i x[t, i] * Wr_m[e, i] ("RFC ...", How the prototype
-    works, Reads: the next layers' routers run on the current hidden states to
-    guess their experts).  x: bf16 bits [T, H]; w: bf16 bits [n, E, H]."""
+    works, Reads: applying the following layers' routers to the present hidden
+    state predicts their experts).  x: bf16 bits [T, H]; w: bf16 bits [n, E, H]."""
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
     w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
     T, H = x.shape

@@ -15,20 +15,20 @@
  *    a Taylor polynomial) and summation order, so ids and weights are comparable
  *    bit for bit.
  *  - Cache-aware substitution (BigMoeOnEdge commit message adding it, after
- *    Skliar et al.): before the routing is committed every cached expert's score
- *    is raised by L times the token's score range and top-k is taken again; the
- *    same number of experts runs.
+ *    Skliar et al.): each cached expert's score gains L x (max - min of the
+ *    token's scores) and the k winners are picked again from the adjusted
+ *    scores; k experts still run.
  *  - Sort by expert and passes of at most 64 hit experts ("POC: Experts
- *    offload", commit messages: sorted prefill runs 64 experts at a time; RFC,
- *    How the prototype works, Prefill).
+ *    offload", commit messages: the sorted prefill handles the hit experts in
+ *    batches of 64; RFC, How the prototype works, Prefill).
  *  - Router logits for the lookahead guesses ("RFC ...", How the prototype
- *    works, Reads: the next two layers' experts are guessed by running their
- *    routers on the current hidden states): logits[m][t][e] = sum_i x[t][i] *
+ *    works, Reads: the two following layers' routers are applied to the present
+ *    hidden state to predict their experts): logits[m][t][e] = sum_i x[t][i] *
  *    Wr_m[e][i] in fp64 over the bf16 values, a plain linear map per layer.
  *  - The layer ("RFC ...", How the prototype works: experts are gated,
  *    concatenated, untransposed and without bias, run on the slot pool through a
- *    per-layer expert -> slot table; quantized experts in a group-wise affine
- *    format, one contiguous row per expert):
+ *    map from expert id to slot for each layer; quantized experts in a
+ *    group-wise affine format, each expert a single unbroken row):
  *        out[t] = sum_j w[t,j] * Wd_e (silu(Wg_e x_t) * (Wu_e x_t)),  e = ids[t,j]
  *    written out directly in fp64 with plain loops.  Dequantization s*q + z is
  *    exact in fp64.

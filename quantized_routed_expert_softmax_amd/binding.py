@@ -290,7 +290,7 @@ def moe_experts_forward(x, topk_ids, topk_w, E: int, slot_table, slot_pool, desc
         raise ValueError("slot_pool smaller than n_slots * slot_bytes")
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
-    if ws is None:  # zero-filled: the first 256 bytes must start at zero
+    if ws is None:  # zero-filled: the first MOE_WS_RESERVED_BYTES must start at zero
         ws = torch.zeros(max(moe_forward_workspace_size(T, k, E, desc), 256), dtype=torch.uint8,
                          device=x.device)
     _check(lib().moe_experts_forward_ex(

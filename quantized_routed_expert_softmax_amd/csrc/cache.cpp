@@ -3,16 +3,17 @@
 // slots whose fill is in flight.
 //
 // Sources: "RFC: stream MoE experts from disk in from_pretrained", How the
-// prototype works, Cache (one preallocated pool of expert slots, LRU, per-layer
-// expert -> slot table kept on the host) and Reads (misses filled by one
-// non-blocking host-to-device copy per expert); "POC: Experts offload", host-tier
-// commit message (rows stay reserved until the copy that reads them has run);
+// prototype works, Cache (a fixed pool of expert slots allocated up front, LRU
+// eviction, the host holds each layer's map from expert to slot) and Reads (a
+// miss lands in its slot through a single asynchronous copy); "POC: Experts
+// offload", host-tier commit message (a host row is not reused before the copy
+// reading it has finished);
 // "moe: expert slots in size classes", PR description and the ExpertCache
-// constructor in its review (layers grouped by bytes per expert; each group has
-// its own slots and LRU; slots of a class are contiguous; empty slots sit at the
-// LRU's back and are taken first; budget never moves between classes; with
-// --per-layer every layer has its own LRU and the same share); the RFC's Cache
-// bullet (LRU, optional LFU).
+// constructor in its review (a class = the layers whose experts take equal bytes,
+// with a separate slot pool and LRU; a class's slots are adjacent; unused slots
+// are queued at the LRU's tail and handed out before any eviction; no class
+// borrows another's budget; --per-layer gives every layer an LRU of its own and
+// an equal fraction); the RFC's Cache bullet (LRU, optional LFU).
 //
 // A class's slots form one partition (shared LRU) or one partition per layer of
 // the class (per-layer mode: slots split as evenly as possible, in layer order,
@@ -168,7 +169,7 @@ moe_cache* moe_cache_create_ex(const moe_size_class_desc* classes, int n_classes
             const int64_t cnt = base + (pi < extra ? 1 : 0);
             for (int64_t i = 0; i < cnt; ++i, ++s) {
                 CachePart& part = k.parts[(size_t)pi];
-                part.lru.push_back(s);  // empty slots at the back: taken first
+                part.lru.push_back(s);  // unused slots queue at the tail, where victims come from
                 k.slots[(size_t)s].it = std::prev(part.lru.end());
                 k.slots[(size_t)s].part = pi;
             }

@@ -7,8 +7,8 @@
 // experts through a gather quantized matmul on the device cache; the GPU should
 // not idle between a layer's sub-steps); "RFC: stream MoE experts from disk in
 // from_pretrained", How the prototype works (gated, concatenated, untransposed
-// experts, no bias; per-layer expert -> slot table; when every expert is
-// resident, layers never synchronise with the host); BigMoeOnEdge commit message
+// experts, no bias; each layer maps expert ids to slots; a fully resident model
+// runs its layers without host round trips); BigMoeOnEdge commit message
 // (cache-aware substitution, optional).
 //
 // Why one kernel: a decode layer moves ~14 MB (10 experts of 1.38 MB at 3 bits),

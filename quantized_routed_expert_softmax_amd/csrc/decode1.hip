@@ -4,33 +4,43 @@
 //
 // Sources: "RFC: stream MoE experts from disk in from_pretrained", Motivation
 // (each token reads only its k routed experts) and How the prototype works
-// (gated, concatenated, untransposed experts without bias, a per-layer expert
-// -> slot table; with every expert resident a layer never waits for the host);
+// (gated, concatenated, untransposed experts without bias, each layer mapping
+// expert ids to slots; a fully resident model runs without host round trips);
 // "POC: Experts offload", commit messages (queued GPU work must not idle
 // between a layer's steps).
 //
 // A decode layer moves ~14 MB (10 experts of 1.38 MB at 3 bits): ~2 us of HBM
 // time against ~1 us per dependent memory round trip, so the kernel is shaped
-// by its dependency chain, not by arithmetic:
-//   1. every wave loads what it needs at once: the router logits and the slot
-//      table (8 per lane, lane l holds experts l + 64 j), its share of x (lane l:
-//      inputs 32 l .. 32 l + 31), and the workgroup's call-tag counter;
-//   2. every wave routes the token itself, in registers, with no LDS round trip
-//      and no barrier: the top k+1 keys by logit (each lane sorts its 8 keys,
-//      then k+1 rounds of a wave-wide maximum), the set proven equal to the
-//      contract's top-k by the logit-gap argument (else the contract's routine
-//      runs); the slots of the chosen experts come from the table registers;
-//   3. it then requests ALL its weight rows: its phase-1 item(s) (rows n, n+16
-//      of gate and of up of one expert) and its phase-2 rows (the workgroup's
-//      output rows of down for its own expert(s)), so the whole layer's bytes are
-//      in flight from the first microsecond of streaming;
-//   4. the routing weights (which need Z over all logits) are computed while
-//      the weights are in flight;
-//   5. phase 1: SwiGLU pairs published as 64-bit (h pair, call tag) words;
-//   6. phase 2: a wave polls only its own expert's h words (one round of loads
-//      when its producers are done), stages them in its own LDS, computes its
-//      rows of down and weights them; partial sums meet in LDS in wave order
-//      (deterministic) and become the bf16 output rows.
+// by its dependency chain, not by arithmetic.  One workgroup of W waves per
+// compute unit:
+//   1. one round of loads shared through LDS: the router logits and the slot
+//      table (list wave j takes experts 64 j .. 64 j + 63 and sorts its 16
+//      largest logit keys), x, and the workgroup's call-tag counter;
+//   2. every wave merges the eight lists itself and checks that the top k by
+//      logit is the contract's top k (a gap of at least 2^-9 between the k-th
+//      and (k+1)-th logit, the k-th within 64 of the largest); then hit h is
+//      routing position h and its slot comes from the table, with no further
+//      barrier.  Otherwise (near-ties, non-finite logits, or given ids) wave 0
+//      runs the contract's own routine and builds the hit list in id order
+//      while the others wait;
+//   3. each wave then requests ALL its weight rows: its phase-1 item(s) (rows
+//      n, n+16 of gate and of up of one expert) and its phase-2 rows (the
+//      workgroup's output rows of down for its own expert(s)), so the layer's
+//      bytes are in flight from the first microsecond of streaming;
+//   4. phase 1: SwiGLU pairs published as 64-bit (h pair, call tag) words;
+//   5. wave 0 then computes the routing weights (they need Z over all logits;
+//      nothing before the final combine uses them, and computing them before
+//      its phase-1 item would delay words that every consumer waits for);
+//   6. phase 2: a wave polls only its own expert's h words (first one word with
+//      pauses, then all of them), stages them in its own LDS, computes its rows
+//      of down and weights them; partial sums meet in LDS and become the bf16
+//      output rows, summed over the hits in ascending expert id (fixed order,
+//      the same whichever routing order the hits were numbered in).
+// Measured on MI355X (in-kernel timestamps, median over workgroups, from the
+// first workgroup's start): routing done 1.9 us, rows requested 2.3 us, phase 1
+// done 3.9-5.3 us (the third wave on a SIMD finishes last: 10 items on 4 SIMDs,
+// ~0.6 us of VALU work each), h complete 7.2 us, end 8.4 us; plus ~1.4 us from
+// the previous kernel's end to this one's start.
 // All workgroups are co-resident (one per compute unit, occupancy checked on the
 // host), so every polled word is eventually written; the poll is bounded and
 // reports MOE_ERRW_TIMEOUT instead of hanging.
@@ -70,6 +80,7 @@ struct D1Params {
     uint64_t* xw;
     uint32_t* err;
     int rows_per_wg;  // output rows per workgroup (a multiple of 64 / LPRD)
+    int ipw;          // phase-1 items per workgroup: ceil(k * I/2 / grid)
     unsigned spin_limit;
 };
 
@@ -187,15 +198,16 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
     __shared__ float s_hs[W][32];           // its unit sums
     __shared__ float s_y[kD1MaxHits][W][64];  // down rows of each wave's experts
     __shared__ float s_hw[kD1MaxK];         // weight of each hit
-    __shared__ int32_t s_hit[kD1MaxK];      // hit list: expert ids ascending
-    __shared__ int32_t s_hslot[kD1MaxK];    // slot of each hit, -1 not resident
+    __shared__ int32_t s_hslot[kD1MaxK];    // slot of each hit, -1 not resident (slow path)
+    __shared__ int32_t s_ord[kD1MaxK];      // hits by ascending expert id
     __shared__ int s_nhit;
     __shared__ float s_sel[kD1MaxK];        // routing: p by position
     __shared__ RouteScratch s_rsc[1];       // routing fallback (wave 0)
     __shared__ int32_t s_fid[1][32];
     __shared__ float s_fw[1][32];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);  // wave-uniform
     const int G = gridDim.x;
     const int E = P.E, k = P.k, I = P.I;
     const bool wg0 = blockIdx.x == 0;
@@ -230,40 +242,60 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
     uint32_t tag = gen0 + 1u;
     if (tag == 0u) tag = 1u;
 
-    // ---- 2. routing by wave 0 (the others wait at the next barrier) ----
-    // lanes < k of wave 0: the expert of pair `lane` (idv), its weight when given
-    // or from the fallback (wv), its hit index (hidx), first pair of its expert
+    // ---- 2. routing ----
+    // Every wave merges the eight lists and takes the gap test itself (same
+    // inputs, same result in every wave), so on the usual path no wave waits for
+    // another before requesting its rows.  Lanes < k: the expert of pair `lane`
+    // (idv), its weight when given or from the fallback (wv, wave 0), its hit
+    // index (hidx) and whether it is the first pair of its expert (first).
     int32_t idv = 0;
     float wv = 0.0f;
     bool fast = false, nonfinite = false, first = false;
     int hidx = 0;
-    if (wave == 0) {
-        if (P.logits) {
-            int nb = 0;
-            for (int i = 0; i < nl; ++i) nb |= s_bad[i];
-            if (nb) {
-                nonfinite = true;
-                idv = lane;  // ids 0..k-1 with weight 0 (the token's result is discarded)
-            } else {
-                const int r = lane >> 4;
-                const uint32_t A = r < nl ? s_list[r][lane & 15] : kPadKey32;
-                const uint32_t Bv = r + 4 < nl ? s_list[r + 4][lane & 15] : kPadKey32;
-                uint32_t K = row_merge_u32(A, Bv, lane);
-                K = row_merge_u32(K, swap16_u32(K), lane);
-                K = row_merge_u32(K, swap32_u32(K), lane);  // lanes 0-15: the 16 largest keys
-                const uint32_t c0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)K);
-                const uint32_t c_last = (uint32_t)__builtin_amdgcn_readlane((int)K, k - 1);
-                const uint32_t c_next = (uint32_t)__builtin_amdgcn_readlane((int)K, k);
-                const float m_hi = order_bits_logit(c0 | 0x1ffu);        // >= the largest logit
-                const float lo_in = order_bits_logit(c_last & ~0x1ffu);  // <= every chosen logit
-                const float hi_out = c_next == kPadKey32 ? -INFINITY : order_bits_logit(c_next | 0x1ffu);
-                fast = lo_in - m_hi >= -64.0f && lo_in - hi_out >= 0x1p-9f;
-                if (fast) {
-                    idv = key32_id(K);
+    if (P.logits) {
+        int nb = 0;
+        for (int i = 0; i < nl; ++i) nb |= s_bad[i];
+        if (nb) {
+            nonfinite = true;
+        } else {
+            const int r = lane >> 4;
+            const uint32_t A = r < nl ? s_list[r][lane & 15] : kPadKey32;
+            const uint32_t Bv = r + 4 < nl ? s_list[r + 4][lane & 15] : kPadKey32;
+            uint32_t K = row_merge_u32(A, Bv, lane);
+            K = row_merge_u32(K, swap16_u32(K), lane);
+            K = row_merge_u32(K, swap32_u32(K), lane);  // lanes 0-15: the 16 largest keys
+            const uint32_t c0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)K);
+            const uint32_t c_last = (uint32_t)__builtin_amdgcn_readlane((int)K, k - 1);
+            const uint32_t c_next = (uint32_t)__builtin_amdgcn_readlane((int)K, k);
+            const float m_hi = order_bits_logit(c0 | 0x1ffu);        // >= the largest logit
+            const float lo_in = order_bits_logit(c_last & ~0x1ffu);  // <= every chosen logit
+            const float hi_out = c_next == kPadKey32 ? -INFINITY : order_bits_logit(c_next | 0x1ffu);
+            fast = lo_in - m_hi >= -64.0f && lo_in - hi_out >= 0x1p-9f;
+            idv = key32_id(K);
+        }
+    }
+    // slots: on the fast path lane h of every wave holds hit h's slot (hit h =
+    // routing position h: the k ids are distinct and in range), else s_hslot
+    int32_t hsl = -1;
+    int n_hit = k;
+    if (fast) {
+        if (lane < k) {
+            const int32_t sl = s_table[idv];
+            const bool res = sl >= 0 && sl < P.n_slots;
+            if (!res && wg0 && wave == 0) d1_flag(P.err, sl < 0 ? MOE_ERRW_NOT_RESIDENT : MOE_ERRW_BAD_SLOT);
+            hsl = res ? sl : -1;
+        }
+        first = lane < k;
+        hidx = lane;  // s_ord puts the hits in id order after phase 1
+    } else {
+        // wave 0 routes with the contract's own routine (near-ties at the
+        // boundary, the k-th logit far below the largest, or a non-finite logit)
+        // or takes the given routing, and builds the hit list; the others wait
+        if (wave == 0) {
+            if (P.logits) {
+                if (nonfinite) {
+                    idv = lane;  // ids 0..k-1 with weight 0 (the token's result is discarded)
                 } else {
-                    // the contract's own routine (near-ties at the boundary, or the
-                    // k-th logit far below the largest): ids by (p desc, id asc),
-                    // weights final
                     route_token_512(s_logit, E, k, MOE_ROUTE_PLAIN, 0.0f, nullptr, lane, s_fid[0], s_fw[0],
                                     &s_rsc[0]);
                     __builtin_amdgcn_wave_barrier();
@@ -271,48 +303,47 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
                     idv = lane < k ? s_fid[0][lane] : 0;
                     wv = lane < k ? s_fw[0][lane] : 0.0f;
                 }
+            } else if (lane < k) {
+                idv = P.ids_in[lane];
+                wv = P.w_in[lane];
             }
-        } else if (lane < k) {
-            idv = P.ids_in[lane];
-            wv = P.w_in[lane];
-        }
-        // hit list: distinct ids ascending (pairs with an id outside [0, E)
-        // dropped); hit index = distinct ids below this one
-        const bool valid = lane < k && idv >= 0 && idv < E;
-        if (lane < k && !valid && wg0) d1_flag(P.err, MOE_ERRW_BAD_ID);
-        // (loops, not unrolled: this code runs once per launch, so its length in
-        // instruction-cache lines costs more than its instruction count)
-        int dup = 0;
+            // hit list: distinct ids ascending (pairs with an id outside [0, E)
+            // dropped); hit index = distinct ids below this one
+            const bool valid = lane < k && idv >= 0 && idv < E;
+            if (lane < k && !valid && wg0) d1_flag(P.err, MOE_ERRW_BAD_ID);
+            int dup = 0;
 #pragma unroll 1
-        for (int q = 0; q < k; ++q) {
-            const int o = __builtin_amdgcn_readlane(idv, q);
-            dup += (o == idv && q < lane) ? 1 : 0;
-        }
-        first = valid && dup == 0;
-        const unsigned long long fm = __ballot(first);
+            for (int q = 0; q < k; ++q) {
+                const int o = __builtin_amdgcn_readlane(idv, q);
+                dup += (o == idv && q < lane) ? 1 : 0;
+            }
+            first = valid && dup == 0;
+            const unsigned long long fm = __ballot(first);
 #pragma unroll 1
-        for (int q = 0; q < k; ++q) {
-            const int o = __builtin_amdgcn_readlane(idv, q);
-            hidx += (((fm >> q) & 1ull) && o < idv) ? 1 : 0;
+            for (int q = 0; q < k; ++q) {
+                const int o = __builtin_amdgcn_readlane(idv, q);
+                hidx += (((fm >> q) & 1ull) && o < idv) ? 1 : 0;
+            }
+            if (first) {
+                const int32_t sl = s_table[idv];
+                const bool res = sl >= 0 && sl < P.n_slots;
+                if (!res && wg0) d1_flag(P.err, sl < 0 ? MOE_ERRW_NOT_RESIDENT : MOE_ERRW_BAD_SLOT);
+                s_hslot[hidx] = res ? sl : -1;
+            }
+            if (lane == 0) s_nhit = __popcll(fm);
+            if (lane < k) s_ord[lane] = lane;  // hits already ascending
         }
-        if (first) {
-            const int32_t sl = s_table[idv];
-            const bool res = sl >= 0 && sl < P.n_slots;
-            if (!res && wg0) d1_flag(P.err, sl < 0 ? MOE_ERRW_NOT_RESIDENT : MOE_ERRW_BAD_SLOT);
-            s_hit[hidx] = idv;
-            s_hslot[hidx] = res ? sl : -1;
-        }
-        if (lane == 0) s_nhit = __popcll(fm);
+        __syncthreads();
+        n_hit = s_nhit;
     }
-    __syncthreads();
-    const int n_hit = s_nhit;
 
     // ---- 3. every weight row this wave needs, requested now ----
-    // phase-1 items: (hit, pair p) over n_hit * I/2 items, ipw per workgroup;
-    // wave w takes the workgroup's items w, w + W
+    // phase-1 items: (hit, pair p) over n_hit * I/2 items, P.ipw per workgroup
+    // (sized for k hits; with repeated ids the last workgroups idle); wave w
+    // takes the workgroup's items w, w + W
     const int half_i = I >> 1;
     const int n_items = n_hit * half_i;
-    const int ipw = (n_items + G - 1) / G;
+    const int ipw = P.ipw;
     Unit<BG> gu[kD1MaxItems][4];
     int it_hit[kD1MaxItems], it_p[kD1MaxItems], it_slot[kD1MaxItems];
     const uint32_t g_row_b = (uint32_t)(H * BG / 8), g_sb_b = (uint32_t)(H / 16);
@@ -324,7 +355,7 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
         const int h = on ? udiv(it, half_i) : 0;
         it_hit[q] = on ? h : -1;
         it_p[q] = on ? it - h * half_i : 0;
-        it_slot[q] = on ? s_hslot[h] : -1;
+        it_slot[q] = !on ? -1 : fast ? __builtin_amdgcn_readlane(hsl, h) : s_hslot[h];
         if (it_slot[q] >= 0) {
             const uint8_t* base = P.pool + (size_t)it_slot[q] * (size_t)P.slot_bytes;
             const uint32_t n0 = (uint32_t)pair_row(2 * it_p[q]);
@@ -346,7 +377,7 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
 #pragma unroll
     for (int q = 0; q < kD1MaxHits; ++q) {
         const int h = wave + W * q;
-        hs_slot[q] = h < n_hit ? s_hslot[h] : -1;
+        hs_slot[q] = h >= n_hit ? -1 : fast ? __builtin_amdgcn_readlane(hsl, h) : s_hslot[h];
         if (hs_slot[q] >= 0) {
             const uint8_t* base = P.pool + (size_t)hs_slot[q] * (size_t)P.slot_bytes;
 #pragma unroll
@@ -359,56 +390,7 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
         }
     }
 
-    // ---- 4. routing weights, by wave 0 while the rows are in flight ----
-    if (wave == 0) {
-        if (P.logits && fast) {
-            // m and Z of the contract over every logit, p of the chosen, ordered by
-            // (p desc, id asc), weights = p / (their sum in that order)
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = lane + 64 * j < E ? s_logit[lane + 64 * j] : -INFINITY;
-            float m = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-            m = wave_max_f(m);
-            const float Z = route_sel_z(v, E, m);
-            const float lx = lane < k ? s_logit[idv] : 0.0f;
-            const float p = lane < k ? __fdiv_rn(exp_contract_nb(lx - m), Z) : 0.0f;
-            int pos = 0;
-#pragma unroll 1
-            for (int q = 0; q < k; ++q) {
-                const float po = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), q));
-                const int io = __builtin_amdgcn_readlane(idv, q);
-                pos += (po > p || (po == p && io < idv)) ? 1 : 0;
-            }
-            if (lane < k) s_sel[pos] = p;
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            float ssum = 0.0f;
-            for (int q = 0; q < k; ++q) ssum = ssum + s_sel[q];
-            wv = lane < k ? __fdiv_rn(p, ssum) : 0.0f;
-            if (wg0 && lane < k && P.ids_out) {
-                P.ids_out[pos] = idv;
-                P.w_out[pos] = wv;
-            }
-        } else if (P.logits) {
-            if (nonfinite && wg0 && lane == 0) d1_flag(P.err, MOE_ERRW_NONFINITE);
-            if (wg0 && lane < k && P.ids_out) {  // fallback or non-finite: already in contract order
-                P.ids_out[lane] = idv;
-                P.w_out[lane] = wv;
-            }
-        }
-        // weight of each hit: the weights of its pairs, in pair order
-        if (first) {
-            float ws = 0.0f;
-            for (int q = 0; q < k; ++q) {
-                const int o = __builtin_amdgcn_readlane(idv, q);
-                const float wo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), q));
-                if (o == idv) ws = ws + wo;
-            }
-            s_hw[hidx] = ws;
-        }
-    }
-
-    // ---- 5. phase 1: gate/up + SwiGLU -> tagged h pair words ----
+    // ---- 4. phase 1: gate/up + SwiGLU -> tagged h pair words ----
     const uint64_t tag_hi = (uint64_t)tag << 32;
     if (it_hit[0] >= 0) {
         uint32_t xw16[16], xp[16];
@@ -445,6 +427,64 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
             if (lane == 0)
                 __hip_atomic_store(&P.xw[(size_t)it_hit[q] * half_i + it_p[q]], word, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    // ---- 5. routing weights, by wave 0 after its phase-1 items (nothing before
+    // the final combine needs them; computed earlier they would hold up wave 0's
+    // share of phase 1, which every expert's consumers wait for) ----
+    if (wave == 0) {
+        if (P.logits && fast) {
+            // m and Z of the contract over every logit, p of the chosen, ordered by
+            // (p desc, id asc), weights = p / (their sum in that order)
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = lane + 64 * j < E ? s_logit[lane + 64 * j] : -INFINITY;
+            float m = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+            m = wave_max_f(m);
+            const float Z = route_sel_z(v, E, m);
+            const float lx = lane < k ? s_logit[idv] : 0.0f;
+            const float p = lane < k ? __fdiv_rn(exp_contract_nb(lx - m), Z) : 0.0f;
+            int pos = 0;
+#pragma unroll 1
+            for (int q = 0; q < k; ++q) {
+                const float po = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), q));
+                const int io = __builtin_amdgcn_readlane(idv, q);
+                pos += (po > p || (po == p && io < idv)) ? 1 : 0;
+            }
+            if (lane < k) s_sel[pos] = p;
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            float ssum = 0.0f;
+            for (int q = 0; q < k; ++q) ssum = ssum + s_sel[q];
+            wv = lane < k ? __fdiv_rn(p, ssum) : 0.0f;
+            if (wg0 && lane < k && P.ids_out) {
+                P.ids_out[pos] = idv;
+                P.w_out[pos] = wv;
+            }
+        } else if (P.logits) {
+            if (nonfinite && wg0 && lane == 0) d1_flag(P.err, MOE_ERRW_NONFINITE);
+            if (wg0 && lane < k && P.ids_out) {  // fallback or non-finite: already in contract order
+                P.ids_out[lane] = idv;
+                P.w_out[lane] = wv;
+            }
+        }
+        if (fast) {
+            // one pair per hit; hits in id order for the combine
+            if (lane < k) s_hw[lane] = wv;
+            int rank = 0;
+#pragma unroll 1
+            for (int q = 0; q < k; ++q) rank += __builtin_amdgcn_readlane(idv, q) < idv ? 1 : 0;
+            if (lane < k) s_ord[rank] = lane;
+        } else if (first) {
+            // weight of each hit: the weights of its pairs, in pair order
+            float ws = 0.0f;
+            for (int q = 0; q < k; ++q) {
+                const int o = __builtin_amdgcn_readlane(idv, q);
+                const float wo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), q));
+                if (o == idv) ws = ws + wo;
+            }
+            s_hw[hidx] = ws;
         }
     }
 
@@ -520,12 +560,13 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
     // the next call's counters: b, b + G, ... (every wave has read counter b)
     for (int j = blockIdx.x + G * (int)threadIdx.x; j < kMaxGrid; j += G * 64 * W)
         __hip_atomic_store(&P.gen[kGenBase + j], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // out[row] = sum over hits (ascending id) of weight * y, in fp32
+    // out[row] = sum over hits (ascending expert id) of weight * y, in fp32
     if ((int)threadIdx.x < P.rows_per_wg) {
         const int row = row0 + (int)threadIdx.x;
         if (row < H) {
             float o = 0.0f;
-            for (int h = 0; h < n_hit; ++h) {
+            for (int r = 0; r < n_hit; ++r) {
+                const int h = s_ord[r];
                 const int q = h / W, w = h - q * W;
                 o = __builtin_fmaf(s_hw[h], s_y[q][w][threadIdx.x], o);
             }
@@ -666,6 +707,7 @@ hipError_t launch_decode1(const float* logits, const int32_t* ids_in, const floa
     P.xw = (uint64_t*)((uint8_t*)reserved + MOE_WS_GEN_BYTES);
     P.err = err;
     P.rows_per_wg = rows;
+    P.ipw = (int)(((int64_t)k * (c.I / 2) + G - 1) / G);
     P.spin_limit = 1u << 20;
     return v->launch(P, G, s);
 }

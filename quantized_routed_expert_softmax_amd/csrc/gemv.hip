@@ -4,7 +4,7 @@
 // Sources: "POC: Experts offload", PR description (quantized experts run through
 // a gather quantized matmul on the device cache); "RFC: stream MoE experts from
 // disk in from_pretrained", How the prototype works (gated, concatenated,
-// untransposed experts without bias; per-layer expert -> slot table).
+// untransposed experts without bias; each layer maps expert ids to slots).
 //
 // Decode reads each routed expert's bytes once and does ~2 flop per weight, so
 // it is bound by HBM bandwidth.  Design:

@@ -2,10 +2,10 @@
 // dequantizing GEMM on bf16 matrix cores (v_mfma_f32_16x16x32_bf16).
 //
 // Sources: "RFC: stream MoE experts from disk in from_pretrained", How the
-// prototype works, Prefill (a long prompt routes to nearly every expert; they
-// run through the sorted gather quantized matmul in groups of 64) and Quantized
-// experts (group-wise affine format); "POC: Experts offload", commit messages
-// (sorted prefill, 64 experts at a time).
+// prototype works, Prefill (a long prompt touches almost all experts, which are
+// then processed by a sorted, gathered quantized matmul, 64 experts per batch)
+// and Quantized experts (group-wise affine format); "POC: Experts offload",
+// commit messages (the sorted prefill's batches of 64 experts).
 //
 // Work split: a workgroup owns (hit expert, 64 output columns); each of its 4
 // waves owns 16 columns and loops over the expert's rows (its sorted pairs) in

@@ -2,8 +2,8 @@
 // MoE layer: bf16 pair arithmetic, code extraction from the slot format's pack
 // units, wave reductions.
 //
-// Slot format (one expert row; the pages only say "group-wise affine, one
-// contiguous row per expert" — "RFC: stream MoE experts from disk in
+// Slot format (one expert row; the pages fix only a group-wise affine code and
+// a single unbroken row per expert — "RFC: stream MoE experts from disk in
 // from_pretrained", How the prototype works): codes are a little-endian bit
 // stream in pack units of 32 values held in B uint32 words; scale and bias are
 // one fp16 pair per group of 64 inputs.

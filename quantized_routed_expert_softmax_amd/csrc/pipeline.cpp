@@ -1,19 +1,20 @@
 // pipeline.cpp — the miss path of the bounded expert cache: an expert store
-// (a file, or host memory standing in for one), an optional tier of expert rows
-// in pinned host memory, I/O threads that read missing experts into recycled
-// pinned buffers, installs on a copy stream, and the stream-ordered reservations
+// (a file, or host memory standing in for one), an optional pinned-host level of
+// expert rows, I/O threads that read missing experts into reused pinned staging
+// buffers, installs on a copy stream, and the stream-ordered reservations
 // that let installs overlap compute without a host synchronisation.
 //
 // Sources: "RFC: stream MoE experts from disk in from_pretrained", How the
-// prototype works, Cache and Reads bullets (misses read on I/O threads into
-// recycled pinned buffers, one contiguous read and one non-blocking host-to-device
-// copy per expert; the next layers' experts guessed and read in the background;
-// when every expert is resident no layer waits for the host) and Host tier bullet
-// (pinned rows between storage and the device cache, optional preload at load
-// time); "POC: Experts offload", commit messages (reads through one descriptor per
-// shard; a layer sends its slots in one small copy; host rows stay reserved until
-// the copy that reads them has run; guessed reads still in flight are skipped,
-// not waited for).
+// prototype works, Cache and Reads bullets (a missing expert is fetched by a
+// worker thread as a single read into a pinned staging buffer that is reused,
+// then moved to its slot by one asynchronous copy; experts that later layers are
+// predicted to need are fetched ahead of time; a fully resident model never
+// makes a layer wait on the host) and Host tier bullet (a pinned host copy of
+// expert rows forms a level under the device cache and may be filled when
+// the model loads); "POC: Experts offload", commit messages (one open file per
+// shard serves all reads; each layer's slot numbers go to the device in a single
+// small copy; a host row is not reused before the copy reading it has finished;
+// a predicted read that has not landed yet is bypassed rather than awaited).
 //
 // Ordering without host waits.  Three event rings carry every dependency:
 //   fill rings (one per copy   — recorded after each install copy.  The compute
@@ -731,7 +732,7 @@ moe_pipeline* moe_pipeline_create(moe_cache* cache, moe_store* store, void* cons
             return bail(MOE_E_HIP, "moe_pipeline_create: pinned staging buffer");
 
     // host tier: the budget is split between classes in proportion to the bytes
-    // of all their experts, so every layer keeps the same share
+    // of all their experts, so each layer gets an equal fraction
     if (cfg->host_tier_bytes > 0) {
         std::vector<double> weight(nc, 0.0);
         double sum = 0.0;

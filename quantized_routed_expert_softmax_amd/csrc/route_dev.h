@@ -3,9 +3,9 @@
 //
 // Sources: "RFC: stream MoE experts from disk in from_pretrained", Motivation
 // (each token uses k of E experts; only the top-k are read); BigMoeOnEdge commit
-// message adding cache-aware substitution (every cached expert's score is
-// raised by L times the token's score range, then top-k is taken again; the
-// same number of experts runs).
+// message adding cache-aware substitution (cached experts get a bonus of L x
+// (max - min of the token's scores), the k winners are picked again from the
+// adjusted scores, and k experts still run).
 //
 // The arithmetic follows the routing numeric contract of include/moe.h
 // operation by operation: no contraction (this header must be compiled under

@@ -2,9 +2,9 @@
 // the input of the lookahead guesses: logits[m][t][e] = sum_i x[t][i] * Wr_m[e][i].
 //
 // Source: "RFC: stream MoE experts from disk in from_pretrained", How the
-// prototype works, Reads bullet (the next two layers' experts are guessed by
-// running their routers on the current hidden states and read in the
-// background).
+// prototype works, Reads bullet (the experts of the two following layers are
+// predicted by applying their router weights to the present hidden state, and
+// fetched while compute goes on).
 //
 // HBM-bound GEMV: the routers' bf16 rows are read once.  One wave owns one
 // (layer, expert) row; its 64 lanes each load 16 bytes (8 values) per step along

@@ -1,11 +1,11 @@
 // sort.hip — stable counting sort of the routed (token, j) pairs by expert and
 // the pass table (hit experts in ascending id, at most P per pass).
 //
-// Sources: "POC: Experts offload", commit messages (sorted prefill runs 64
-// experts at a time, so a prompt that routes to every expert stays bounded);
-// "RFC: stream MoE experts from disk in from_pretrained", How the prototype
-// works, Prefill (a long prompt routes to nearly every expert; they run through
-// the sorted gather in groups of 64).
+// Sources: "POC: Experts offload", commit messages (the sorted prefill takes the
+// hit experts 64 per batch, which bounds its memory even when a prompt touches
+// all of them); "RFC: stream MoE experts from disk in from_pretrained", How the
+// prototype works, Prefill (almost every expert is hit by a long prompt; the
+// sorted gather processes them in batches of 64).
 //
 // Integer-only and deterministic: counts come from integer atomics (order-free),
 // a pair's place is offsets[e] + (pairs of e in earlier tiles) + (pairs of e

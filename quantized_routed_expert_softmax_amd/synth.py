@@ -7,7 +7,7 @@ GPU library nor the CPU oracle, so both can be fed from it.
 
 Shapes and distributions follow the workloads on the pages:
   * "RFC: stream MoE experts from disk in from_pretrained", section "Motivation":
-    a 48-layer MoE with 512 experts per layer and 10 experts per token, experts
+    48 MoE layers, each of 512 experts with 10 routed per token, experts
     quantized to 3 bits, prompts processed in 1K-token chunks.
   * "moe: expert slots in size classes", PR description: mixed-quant models whose
     layers need different bytes per expert (two size classes).

@@ -7,10 +7,11 @@ least recently used entry that is not pinned (LFU: the least used since it
 arrived, ties to the least recently used).  Layers are mapped to classes;
 budget never moves between classes.  Sources: "RFC: stream MoE experts from disk
 in from_pretrained", How the prototype works, Cache bullet (pool of slots, LRU,
-per-layer expert -> slot table); "moe: expert slots in size classes", PR
-description and the ExpertCache constructor in its review (own slots and LRU
-per class, empty slots taken first; one LRU per layer with --per-layer, every
-layer keeping the same share); the RFC's Cache bullet (LRU, optional LFU).
+each layer's map from expert to slot); "moe: expert slots in size classes", PR
+description and the ExpertCache constructor in its review (a separate slot pool
+and LRU for every class, unused slots handed out first; --per-layer gives each
+layer a list of its own over an equal fraction); the RFC's Cache bullet (LRU,
+optional LFU).
 
 The model is written from those statements alone, with Python lists, so that a
 mistake in the native cache (a wrong victim, a shared budget, a lost touch)

@@ -2,12 +2,12 @@
 pins.  Pure host code (fills are completed with a NULL event, so no GPU call).
 
 Sources: "RFC: stream MoE experts from disk in from_pretrained", How the
-prototype works (preallocated pool of slots, LRU, per-layer expert -> slot
-table); "POC: Experts offload", host-tier commit (rows stay reserved until the
-copy that reads them has run); "moe: expert slots in size classes", PR
-description and the ExpertCache constructor (own slots and LRU per class;
-empty slots at the LRU's back are taken first; budget never moves between
-classes).
+prototype works (a fixed pool of slots allocated up front, LRU, each layer's
+map from expert to slot); "POC: Experts offload", host-tier commit (a row is not
+reused before the copy reading it has finished); "moe: expert slots in size
+classes", PR description and the ExpertCache constructor (a separate slot pool
+and LRU for every class; unused slots queue at the LRU's tail and are handed out
+first; no class borrows another's budget).
 """
 import numpy as np
 import pytest

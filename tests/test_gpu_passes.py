@@ -1,10 +1,10 @@
 """Prefill in passes of at most 64 hit experts, on the GPU.
 
-A long prompt routes to nearly every expert of a layer; its hit experts run in
+Almost every expert of a layer is hit by a long prompt; the hit experts run in
 ascending id, 64 per pass, so that only one pass's experts must be resident at a
 time ("RFC: stream MoE experts from disk in from_pretrained", How the prototype
-works, Prefill bullet; "POC: Experts offload", commit messages: sorted prefill,
-64 experts at a time).
+works, Prefill bullet; "POC: Experts offload", commit messages: the sorted
+prefill's batches of 64 experts).
 
 Checked here:
   * sort once, passes one by one (or in groups), combine once: bit-identical to

@@ -11,10 +11,10 @@ exactly the store's rows.
 
 Sources: "RFC: stream MoE experts from disk in from_pretrained", How the
 prototype works (Cache, Reads and Host tier bullets); "POC: Experts offload",
-commit messages (recycled pinned buffers, one small table copy per layer, host
-rows reserved until their copy has run, guessed reads skipped while in flight);
-"moe: expert slots in size classes", PR description (own slots and LRU per
-class, the same share for every layer).
+commit messages (reused pinned staging buffers, one small table copy per layer,
+host rows kept until their copy has finished, predicted reads still in flight
+bypassed); "moe: expert slots in size classes", PR description (a separate slot
+pool and LRU for every class, an equal fraction for every layer).
 """
 import numpy as np
 import pytest
@@ -170,7 +170,7 @@ def replay():
 
 @pytest.mark.parametrize("kind", ["file", "memory"])
 def test_replay_from_store_matches_resident_run_and_lru_model(replay, kind, tmp_path):
-    """No host tier: every device miss is a store read into a recycled pinned
+    """No host tier: every device miss is a store read into a reused pinned
     buffer, then one copy.  Installs complete between layers (drain), so the cache
     follows the LRU model exactly."""
     rp, ids, ws, host, ref = replay

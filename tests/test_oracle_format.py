@@ -2,10 +2,10 @@
 fixtures (tests/golden/pack_units.txt, tests/golden/layout.txt), the test
 quantizer's own arrays, and exact closed forms.
 
-The pages give the format only as group-wise affine quantization with one
-contiguous row per expert ("RFC: stream MoE experts from disk in
-from_pretrained", How the prototype works, Quantized experts); the bit order
-and block order are this build's reading, written in include/moe.h.
+The pages fix only a group-wise affine code with each expert stored as a
+single unbroken row ("RFC: stream MoE experts from disk in from_pretrained",
+How the prototype works, Quantized experts); the bit order and block order are
+a reading of that, written out in include/moe.h.
 """
 import os
 

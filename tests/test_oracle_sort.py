@@ -2,9 +2,9 @@
 
 Brute force: an O(n^2) stable placement written from the definition (pair p
 goes to offsets[e] + #{p' < p with the same expert}).  Source: "POC: Experts
-offload", commit messages (sorted prefill runs 64 experts at a time); "RFC:
+offload", commit messages (the sorted prefill's batches of 64 experts); "RFC:
 stream MoE experts from disk in from_pretrained", How the prototype works,
-Prefill (sorted gather in groups of 64).
+Prefill (sorted gather, 64 experts per batch).
 """
 import numpy as np
 import pytest

@@ -1,10 +1,10 @@
-"""Expert store (host side of the miss pipeline): layer-major rows, one
-contiguous row per expert, file- or memory-backed.  No GPU call is made here.
+"""Expert store (host side of the miss pipeline): layer-major rows, each
+expert a single unbroken row, file- or memory-backed.  No GPU call is made here.
 
 Sources: "RFC: stream MoE experts from disk in from_pretrained", How the
-prototype works, Quantized experts and Reads bullets (one contiguous row per
-expert, one contiguous read per expert); "POC: Experts offload", commit
-message (reads through one descriptor per shard).
+prototype works, Quantized experts and Reads bullets (each expert a single
+unbroken row, fetched by a single read); "POC: Experts offload", commit
+message (one open file per shard serves every read).
 """
 import ctypes
 
