@@ -809,9 +809,14 @@ int moe_pipeline_prepare(moe_pipeline* p, int layer, const int32_t* ids, int n, 
         int needs_fill = 0;
         int rc = moe_cache_acquire(p->cache, layer, e, &s, &needs_fill);
         // installs still in flight (earlier passes' or guesses') may hold every
-        // unpinned slot: wait for them one at a time, oldest first
-        while (rc == MOE_E_NO_SLOT && p->wait_oldest_fill(lk, cls))
+        // unpinned slot: wait for them one at a time, oldest first.  A fill can
+        // complete between the cache's check and ours, so when nothing is left in
+        // flight the cache is asked once more before the class counts as full.
+        while (rc == MOE_E_NO_SLOT) {
+            const bool waited = p->wait_oldest_fill(lk, cls);
             rc = moe_cache_acquire(p->cache, layer, e, &s, &needs_fill);
+            if (!waited) break;
+        }
         if (rc != MOE_OK && rc != MOE_E_BUSY) {
             lk.unlock();
             p->unpin_all(layer);
