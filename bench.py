@@ -611,28 +611,25 @@ def ceilings(torch, mb, dev, quick=False):
     out["read_prefill_rows"] = curve_point(512, row, 4, shapes + (8192, 16384), scattered=True)
     log(json.dumps({"ceiling_prefill_rows": out["read_prefill_rows"]}))
 
-    # idle latency: one lane chasing a random cycle of 64-byte nodes
+    # idle latency per level: one lane chasing a random cycle of 64-byte nodes,
+    # timed in-kernel.  L2 (1 MiB) and MALL (32 MiB) chains are warmed by a full
+    # lap in the same launch first; the HBM chain (4 GiB) is timed on nodes no
+    # earlier hop touched.
     lat = {}
-    for name, nbytes in (("hbm_1GiB", 1 << 30), ("l2_1MiB", 1 << 20)):
+    hops = 20000
+    for name, nbytes, warm_lap in (("l2_1MiB", 1 << 20, True), ("mall_32MiB", 32 << 20, True),
+                                   ("hbm_4GiB", 4 << 30, False)):
         n = nbytes // 64
         g = torch.Generator(device=dev)
         g.manual_seed(99)
         perm = torch.randperm(n, generator=g, device=dev, dtype=torch.int64)
         nxt = torch.zeros((n, 16), dtype=torch.int32, device=dev)
         nxt[perm, 0] = torch.roll(perm, -1).to(torch.int32)
-        o = torch.zeros(1, dtype=torch.int32, device=dev)
-        start = int(perm[0].item())
-        res = []
-        for hops in (2000, 22000):
-            mb.chase(nxt, start, hops, o)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            mb.chase(nxt, start, hops, o)
-            e1.record()
-            torch.cuda.synchronize()
-            res.append(e0.elapsed_time(e1))
-        lat[name + "_ns"] = round((res[1] - res[0]) * 1e6 / 20000, 1)   # per dependent load
+        o = torch.zeros(2, dtype=torch.int32, device=dev)
+        start = int(perm[n // 2].item())
+        mb.chase(nxt, start, n + hops if warm_lap else 0, hops, o)
+        torch.cuda.synchronize()
+        lat[name + "_ns"] = round(int(o[1].item()) * 10.0 / hops, 1)   # per dependent load
         del nxt, perm
     out["latency"] = lat
     log(json.dumps({"latency": lat}))

@@ -30,7 +30,7 @@ def lib() -> ctypes.CDLL:
             for name, args in {
                 "mb_residual_rmsnorm": [P, P, I32, I32, F32, P, P, P],
                 "mb_read_rows": [P, I32, I64, P, I32, P],
-                "mb_chase": [P, U32, I32, P, P],
+                "mb_chase": [P, U32, I32, I32, P, P],
                 "mb_mfma_loop": [I32, I32, P, P],
                 "mb_empty": [I32, I32, P],
             }.items():
@@ -71,9 +71,11 @@ def read_rows(rows_dev, n_rows: int, row_bytes: int, sink, wgs_per_row: int, str
                               ctypes.c_void_p(sink.data_ptr()), wgs_per_row, _stream(stream)), "read_rows")
 
 
-def chase(next_buf, start: int, hops: int, out, stream=None):
-    _check(lib().mb_chase(ctypes.c_void_p(next_buf.data_ptr()), start, hops, ctypes.c_void_p(out.data_ptr()),
-                          _stream(stream)), "chase")
+def chase(next_buf, start: int, warm: int, hops: int, out, stream=None):
+    """Follow the chain for `warm` untimed then `hops` timed loads; out (int32
+    [2]) gets the node reached and the timed part's 100 MHz ticks."""
+    _check(lib().mb_chase(ctypes.c_void_p(next_buf.data_ptr()), start, warm, hops,
+                          ctypes.c_void_p(out.data_ptr()), _stream(stream)), "chase")
 
 
 def mfma_loop(grid: int, iters: int, sink, stream=None):

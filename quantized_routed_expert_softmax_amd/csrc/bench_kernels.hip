@@ -6,7 +6,8 @@
 //    (no gain) of the sum; one launch per layer does both;
 //  * ceiling microbenchmarks that bound what a kernel of a given shape can reach
 //    on this GPU: streamed reads of given rows (bytes per launch as the layer
-//    kernels move them), a dependent-load chase (idle memory latency), a bf16
+//    kernels move them), a dependent-load chase (idle latency of each level of the
+//    memory hierarchy), a bf16
 //    MFMA loop (matrix-core peak) and an empty kernel (launch floor).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -107,15 +108,34 @@ __global__ __launch_bounds__(256) void read_rows_kernel(const uint8_t* const* __
     if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads live
 }
 
-// One lane follows next[] for `hops` dependent loads starting at `start`
-// (idle memory latency when the links are spread over more than the caches).
-__global__ void chase_kernel(const uint32_t* __restrict__ next, uint32_t start, int hops,
+// One lane follows next[] for `warm` dependent loads from `start` (untimed:
+// a full lap of a chain that fits a cache leaves it resident there), then for
+// `hops` more, timed in-kernel with s_memrealtime (100 MHz), so the warm-up and
+// the timed part run on the same compute unit and its caches.  out[0] = the
+// node reached, out[1] = ticks of the timed part.  The index goes through a VGPR
+// move the compiler cannot see through, so the loads are vector loads (the path
+// the layer kernels use), not scalar ones.
+__global__ void chase_kernel(const uint32_t* __restrict__ next, uint32_t start, int warm, int hops,
                              uint32_t* __restrict__ out)
 {
     if (threadIdx.x != 0) return;
     uint32_t p = start;
-    for (int h = 0; h < hops; ++h) p = next[(size_t)p * 16];
+    for (int h = 0; h < warm; ++h) {
+        uint32_t v;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"(p));
+        p = next[(size_t)v * 16];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::"v"(p));
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (int h = 0; h < hops; ++h) {
+        uint32_t v;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"(p));
+        p = next[(size_t)v * 16];
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::"v"(p));
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
     out[0] = p;
+    out[1] = (uint32_t)(t1 - t0);
 }
 
 // Every wave runs `iters` rounds of 8 independent v_mfma_f32_16x16x32_bf16
@@ -165,10 +185,10 @@ int mb_read_rows(const void* rows_dev, int n_rows, int64_t row_bytes, void* sink
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
-int mb_chase(const void* next, uint32_t start, int hops, void* out, hipStream_t s)
+int mb_chase(const void* next, uint32_t start, int warm, int hops, void* out, hipStream_t s)
 {
-    if (hops <= 0) return -1;
-    hipLaunchKernelGGL(chase_kernel, dim3(1), dim3(64), 0, s, (const uint32_t*)next, start, hops,
+    if (warm < 0 || hops <= 0) return -1;
+    hipLaunchKernelGGL(chase_kernel, dim3(1), dim3(64), 0, s, (const uint32_t*)next, start, warm, hops,
                        (uint32_t*)out);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
