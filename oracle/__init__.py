@@ -63,8 +63,15 @@ def _load():
             lib.oracle_layer.argtypes = [P, i32, i32, i32, i32, i32, P, P, i32, i32, P, P, i64,
                                          P, i32, P, i32]
             lib.oracle_router_logits.argtypes = [P, i32, i32, P, i32, i32, P]
+            lib.oracle_round_half.argtypes = [ctypes.c_double]
+            lib.oracle_round_half.restype = ctypes.c_uint16
+            lib.oracle_round_bf16.argtypes = [ctypes.c_double]
+            lib.oracle_round_bf16.restype = ctypes.c_uint16
+            lib.oracle_quantize.argtypes = [P, i32, i32, i32, P, P, P]
+            lib.oracle_convert_expert.argtypes = [P, P, i32, i32, i32, i32, P]
             for f in ("oracle_softmax", "oracle_route", "oracle_sort", "oracle_layout",
-                      "oracle_dequant", "oracle_layer", "oracle_router_logits"):
+                      "oracle_dequant", "oracle_layer", "oracle_router_logits", "oracle_quantize",
+                      "oracle_convert_expert"):
                 getattr(lib, f).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -182,3 +189,39 @@ def router_logits(x_bf16: np.ndarray, w_bf16: np.ndarray) -> np.ndarray:
     out = np.empty((n, T, E), dtype=np.float64)
     _check(_load().oracle_router_logits(_p(x), T, H, _p(w), n, E, _p(out)))
     return out
+
+
+# --------------------------------------------------------------------------- #
+# One-time conversion of expert weights ("RFC: stream MoE experts from disk in  #
+# from_pretrained", How the prototype works, Quantized experts bullet)         #
+# --------------------------------------------------------------------------- #
+def round_half(x: float) -> int:
+    """fp16 bit pattern nearest to x (ties to the even pattern)."""
+    return int(_load().oracle_round_half(float(x)))
+
+
+def round_bf16(x: float) -> int:
+    """bf16 bit pattern nearest to x (ties to the even pattern)."""
+    return int(_load().oracle_round_bf16(float(x)))
+
+
+def quantize(w: np.ndarray, bits: int):
+    """Min/max affine quantization of an fp32 [R, C] matrix in groups of 64 along C:
+    (codes uint8 [R, C], scale fp16 bits uint16 [R, C/64], bias fp16 bits uint16 [R, C/64])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    R, C = w.shape
+    q = np.empty((R, C), dtype=np.uint8)
+    s = np.empty((R, C // 64), dtype=np.uint16)
+    z = np.empty((R, C // 64), dtype=np.uint16)
+    _check(_load().oracle_quantize(_p(w), R, C, bits, _p(q), _p(s), _p(z)))
+    return q, s, z
+
+
+def convert_expert(w_gu: np.ndarray, w_d: np.ndarray, H: int, I: int, bits_gu: int, bits_d: int) -> np.ndarray:
+    """One expert's slot row (uint8 [slot_bytes]) from fp32 gate_up [2I, H] and down [H, I]."""
+    a = np.ascontiguousarray(w_gu, dtype=np.float32)
+    b = np.ascontiguousarray(w_d, dtype=np.float32)
+    assert a.shape == (2 * I, H) and b.shape == (H, I)
+    row = np.empty(int(layout(H, I, bits_gu, bits_d)[4]), dtype=np.uint8)
+    _check(_load().oracle_convert_expert(_p(a), _p(b), H, I, bits_gu, bits_d, _p(row)))
+    return row

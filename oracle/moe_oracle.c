@@ -386,3 +386,144 @@ int oracle_router_logits(const uint16_t* x, int T, int H, const uint16_t* w, int
             }
     return OR_OK;
 }
+
+/* ------------------------------------------------------------------------- */
+/* One-time conversion of expert weights into slot rows                       */
+/* ------------------------------------------------------------------------- */
+/*
+ * Source: "RFC: stream MoE experts from disk in from_pretrained", How the
+ * prototype works, Quantized experts bullet: an optional offline pass converts
+ * the experts to the affine quantized format and writes each expert as one
+ * contiguous row.  The pages print no rule for choosing scale and bias; the
+ * reading taken here is plain min/max affine quantization per group of 64
+ * inputs: scale = (max - min) / (2^b - 1) and bias = min, each rounded to the
+ * nearest fp16 (ties to even mantissa), code = (w - bias) / scale rounded to
+ * the nearest integer (ties to even) and clamped to [0, 2^b - 1], computed in
+ * double from the fp16 scale and bias; a group whose fp16 scale is 0 gets code 0.
+ * A minimum of zero is stored as +0.  Width 16 stores the weights rounded to the
+ * nearest bf16 (ties to even).  Weights must be finite.
+ */
+
+/* Nearest value of a 16-bit float format to x, ties to the even bit pattern:
+ * a binary search over the format's non-negative finite patterns, which are
+ * ordered like their values, then the closer neighbour.  dec() decodes a
+ * pattern, top is the largest finite pattern; beyond the largest finite value
+ * plus half its spacing the result is infinity (pattern top + 1). */
+static uint16_t nearest16(double x, double (*dec)(uint16_t), uint16_t top)
+{
+    const uint16_t sign = (x < 0 || (x == 0 && signbit(x))) ? 0x8000u : 0u;
+    const double a = fabs(x);
+    uint16_t lo = 0, hi = top;  /* dec(lo) <= a is kept true where possible */
+    if (a >= dec(top)) {
+        const double spacing = dec(top) - dec((uint16_t)(top - 1));
+        if (a > dec(top) + spacing / 2 || (a == dec(top) + spacing / 2 && (top & 1)))
+            return (uint16_t)(sign | (top + 1));
+        return (uint16_t)(sign | top);
+    }
+    while (hi - lo > 1) {  /* dec(lo) <= a < dec(hi) */
+        uint16_t mid = (uint16_t)((lo + hi) / 2);
+        if (dec(mid) <= a) lo = mid;
+        else hi = mid;
+    }
+    const double dl = a - dec(lo), dh = dec(hi) - a;
+    uint16_t r;
+    if (dl < dh) r = lo;
+    else if (dh < dl) r = hi;
+    else r = (lo & 1) ? hi : lo;
+    return (uint16_t)(sign | r);
+}
+
+uint16_t oracle_round_half(double x) { return nearest16(x, half_to_double, 0x7BFF); }
+uint16_t oracle_round_bf16(double x) { return nearest16(x, bf16_to_double, 0x7F7F); }
+
+/* Group-wise affine quantization of an R x C fp32 matrix (C a multiple of 64):
+ * codes[r][c] (one byte each), scale16 / bias16 [r][c / 64] fp16 patterns. */
+int oracle_quantize(const float* w, int R, int C, int bits, uint8_t* codes, uint16_t* scale16,
+                    uint16_t* bias16)
+{
+    if (!w || !codes || !scale16 || !bias16 || R < 0 || C <= 0 || C % 64) return OR_INVALID;
+    if (!(bits == 3 || bits == 4 || bits == 6 || bits == 8)) return OR_INVALID;
+    const double qmax = (double)((1 << bits) - 1);
+    for (int r = 0; r < R; r++)
+        for (int g = 0; g < C / 64; g++) {
+            const float* v = w + (size_t)r * C + (size_t)g * 64;
+            double mn = v[0], mx = v[0];
+            for (int i = 1; i < 64; i++) {
+                if (v[i] < mn) mn = v[i];
+                if (v[i] > mx) mx = v[i];
+            }
+            const uint16_t s16 = oracle_round_half((mx - mn) / qmax);
+            const uint16_t z16 = oracle_round_half(mn + 0.0);  /* -0 + 0 = +0: one pattern for zero */
+            const double s = half_to_double(s16), z = half_to_double(z16);
+            scale16[(size_t)r * (C / 64) + g] = s16;
+            bias16[(size_t)r * (C / 64) + g] = z16;
+            for (int i = 0; i < 64; i++) {
+                double q = 0.0;
+                if (s != 0.0) {
+                    q = nearbyint(((double)v[i] - z) / s);  /* default mode: ties to even */
+                    if (q < 0) q = 0;
+                    if (q > qmax) q = qmax;
+                }
+                codes[(size_t)r * C + (size_t)g * 64 + i] = (uint8_t)q;
+            }
+        }
+    return OR_OK;
+}
+
+/* Write code q of column c into a code row: bit b of q becomes bit bits*(c%32)+b
+ * of pack unit c/32 read as a little-endian bit string (the inverse of
+ * oracle_code). */
+static void put_code(uint8_t* row, int bits, int c, uint32_t q)
+{
+    uint8_t* unit = row + (size_t)(c / 32) * 4 * (size_t)bits;
+    int first = bits * (c % 32);
+    for (int b = 0; b < bits; b++) {
+        int bit = first + b;
+        if ((q >> b) & 1u) unit[bit / 8] |= (uint8_t)(1u << (bit % 8));
+        else unit[bit / 8] &= (uint8_t)~(1u << (bit % 8));
+    }
+}
+
+/* One matrix into its code block and scale/bias block (scale low half, bias
+ * high half of each little-endian 32-bit word). */
+static int convert_matrix(const float* w, int R, int C, int bits, uint8_t* code_blk, uint8_t* sb_blk)
+{
+    const size_t row_bytes = (size_t)C * bits / 8;
+    if (bits == 16) {
+        for (int r = 0; r < R; r++)
+            for (int c = 0; c < C; c++)
+                put_code(code_blk + (size_t)r * row_bytes, 16, c, oracle_round_bf16(w[(size_t)r * C + c]));
+        return OR_OK;
+    }
+    uint8_t* q = (uint8_t*)malloc((size_t)R * C);
+    uint16_t* s = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)R * (C / 64));
+    uint16_t* z = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)R * (C / 64));
+    int rc = (q && s && z) ? oracle_quantize(w, R, C, bits, q, s, z) : OR_INVALID;
+    if (rc == OR_OK) {
+        for (int r = 0; r < R; r++)
+            for (int c = 0; c < C; c++) put_code(code_blk + (size_t)r * row_bytes, bits, c, q[(size_t)r * C + c]);
+        for (size_t i = 0; i < (size_t)R * (C / 64); i++) {
+            sb_blk[4 * i + 0] = (uint8_t)(s[i] & 0xFF);
+            sb_blk[4 * i + 1] = (uint8_t)(s[i] >> 8);
+            sb_blk[4 * i + 2] = (uint8_t)(z[i] & 0xFF);
+            sb_blk[4 * i + 3] = (uint8_t)(z[i] >> 8);
+        }
+    }
+    free(q);
+    free(s);
+    free(z);
+    return rc;
+}
+
+/* One expert's slot row from fp32 gate_up [2I][H] (gate rows, then up rows) and
+ * down [H][I]; padding between blocks is zero. */
+int oracle_convert_expert(const float* w_gu, const float* w_d, int H, int I, int bits_gu, int bits_d,
+                          uint8_t* row)
+{
+    int64_t offs[5];
+    if (!w_gu || !w_d || !row || oracle_layout(H, I, bits_gu, bits_d, offs)) return OR_INVALID;
+    memset(row, 0, (size_t)offs[4]);
+    int rc = convert_matrix(w_gu, 2 * I, H, bits_gu, row + offs[0], row + offs[1]);
+    if (rc == OR_OK) rc = convert_matrix(w_d, H, I, bits_d, row + offs[2], row + offs[3]);
+    return rc;
+}
