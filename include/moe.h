@@ -144,6 +144,10 @@ extern "C" {
 #define MOE_SRC_HOST    0 /* pinned host memory (hipHostMalloc)                 */
 #define MOE_SRC_DEVICE  1 /* device memory                                      */
 
+/* ---- weight element types of the one-time conversion ---------------------- */
+#define MOE_DTYPE_F32   0
+#define MOE_DTYPE_BF16  1
+
 /*
  * Size class: every expert whose row has the same byte size shares one pool of
  * slots and one LRU ([CLASS] PR description: layers whose experts take the same
@@ -358,6 +362,30 @@ int moe_prefill_pass(int T, int k, int E, int pass_begin, int pass_end, const in
                      uint32_t* err_word, hipStream_t stream);
 int moe_prefill_combine(int T, int k, int E, const float* topk_w, const moe_size_class_desc* d,
                         void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One-time conversion of expert weights into slot rows of class d's format, the
+ * rows a store file holds (see moe_store_open_file) and moe_cache_install copies.
+ * Source: [RFC] "How the prototype works", Quantized experts bullet (an offline
+ * pass converts the experts to the affine quantized format once and writes each
+ * one as a single contiguous row).  The pages print no rule for scale and bias;
+ * this library's reading, per row and group of 64 inputs:
+ *   scale = (max - min) / (2^b - 1), bias = min, each rounded to the nearest fp16
+ *   (ties to the even pattern; a zero minimum is stored as +0);
+ *   code = (w - bias) / scale, computed in double from the fp16 scale and bias,
+ *   rounded to nearest (ties to even) and clamped to [0, 2^b - 1]; 0 where the
+ *   fp16 scale is 0.
+ * Width 16 stores each weight rounded to the nearest bf16 (ties to even).
+ * w_gu: [n_experts, 2I, H] (gate rows 0 .. I-1, then up rows), w_d:
+ * [n_experts, H, I]; both device memory, row-major, element type `dtype`
+ * (MOE_DTYPE_F32 or MOE_DTYPE_BF16), finite with |w| < 65504.
+ * rows: device memory of n_experts * d->slot_bytes bytes, 256-byte aligned,
+ * written whole (zero between blocks).  Asynchronous on `stream`; nothing is
+ * allocated.  MOE_E_INVALID on a bad descriptor, dtype, pointer or alignment;
+ * n_experts = 0 is a no-op.
+ */
+int moe_quantize_experts(const void* w_gu, const void* w_d, int dtype, int n_experts,
+                         const moe_size_class_desc* d, void* rows, hipStream_t stream);
 
 /*
  * Enqueue the copy of one expert row (d->slot_bytes bytes at `src`) into slot

@@ -41,6 +41,8 @@ MOE_PATH_MFMA = 2
 MOE_PATH_GEMV3 = 3
 MOE_SRC_HOST = 0
 MOE_SRC_DEVICE = 1
+MOE_DTYPE_F32 = 0
+MOE_DTYPE_BF16 = 1
 MOE_EVICT_LRU = 0
 MOE_EVICT_LFU = 1
 
@@ -112,6 +114,7 @@ def lib() -> ctypes.CDLL:
                 "moe_prefill_pass": (I32, [I32, I32, I32, I32, I32, P, P, D, P, SZ, P, P]),
                 "moe_prefill_combine": (I32, [I32, I32, I32, P, D, P, P, SZ, P]),
                 "moe_cache_install": (I32, [P, D, I64, P, I32, P, P]),
+                "moe_quantize_experts": (I32, [P, P, I32, I32, D, P, P]),
                 "moe_cache_create": (P, [D, I32, P, I32, I32]),
                 "moe_cache_create_ex": (P, [D, I32, P, I32, I32, I32, I32]),
                 "moe_cache_destroy": (None, [P]),
@@ -420,6 +423,25 @@ def moe_layer_forward_static(logits, x, slot_table, slot_pool, desc: SizeClassDe
         _dev_ptr(topk_w, torch.float32, "topk_w", 2), _dev_ptr(out, torch.bfloat16, "out", 2),
         _opt_ptr(err_word, torch.int32, "err_word"), _stream(stream)))
     return out, topk_ids, topk_w
+
+
+def moe_quantize_experts(w_gu, w_d, desc: SizeClassDesc, out=None, stream=None):
+    """Slot rows (uint8 [n, slot_bytes], device) of n experts from gate_up
+    [n, 2I, H] and down [n, H, I] weights (float32 or bfloat16, device)."""
+    torch = _torch()
+    if w_gu.dtype != w_d.dtype or w_gu.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("weights must both be float32 or both bfloat16")
+    n = w_gu.shape[0]
+    if tuple(w_gu.shape) != (n, 2 * desc.I, desc.H) or tuple(w_d.shape) != (n, desc.H, desc.I):
+        raise ValueError("weights must be [n, 2I, H] and [n, H, I]")
+    if out is None:
+        out = torch.empty((n, desc.slot_bytes), dtype=torch.uint8, device=w_gu.device)
+    elif tuple(out.shape) != (n, desc.slot_bytes):
+        raise ValueError("out must be [n, slot_bytes]")
+    dt = MOE_DTYPE_F32 if w_gu.dtype == torch.float32 else MOE_DTYPE_BF16
+    _check(lib().moe_quantize_experts(_dev_ptr(w_gu, None, "w_gu"), _dev_ptr(w_d, None, "w_d"), dt, n,
+                                      ctypes.byref(desc), _dev_ptr(out, torch.uint8, "out"), _stream(stream)))
+    return out
 
 
 def moe_cache_install(slot_pool, desc: SizeClassDesc, slot: int, src, stream=None, event=None):

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libmoe.so")
 # library of its own, never linked into libmoe.so
 BENCH_SOURCES = ["bench_kernels.hip"]
 BENCH_LIB = os.path.join(HERE, "libmoebench.so")
-SOURCES = ["router.hip", "route.hip", "sort.hip", "gemv.hip", "decode.hip", "decode1.hip", "mfma.hip", "api.cpp", "cache.cpp", "pipeline.cpp"]
+SOURCES = ["router.hip", "route.hip", "sort.hip", "gemv.hip", "decode.hip", "decode1.hip", "mfma.hip", "convert.hip", "api.cpp", "cache.cpp", "pipeline.cpp"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

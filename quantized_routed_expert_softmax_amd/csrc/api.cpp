@@ -534,6 +534,22 @@ int moe_prefill_combine(int T, int k, int E, const float* topk_w, const moe_size
     return MOE_OK;
 }
 
+int moe_quantize_experts(const void* w_gu, const void* w_d, int dtype, int n_experts,
+                         const moe_size_class_desc* d, void* rows, hipStream_t stream)
+{
+    if (int rc = check_desc(d)) return rc;
+    if (dtype != MOE_DTYPE_F32 && dtype != MOE_DTYPE_BF16) return fail(MOE_E_INVALID, "unknown weight dtype %d", dtype);
+    if (n_experts < 0) return fail(MOE_E_INVALID, "n_experts %d < 0", n_experts);
+    if (n_experts == 0) return MOE_OK;
+    if (!w_gu || !w_d || !rows) return fail(MOE_E_INVALID, "NULL buffer");
+    if (((uintptr_t)rows & 255) != 0) return fail(MOE_E_INVALID, "rows must be 256-byte aligned");
+    const size_t el = dtype == MOE_DTYPE_F32 ? 4 : 2;
+    if (((uintptr_t)w_gu | (uintptr_t)w_d) & (el - 1)) return fail(MOE_E_INVALID, "weights not aligned to their element");
+    hipError_t e = moe::launch_convert(w_gu, w_d, dtype == MOE_DTYPE_BF16, n_experts, view_of(d), rows, stream);
+    if (e != hipSuccess) return hip_fail(e, "convert launch");
+    return MOE_OK;
+}
+
 int moe_cache_install(void* slot_pool, const moe_size_class_desc* d, int64_t slot, const void* src,
                       int src_kind, hipStream_t copy_stream, hipEvent_t done)
 {

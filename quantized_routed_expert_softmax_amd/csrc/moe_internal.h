@@ -88,5 +88,8 @@ hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, int pass_lo
                             const uint16_t* hbuf, uint16_t* ybuf, uint32_t* err, hipStream_t s);
 hipError_t launch_combine(const uint16_t* ybuf, const float* topk_w, int T, int k, int H,
                           uint16_t* out, hipStream_t s);
+// one-time conversion: fp32 / bf16 (bf16_in) weights of n experts -> n slot rows
+hipError_t launch_convert(const void* w_gu, const void* w_d, int bf16_in, int64_t n, const ClassView& c,
+                          void* rows, hipStream_t s);
 
 }  // namespace moe
