@@ -418,11 +418,16 @@ void mfma_grouped_kernel(
 //   sb     row r at dwords 2 r, 2 r + 1
 //   a      row m at dwords [64 m, 64 m + 64); its 16-byte chunk c sits in slot
 //          c ^ (m & 15), so the 16 rows read by one lane group spread over the banks
+constexpr int kKC3 = 128;               // inputs per stage of the width-3 kernel
+constexpr int kPPR3 = kKC3 * 3 / 128;    // 16-byte code pieces per row and stage
+constexpr int kGPC3 = kKC3 / 64;         // groups per stage
+constexpr int kCPR3 = kKC3 / 8;          // 16-byte activation chunks per row and stage
+static_assert(kKC3 % 128 == 0, "whole 16-byte code pieces per row");
 template <int NB, int MT>
 struct DmaStage {
-    uint32_t codes[NB * 64 * 12];
-    uint32_t sb[NB * 64 * kGPC];
-    uint32_t a[MT * 16 * (kKC / 2)];
+    uint32_t codes[NB * 64 * 4 * kPPR3];
+    uint32_t sb[NB * 64 * kGPC3];
+    uint32_t a[MT * 16 * (kKC3 / 2)];
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -465,8 +470,8 @@ void mfma_dma3_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const int K = GU ? H : I;
-    const int NC = K / kKC;
-    const bool tail = (K % kKC) != 0;
+    const int NC = K / kKC3;
+    const bool tail = (K % kKC3) != 0;
     const int n_stages = NC + (tail ? 1 : 0);
     const int n0 = cb0 * (GU ? 64 : 128);
 
@@ -479,46 +484,56 @@ void mfma_dma3_kernel(
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
     auto wrow = [&](int r) { return GU ? (r < 64 ? n0 + r : I + n0 + (r - 64)) : min(n0 + r, H - 1); };
 
-    // loads of one stage: code pieces q = 256 i + tid (row q / 3, piece q % 3),
-    // sb dwords q = tid (row q / 2, group q % 2), activation pieces q = 256 i + tid
-    constexpr int BPIECES = ROWS * B;                    // 16-byte code pieces per stage
+    // loads of one stage: code pieces q = 256 i + tid (row q / kPPR3, piece
+    // q % kPPR3), sb dwords q = 256 i + tid (row q / kGPC3, group q % kGPC3),
+    // activation pieces q = 256 i + tid
+    constexpr int BPIECES = ROWS * kPPR3;                // 16-byte code pieces per stage
     constexpr int BPT = (BPIECES + 255) / 256;
-    constexpr int SBN = ROWS * kGPC;                     // sb dwords per stage
-    constexpr int APT = MT * 16 * (kKC / 8) / 256;      // 16-byte activation pieces per thread
+    constexpr int SBN = ROWS * kGPC3;                    // sb dwords per stage
+    constexpr int SBT = (SBN + 255) / 256;
+    constexpr int APT = MT * 16 * kCPR3 / 256;          // 16-byte activation pieces per thread
     static_assert(BPIECES % 64 == 0 && SBN % 64 == 0, "whole waves per load");
     const uint32_t* bsrc[BPT];
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
         const int q = min(256 * i + tid, BPIECES - 1);
-        const int r = q / B;
-        bsrc[i] = codes + (size_t)wrow(r) * row_dw + (q - r * B) * 4;
+        const int r = q / kPPR3;
+        bsrc[i] = codes + (size_t)wrow(r) * row_dw + (q - r * kPPR3) * 4;
     }
-    const uint32_t* ssrc = sbg + (size_t)wrow(min(tid, SBN - 1) >> 1) * (K / 64) + (tid & 1);
+    const uint32_t* ssrc[SBT];
+#pragma unroll
+    for (int i = 0; i < SBT; ++i) {
+        const int q = min(256 * i + tid, SBN - 1);
+        ssrc[i] = sbg + (size_t)wrow(q / kGPC3) * (K / 64) + q % kGPC3;
+    }
     const uint16_t* arow_[APT];  // activation row of each A piece, set per sweep
     // stage kin: piece p of a code row is clamped to 0 past the tail's units (the
     // copy lands in LDS but is never read), likewise the sb group and A chunk
     auto issue = [&](int c, int buf) {
-        const int kin = c * kKC;
-        const int units = (kin + kKC <= K) ? kUPC : (K - kin) / 32;
+        const int kin = c * kKC3;
+        const int units = (kin + kKC3 <= K) ? kKC3 / 32 : (K - kin) / 32;
         DmaStage<NB, MT>& S = st[buf];
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
             if (256 * i + wave * 64 < BPIECES) {  // wave-uniform
                 const int q = 256 * i + tid;
-                const int p = q % B;
+                const int p = q % kPPR3;
                 const uint32_t* src = bsrc[i] + (size_t)(kin / 32) * B;
                 dma16(p * 4 < units * B ? src : src - p * 4, &S.codes[(256 * i + wave * 64) * 4]);
             }
         }
-        if (wave * 64 < SBN) {
-            const int gg = tid & 1;
-            dma4(ssrc + kin / 64 - (gg * 64 < units * 32 ? 0 : gg), &S.sb[wave * 64]);
+#pragma unroll
+        for (int i = 0; i < SBT; ++i) {
+            if (256 * i + wave * 64 < SBN) {  // wave-uniform
+                const int gg = (256 * i + tid) % kGPC3;
+                dma4(ssrc[i] + kin / 64 - (gg * 64 < units * 32 ? 0 : gg), &S.sb[256 * i + wave * 64]);
+            }
         }
 #pragma unroll
         for (int i = 0; i < APT; ++i) {
             const int q = 256 * i + tid;
-            const int m = q >> 4;
-            int ch = (q & 15) ^ (m & 15);       // global chunk held by this slot
+            const int m = q / kCPR3;
+            int ch = (q % kCPR3) ^ (m & 15);    // global chunk held by this slot
             ch = ch * 8 < units * 32 ? ch : 0;
             dma16(arow_[i] + kin + ch * 8, &S.a[(256 * i + wave * 64) * 4]);
         }
@@ -530,7 +545,7 @@ void mfma_dma3_kernel(
         // rows past the expert's last pair re-read its last row (results discarded)
 #pragma unroll
         for (int i = 0; i < APT; ++i) {
-            const int m = min((256 * i + tid) >> 4, rows - 1);
+            const int m = min((256 * i + tid) / kCPR3, rows - 1);
             if (GU) arow_[i] = act + (size_t)(sorted_pairs[base + m0 + m] / k) * H;
             else arow_[i] = act + (size_t)(base + m0 + m) * I;
         }
@@ -547,9 +562,9 @@ void mfma_dma3_kernel(
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const int r = nb * 64 + wave * 16 + c16;
-                bw[nb][0] = lds_pairs<B>(&S.codes[r * 12 + (2 * G2) * B], g);
-                bw[nb][1] = lds_pairs<B>(&S.codes[r * 12 + (2 * G2 + 1) * B], g);
-                const uint32_t s2 = S.sb[r * 2 + G2];
+                bw[nb][0] = lds_pairs<B>(&S.codes[r * 4 * kPPR3 + (2 * G2) * B], g);
+                bw[nb][1] = lds_pairs<B>(&S.codes[r * 4 * kPPR3 + (2 * G2 + 1) * B], g);
+                const uint32_t s2 = S.sb[r * kGPC3 + G2];
                 sc[nb] = half_bits_to_f32(s2 & 0xFFFFu);
                 zc[nb] = __builtin_fmaf(-off, sc[nb], half_bits_to_f32(s2 >> 16));
             }
@@ -557,8 +572,8 @@ void mfma_dma3_kernel(
             for (int mt = 0; mt < MT; ++mt) {
                 if (mt < nmt) {
                     const int m = mt * 16 + c16;  // m & 15 == c16
-                    const u32x4_t a0 = *(const u32x4_t*)(&S.a[m * 64 + (((8 * G2 + g) ^ c16) * 4)]);
-                    const u32x4_t a1 = *(const u32x4_t*)(&S.a[m * 64 + (((8 * G2 + 4 + g) ^ c16) * 4)]);
+                    const u32x4_t a0 = *(const u32x4_t*)(&S.a[m * (kKC3 / 2) + (((8 * G2 + g) ^ c16) * 4)]);
+                    const u32x4_t a1 = *(const u32x4_t*)(&S.a[m * (kKC3 / 2) + (((8 * G2 + 4 + g) ^ c16) * 4)]);
                     f32x4_t tx = mfma(a0, ones, zero);
                     tx = mfma(a1, ones, tx);
 #pragma unroll
@@ -573,11 +588,11 @@ void mfma_dma3_kernel(
             }
         };
         auto compute_stage = [&](const DmaStage<NB, MT>& S, int c) __attribute__((always_inline)) {
-            const int kin = c * kKC;
-            const int groups = (kin + kKC <= K) ? kGPC : (K - kin) / 64;
-            if (GU && groups == kGPC) {  // gate/up: both groups in one block for the scheduler
+            const int kin = c * kKC3;
+            const int groups = (kin + kKC3 <= K) ? kGPC3 : (K - kin) / 64;
+            if (GU && groups == kGPC3) {  // gate/up: the stage's groups in one block for the scheduler
 #pragma unroll
-                for (int G2 = 0; G2 < kGPC; ++G2) compute_group(S, G2);
+                for (int G2 = 0; G2 < kGPC3; ++G2) compute_group(S, G2);
             } else {
                 for (int G2 = 0; G2 < groups; ++G2) compute_group(S, G2);
             }
