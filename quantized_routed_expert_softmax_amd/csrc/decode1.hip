@@ -602,6 +602,8 @@ const D1Variant kD1Variants[] = {
     MOE_D1(3, 3, 16, 1, 10),  // hidden 2048, intermediate 512, 3-bit
     MOE_D1(4, 4, 16, 1, 10),
     MOE_D1(8, 8, 16, 1, 10),
+    MOE_D1(4, 4, 8, 3, 8),    // hidden 2048, intermediate 768, 4-bit
+    MOE_D1(4, 6, 8, 3, 8),    // ... with 6-bit down
 };
 #undef MOE_D1
 

@@ -443,6 +443,16 @@ def test_forward_mixed_classes_full_size(T, layer):
         out, ew = forward_dev(dev_bf16(x), ids, w, wl.E, to_dev(table), pool, lay, path)
         assert ew == 0
         check_close(out, ref, f"mixed layer {layer} T {T} path {path}")
+    # router + experts in one launch (one token: the one-token kernel routes itself)
+    desc = B.moe_size_class_init(lay.H, lay.I, bg, bd, wl.slots_per_layer)
+    ew = err_word()
+    out, ids_l, w_l = B.moe_layer_forward(to_dev(lg), dev_bf16(x), to_dev(table), pool.view(-1), desc, wl.k,
+                                          err_word=ew)
+    _torch().cuda.synchronize()
+    assert int(ew.item()) == 0
+    assert np.array_equal(ids_l.cpu().numpy(), ids_o)
+    assert np.array_equal(w_l.cpu().numpy().view(np.uint32), w_o.view(np.uint32))
+    check_close(out, ref, f"mixed layer {layer} T {T} moe_layer_forward")
 
 
 def test_int8_substitution_with_installs_full_size():
