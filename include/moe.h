@@ -534,10 +534,7 @@ int     moe_store_read(const moe_store* s, int layer, int expert, void* dst);
  *   caller-owned, default priority, not the compute stream) carry the install
  *   copies: every copy that reads one host row or staging buffer runs on that
  *   buffer's stream, and rows spread over the streams so copies overlap each
- *   other.  Two is the measured optimum on MI355X with the runtime's default of
- *   four hardware queues per process (the compute and default streams take the
- *   other two): 1.38 MB rows install at ~35 GB/s on one stream, ~48 GB/s on two
- *   and ~7.5 GB/s on four, where streams share queues.  The current device is the pools' device.  The cache and store stay owned by the caller and must outlive the
+ *   other.  The current device is the pools' device.  The cache and store stay owned by the caller and must outlive the
  *   pipeline; while it exists only the pipeline acquires, fills or pins entries of
  *   that cache.  NULL on error.
  * moe_pipeline_prepare: make the experts `ids[0..n)` (duplicates allowed) of
