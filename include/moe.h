@@ -538,7 +538,10 @@ int     moe_store_read(const moe_store* s, int layer, int expert, void* dst);
  *   pipeline; while it exists only the pipeline acquires, fills or pins entries of
  *   that cache.  NULL on error.
  * moe_pipeline_prepare: make the experts `ids[0..n)` (duplicates allowed) of
- *   `layer` resident for a forward about to be enqueued on `compute`.  Hits are
+ *   `layer` resident for a forward about to be enqueued on `compute`.  The
+ *   distinct ids are acquired in the reverse of their first appearance (ascending
+ *   experts then land in ascending slots, and their host-tier installs merge into
+ *   one copy per run of consecutive rows and slots).  Hits are
  *   touched; each miss takes the class's LRU victim, is copied from its host row
  *   (inline) or read from the store on an I/O thread, then copied on the copy
  *   stream after the copy stream has waited for the last forward that read the

@@ -239,6 +239,14 @@ struct SlotState {
     bool failed = false;   // the store read of the last install failed
 };
 
+// A host-tier install of a prepare whose copy is enqueued after the prepare's
+// acquisitions, merged with its neighbours (see flush_deferred).
+struct Deferred {
+    int layer, expert;
+    int64_t row, slot;
+    int use_ev;
+};
+
 enum JobKind { kInstall, kPreload };
 
 struct Job {
@@ -339,6 +347,79 @@ struct moe_pipeline {
         return i;
     }
 
+    // One copy of n consecutive host rows into n consecutive slots on copy stream
+    // q, after the stream waited for the use events of every victim slot; one
+    // fill-ring entry for all of them, or -1 on a HIP error.
+    int enqueue_run(int q, int cls, int64_t s0, int64_t n, const uint8_t* src, const std::vector<int>& use_evs)
+    {
+        std::lock_guard<std::mutex> g(copy_mu[q]);
+        const hipStream_t st = copies[(size_t)q];
+        for (int use_ev : use_evs) {
+            if (use_ev < 0) continue;
+            const uint64_t gen = __atomic_load_n(&use_gen[use_ev], __ATOMIC_ACQUIRE);
+            if (last_wait[q] != use_ev || last_wait_gen[q] != gen) {
+                if (hipStreamWaitEvent(st, use_ring[use_ev], 0) != hipSuccess) return -1;
+                last_wait[q] = use_ev;
+                last_wait_gen[q] = gen;
+            }
+        }
+        if (hipMemcpyAsync(slot_ptr(cls, s0), src, (size_t)n * (size_t)desc[cls].slot_bytes,
+                           hipMemcpyHostToDevice, st) != hipSuccess)
+            return -1;
+        const int i = q * kFillRing + (int)(fill_next[q]++ % kFillRing);
+        if (hipEventRecord(fill_ring[i], st) != hipSuccess) return -1;
+        return i;
+    }
+
+    // Enqueue a prepare's deferred host-tier installs: sorted by host row, each
+    // run of consecutive rows going to consecutive slots becomes one copy (a
+    // prefill pass of consecutive experts whose rows sit in order in the host
+    // tier is one or a few large copies instead of 64 of 1.38 MB, each of which
+    // pays the copy engine's per-copy cost).  Caller holds mu (released while
+    // enqueueing); the rows keep a reader and the slots stay pending until done.
+    void flush_deferred(std::unique_lock<std::mutex>& lk, int cls, std::vector<Deferred>& d)
+    {
+        if (d.empty()) return;
+        std::sort(d.begin(), d.end(), [](const Deferred& a, const Deferred& b) { return a.row < b.row; });
+        struct Run {
+            size_t first, n;
+            int ev;
+        };
+        std::vector<Run> runs;
+        for (size_t i = 0; i < d.size(); ++i) {
+            if (!runs.empty()) {
+                const Deferred& prev = d[i - 1];
+                if (d[i].row == prev.row + 1 && d[i].slot == prev.slot + 1) {
+                    runs.back().n++;
+                    continue;
+                }
+            }
+            runs.push_back(Run{i, 1, -1});
+        }
+        lk.unlock();
+        for (Run& run : runs) {
+            const Deferred& f = d[run.first];
+            std::vector<int> use_evs;
+            for (size_t i = run.first; i < run.first + run.n; ++i)
+                if (std::find(use_evs.begin(), use_evs.end(), d[i].use_ev) == use_evs.end()) use_evs.push_back(d[i].use_ev);
+            run.ev = enqueue_run(row_queue(f.row), cls, f.slot, (int64_t)run.n, host_ptr(cls, f.row), use_evs);
+        }
+        lk.lock();
+        for (const Run& run : runs)
+            for (size_t i = run.first; i < run.first + run.n; ++i) {
+                HostRow& row = host[cls].row[(size_t)d[i].row];
+                row.readers--;
+                if (run.ev >= 0) row.ev = run.ev;
+                else if (!io_error) io_error = MOE_E_HIP;
+                moe_pipeline_stats& st = stats[cls];
+                st.host_hits++;
+                if (run.ev >= 0) st.bytes_copied += desc[cls].slot_bytes;
+                finish_install(d[i].layer, d[i].expert, cls, d[i].slot, run.ev);
+            }
+        d.clear();
+        cv_done.notify_all();
+    }
+
     void sync_copies()
     {
         for (hipStream_t st : copies) hipStreamSynchronize(st);
@@ -400,15 +481,20 @@ struct moe_pipeline {
     }
 
     // Try the host tier for an install.  Caller holds mu; returns true when the
-    // row is present (the copy is then enqueued here, with mu released meanwhile).
+    // row is present (the copy is then enqueued here, with mu released meanwhile,
+    // or, given `defer`, recorded there for flush_deferred).
     bool install_from_host(std::unique_lock<std::mutex>& lk, int layer, int expert, int cls, int64_t s,
-                           int use_ev)
+                           int use_ev, std::vector<Deferred>* defer = nullptr)
     {
         if (host.empty() || host[cls].rows == 0) return false;
         const int64_t r = host_of[(size_t)layer * E + expert];
         if (r < 0 || host[cls].row[(size_t)r].loading) return false;
         host[cls].row[(size_t)r].readers++;
         host_touch(cls, r);
+        if (defer) {
+            defer->push_back(Deferred{layer, expert, r, s, use_ev});
+            return true;
+        }
         lk.unlock();
         const int ev = enqueue_copy(row_queue(r), cls, s, host_ptr(cls, r), use_ev);
         lk.lock();
@@ -532,14 +618,15 @@ struct moe_pipeline {
     }
 
     // Accept a device miss of (layer, expert) into slot s.  Caller holds mu.
-    void start_install(std::unique_lock<std::mutex>& lk, int layer, int expert, int64_t s, bool guess)
+    void start_install(std::unique_lock<std::mutex>& lk, int layer, int expert, int64_t s, bool guess,
+                       std::vector<Deferred>* defer = nullptr)
     {
         const int cls = cls_of(layer);
         SlotState& ss = slot[cls][(size_t)s];
         ss.pending = true;
         ss.failed = false;
         const int use_ev = ss.use_ev;
-        if (install_from_host(lk, layer, expert, cls, s, use_ev)) return;
+        if (install_from_host(lk, layer, expert, cls, s, use_ev, defer)) return;
         jobs.push_back(Job{kInstall, layer, expert, cls, s, use_ev, guess, -1});
         cv_jobs.notify_one();
     }
@@ -799,8 +886,14 @@ int moe_pipeline_prepare(moe_pipeline* p, int layer, const int32_t* ids, int n, 
     Held& h = p->held[(size_t)layer];
     if (h.active) return pfail(MOE_E_BUSY, "moe_pipeline_prepare: layer prepared and not yet released");
     const int cls = p->cls_of(layer);
-    const std::vector<int> want = distinct(ids, n, p->E);
+    // experts are acquired last first: the class hands out victims in LRU order
+    // and empty slots last-created first, so a run of ascending experts (a
+    // prefill pass) lands in ascending slots, next to each other like their
+    // host-tier rows, and its installs merge into few copies
+    std::vector<int> want = distinct(ids, n, p->E);
+    std::reverse(want.begin(), want.end());
     std::vector<int64_t> waits;
+    std::vector<Deferred> deferred;
     std::unique_lock<std::mutex> lk(p->mu);
     if (p->io_error) return pfail(p->io_error, "moe_pipeline_prepare: an earlier install failed");
     h.active = true;
@@ -813,11 +906,13 @@ int moe_pipeline_prepare(moe_pipeline* p, int layer, const int32_t* ids, int n, 
         // complete between the cache's check and ours, so when nothing is left in
         // flight the cache is asked once more before the class counts as full.
         while (rc == MOE_E_NO_SLOT) {
+            p->flush_deferred(lk, cls, deferred);  // what waits may be this prepare's own installs
             const bool waited = p->wait_oldest_fill(lk, cls);
             rc = moe_cache_acquire(p->cache, layer, e, &s, &needs_fill);
             if (!waited) break;
         }
         if (rc != MOE_OK && rc != MOE_E_BUSY) {
+            p->flush_deferred(lk, cls, deferred);
             lk.unlock();
             p->unpin_all(layer);
             return pfail(rc, "moe_pipeline_prepare: no free slot in the layer's size class");
@@ -833,10 +928,11 @@ int moe_pipeline_prepare(moe_pipeline* p, int layer, const int32_t* ids, int n, 
         } else if (!needs_fill) {
             st.hits++;
         } else {
-            p->start_install(lk, layer, e, s, false);
+            p->start_install(lk, layer, e, s, false, &deferred);
             waits.push_back(s);
         }
     }
+    p->flush_deferred(lk, cls, deferred);
     // every install this layer needs has its copy enqueued (or failed)
     p->cv_done.wait(lk, [&] {
         for (int64_t s : waits)

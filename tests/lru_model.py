@@ -89,14 +89,20 @@ class CacheModel:
     def acquire(self, layer: int, expert: int, pinned=frozenset()):
         return self.layer_part[layer].acquire((layer, expert), pinned)
 
-    def prepare(self, layer: int, ids) -> list[tuple[int, int, bool]]:
-        """Acquire the distinct ids of one layer in order of first appearance; the
-        ones acquired earlier in the same call are pinned.  Returns (expert, slot, miss)."""
-        seen, out, pinned = set(), [], set()
+    def prepare(self, layer: int, ids, last_first: bool = False) -> list[tuple[int, int, bool]]:
+        """Acquire the distinct ids of one layer in order of first appearance (or,
+        with last_first, in the reverse of that order, as the miss pipeline does);
+        the ones acquired earlier in the same call are pinned.  Returns (expert,
+        slot, miss)."""
+        seen, order = set(), []
         for e in (int(v) for v in np.asarray(ids).reshape(-1)):
-            if e in seen:
-                continue
-            seen.add(e)
+            if e not in seen:
+                seen.add(e)
+                order.append(e)
+        if last_first:
+            order.reverse()
+        out, pinned = [], set()
+        for e in order:
             slot, miss = self.acquire(layer, e, frozenset(pinned))
             pinned.add((layer, e))
             out.append((e, slot, miss))

@@ -123,7 +123,7 @@ def run_pipeline(rp: Replay, ids, ws, ids_host, store, host_tier_bytes=0, preloa
                 c = rp.layer_class[l]
                 B.moe_pipeline_prepare(p, l, ids_host[j], table)
                 if model is not None:
-                    model.prepare(l, ids_host[j])
+                    model.prepare(l, ids_host[j], last_first=True)
                 if prefetch and j + 1 < len(ids_host):   # a perfect guess of the next layer
                     B.moe_pipeline_prefetch(p, (l + 1) % rp.L, ids_host[j + 1])
                 x = B.moe_experts_forward(x, ids[j], ws[j], E, table, pools[c], rp.classes[c], ws=ws_buf)
