@@ -30,10 +30,10 @@
 // down: y per (pair, output) in bf16 to a workspace; a combine kernel adds the
 // k contributions of each token in j order (deterministic).
 //
-// Width 3 runs mfma_dma3_kernel instead: the same arithmetic with each stage
-// loaded straight into LDS (no staging registers), and down with 128 output
-// columns per workgroup.  Width 16 stages 64 inputs at a time (its rows are
-// four times wider than 3-bit rows).
+// Widths 3, 4, 6 and 8 run mfma_lds_kernel instead: the same arithmetic with
+// each stage loaded straight into LDS (no staging registers), and down with 128
+// output columns per workgroup.  Width 16 runs mfma_grouped_kernel, staging 64
+// inputs at a time (its rows are four times wider than 3-bit rows).
 #include <utility>
 
 #include "../../include/moe.h"
@@ -406,7 +406,7 @@ void mfma_grouped_kernel(
 #undef wrow
 }
 
-// Width 3: the same grouped GEMM with the stages moved from global memory
+// Widths 3, 4, 6, 8: the same grouped GEMM with the stages moved from global memory
 // straight into LDS (global_load_lds_dwordx4 / _dword: lane i of a load writes
 // 16 or 4 bytes at the wave's LDS base + 16 i or 4 i).  No staging registers
 // and no VALU copies into LDS: gate/up spends the registers saved on both
@@ -414,18 +414,26 @@ void mfma_grouped_kernel(
 // workgroup (128 weight rows, like gate and up), so each wave carries two
 // independent chains and one staging of the h rows serves both.  Two LDS
 // buffers: stage c + 1 lands while stage c is consumed.  Layouts in a buffer:
-//   codes  row r at dwords [12 r, 12 r + 12): the row's 3 pieces of 16 bytes
+//   codes  row r at 16-byte slots [S r, S r + B): the row's B pieces (S = B, or
+//          B + 1 for even B, see row_slots)
 //   sb     row r at dwords 2 r, 2 r + 1
 //   a      row m at dwords [64 m, 64 m + 64); its 16-byte chunk c sits in slot
 //          c ^ (m & 15), so the 16 rows read by one lane group spread over the banks
-constexpr int kKC3 = 128;               // inputs per stage of the width-3 kernel
-constexpr int kPPR3 = kKC3 * 3 / 128;    // 16-byte code pieces per row and stage
+constexpr int kKC3 = 128;               // inputs per stage of the LDS-loading kernel
 constexpr int kGPC3 = kKC3 / 64;         // groups per stage
 constexpr int kCPR3 = kKC3 / 8;          // 16-byte activation chunks per row and stage
 static_assert(kKC3 % 128 == 0, "whole 16-byte code pieces per row");
-template <int NB, int MT>
+// 16-byte code pieces per row and stage, and the LDS slots a staged row takes:
+// one more (never loaded) for widths whose piece count is even, so that the 16
+// rows a lane group reads start on 16 distinct banks (a row stride of 3, 5, 7
+// or 9 pieces; 4, 6 or 8 would put several rows on one bank)
+template <int B>
+constexpr int ppr() { return kKC3 * B / 128; }
+template <int B>
+constexpr int row_slots() { return ppr<B>() % 2 ? ppr<B>() : ppr<B>() + 1; }
+template <int B, int NB, int MT>
 struct DmaStage {
-    uint32_t codes[NB * 64 * 4 * kPPR3];
+    uint32_t codes[NB * 64 * 4 * row_slots<B>()];
     uint32_t sb[NB * 64 * kGPC3];
     uint32_t a[MT * 16 * (kKC3 / 2)];
 };
@@ -441,19 +449,19 @@ __device__ __forceinline__ void dma4(const void* g, void* lds_wave_base)
     __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_wave_base, 4, 0, 0);
 }
 
-template <bool GU, int MT>
+template <int B, bool GU, int MT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 2 ? (GU ? 3 : 4) : 1)))
-void mfma_dma3_kernel(
+void mfma_lds_kernel(
     const uint16_t* __restrict__ act, int H, int I, int k, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table, int E,
     int pass_lo, int pass_hi, const int32_t* __restrict__ table, const uint8_t* __restrict__ pool,
     int64_t n_slots, int64_t slot_bytes, int64_t off_codes, int64_t off_sb,
     uint16_t* __restrict__ hbuf, uint16_t* __restrict__ ybuf, uint32_t* __restrict__ err)
 {
-    constexpr int B = 3;
     constexpr int NB = 2;  // gate and up / two blocks of 64 down columns
     constexpr int ROWS = NB * 64;
-    __shared__ DmaStage<NB, MT> st[2];
+    __shared__ DmaStage<B, NB, MT> st[2];
+    constexpr int PPR = ppr<B>(), RS = row_slots<B>();
     // tile order as in mfma_grouped_kernel (one column block per workgroup)
     const int ncb = GU ? I / 64 : (H / 64 + 1) / 2;
     const int L = blockIdx.x, r8 = L >> 3;
@@ -484,10 +492,10 @@ void mfma_dma3_kernel(
     const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
     auto wrow = [&](int r) { return GU ? (r < 64 ? n0 + r : I + n0 + (r - 64)) : min(n0 + r, H - 1); };
 
-    // loads of one stage: code pieces q = 256 i + tid (row q / kPPR3, piece
-    // q % kPPR3), sb dwords q = 256 i + tid (row q / kGPC3, group q % kGPC3),
-    // activation pieces q = 256 i + tid
-    constexpr int BPIECES = ROWS * kPPR3;                // 16-byte code pieces per stage
+    // loads of one stage: code slots q = 256 i + tid (row q / RS, piece q % RS;
+    // the padding slot is not loaded), sb dwords q = 256 i + tid (row q / kGPC3,
+    // group q % kGPC3), activation pieces q = 256 i + tid
+    constexpr int BPIECES = ROWS * RS;                   // 16-byte code slots per stage
     constexpr int BPT = (BPIECES + 255) / 256;
     constexpr int SBN = ROWS * kGPC3;                    // sb dwords per stage
     constexpr int SBT = (SBN + 255) / 256;
@@ -497,8 +505,8 @@ void mfma_dma3_kernel(
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
         const int q = min(256 * i + tid, BPIECES - 1);
-        const int r = q / kPPR3;
-        bsrc[i] = codes + (size_t)wrow(r) * row_dw + (q - r * kPPR3) * 4;
+        const int r = q / RS;
+        bsrc[i] = codes + (size_t)wrow(r) * row_dw + min(q - r * RS, PPR - 1) * 4;
     }
     const uint32_t* ssrc[SBT];
 #pragma unroll
@@ -512,14 +520,14 @@ void mfma_dma3_kernel(
     auto issue = [&](int c, int buf) {
         const int kin = c * kKC3;
         const int units = (kin + kKC3 <= K) ? kKC3 / 32 : (K - kin) / 32;
-        DmaStage<NB, MT>& S = st[buf];
+        DmaStage<B, NB, MT>& S = st[buf];
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
             if (256 * i + wave * 64 < BPIECES) {  // wave-uniform
                 const int q = 256 * i + tid;
-                const int p = q % kPPR3;
+                const int p = q % RS;
                 const uint32_t* src = bsrc[i] + (size_t)(kin / 32) * B;
-                dma16(p * 4 < units * B ? src : src - p * 4, &S.codes[(256 * i + wave * 64) * 4]);
+                if (p < PPR) dma16(p * 4 < units * B ? src : src - p * 4, &S.codes[(256 * i + wave * 64) * 4]);
             }
         }
 #pragma unroll
@@ -556,14 +564,14 @@ void mfma_dma3_kernel(
             for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = zero;
 
         // one group of 64 inputs of the stage in LDS: B operands, then the matrix cores
-        auto compute_group = [&](const DmaStage<NB, MT>& S, int G2) __attribute__((always_inline)) {
+        auto compute_group = [&](const DmaStage<B, NB, MT>& S, int G2) __attribute__((always_inline)) {
             u32x4_t bw[NB][2];
             float sc[NB], zc[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const int r = nb * 64 + wave * 16 + c16;
-                bw[nb][0] = lds_pairs<B>(&S.codes[r * 4 * kPPR3 + (2 * G2) * B], g);
-                bw[nb][1] = lds_pairs<B>(&S.codes[r * 4 * kPPR3 + (2 * G2 + 1) * B], g);
+                bw[nb][0] = lds_pairs<B>(&S.codes[r * 4 * RS + (2 * G2) * B], g);
+                bw[nb][1] = lds_pairs<B>(&S.codes[r * 4 * RS + (2 * G2 + 1) * B], g);
                 const uint32_t s2 = S.sb[r * kGPC3 + G2];
                 sc[nb] = half_bits_to_f32(s2 & 0xFFFFu);
                 zc[nb] = __builtin_fmaf(-off, sc[nb], half_bits_to_f32(s2 >> 16));
@@ -587,7 +595,7 @@ void mfma_dma3_kernel(
                 }
             }
         };
-        auto compute_stage = [&](const DmaStage<NB, MT>& S, int c) __attribute__((always_inline)) {
+        auto compute_stage = [&](const DmaStage<B, NB, MT>& S, int c) __attribute__((always_inline)) {
             const int kin = c * kKC3;
             const int groups = (kin + kKC3 <= K) ? kGPC3 : (K - kin) / 64;
             if (GU && groups == kGPC3) {  // gate/up: the stage's groups in one block for the scheduler
@@ -721,16 +729,16 @@ hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const Sor
                        sv.offsets, sv.sorted_pairs, sv.pass_table, E, pass_lo, pass_hi, table, pool, c.n_slots,         \
                        c.slot_bytes, c.off_gu_codes, c.off_gu_sb, hbuf, nullptr, err)
 #define MOE_MG2(BB) { if (mt == 4) MOE_MG(BB, 4); else MOE_MG(BB, 2); }
-#define MOE_MG3(MM)                                                                                \
-    hipLaunchKernelGGL((mfma_dma3_kernel<true, MM>), dim3((unsigned)((c.I / 64) * ((max_hit + 7) / 8) * 8)), \
+#define MOE_MG3(BB, MM)                                                                            \
+    hipLaunchKernelGGL((mfma_lds_kernel<BB, true, MM>), dim3((unsigned)((c.I / 64) * ((max_hit + 7) / 8) * 8)), \
                        dim3(256), 0, s, xp, c.H, c.I, k, sv.offsets, sv.sorted_pairs, sv.pass_table, \
                        E, pass_lo, pass_hi, table, pool, c.n_slots, c.slot_bytes, c.off_gu_codes, c.off_gu_sb, hbuf,    \
                        nullptr, err)
     switch (c.bits_gu) {
-    case 3: if (mt == 4) MOE_MG3(4); else MOE_MG3(2); break;
-    case 4: MOE_MG2(4); break;
-    case 6: MOE_MG2(6); break;
-    case 8: MOE_MG2(8); break;
+    case 3: if (mt == 4) MOE_MG3(3, 4); else MOE_MG3(3, 2); break;
+    case 4: if (mt == 4) MOE_MG3(4, 4); else MOE_MG3(4, 2); break;
+    case 6: if (mt == 4) MOE_MG3(6, 4); else MOE_MG3(6, 2); break;
+    case 8: if (mt == 4) MOE_MG3(8, 4); else MOE_MG3(8, 2); break;
     case 16: MOE_MG2(16); break;
     default: return hipErrorInvalidValue;
     }
@@ -753,16 +761,16 @@ hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, int pass_lo
                        k, sv.offsets, sv.sorted_pairs, sv.pass_table, E, pass_lo, pass_hi, table, pool, c.n_slots,      \
                        c.slot_bytes, c.off_d_codes, c.off_d_sb, nullptr, ybuf, err)
 #define MOE_MD2(BB) { if (mt == 4) MOE_MD(BB, 4); else MOE_MD(BB, 2); }
-#define MOE_MD3(MM)                                                                                \
-    hipLaunchKernelGGL((mfma_dma3_kernel<false, MM>), dim3((unsigned)(((c.H / 64 + 1) / 2) * ((max_hit + 7) / 8) * 8)), \
+#define MOE_MD3(BB, MM)                                                                            \
+    hipLaunchKernelGGL((mfma_lds_kernel<BB, false, MM>), dim3((unsigned)(((c.H / 64 + 1) / 2) * ((max_hit + 7) / 8) * 8)), \
                        dim3(256), 0, s, hbuf, c.H, c.I, k, sv.offsets, sv.sorted_pairs, sv.pass_table, \
                        E, pass_lo, pass_hi, table, pool, c.n_slots, c.slot_bytes, c.off_d_codes, c.off_d_sb, nullptr,  \
                        ybuf, err)
     switch (c.bits_d) {
-    case 3: if (mt == 4) MOE_MD3(4); else MOE_MD3(2); break;
-    case 4: MOE_MD2(4); break;
-    case 6: MOE_MD2(6); break;
-    case 8: MOE_MD2(8); break;
+    case 3: if (mt == 4) MOE_MD3(3, 4); else MOE_MD3(3, 2); break;
+    case 4: if (mt == 4) MOE_MD3(4, 4); else MOE_MD3(4, 2); break;
+    case 6: if (mt == 4) MOE_MD3(6, 4); else MOE_MD3(6, 2); break;
+    case 8: if (mt == 4) MOE_MD3(8, 4); else MOE_MD3(8, 2); break;
     case 16: MOE_MD2(16); break;
     default: return hipErrorInvalidValue;
     }
