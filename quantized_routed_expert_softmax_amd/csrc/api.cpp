@@ -359,8 +359,9 @@ int moe_experts_forward_ex(const void* x, int T, const int32_t* topk_ids, const 
         if (e != hipSuccess) return hip_fail(e, "fused decode launch");
         return MOE_OK;
     }
-    e = moe::launch_sort(topk_ids, T, k, E, kPassExperts, offsets, sorted, pass,
-                                    w + L.sort_ws, err_word, stream);
+    const bool mfma = !(path == MOE_PATH_GEMV || path == MOE_PATH_GEMV3);
+    e = moe::launch_sort(topk_ids, T, k, E, kPassExperts, offsets, sorted, pass, w + L.sort_ws, err_word,
+                         stream, mfma ? (const uint16_t*)x : nullptr, c.H, (uint16_t*)(w + L.xp));
     if (e != hipSuccess) return hip_fail(e, "sort launch");
     moe::SortView sv{offsets, sorted, pass};
     if (path == MOE_PATH_GEMV || path == MOE_PATH_GEMV3) {
@@ -372,9 +373,8 @@ int moe_experts_forward_ex(const void* x, int T, const int32_t* topk_ids, const 
         if (e != hipSuccess) return hip_fail(e, "gemv down launch");
         return MOE_OK;
     }
-    // MFMA: every pass in one launch pair (the whole hit list is resident)
-    e = moe::launch_permute_x((const uint16_t*)x, T, c.H, (uint16_t*)(w + L.xp), stream);
-    if (e != hipSuccess) return hip_fail(e, "permute launch");
+    // MFMA: every pass in one launch pair (the whole hit list is resident; x
+    // was permuted by the sort's launch)
     if (int rc = run_passes(T, k, E, 0, n_pass_max(E), slot_table, pool, c, L, w, err_word, stream))
         return rc;
     e = moe::launch_combine((const uint16_t*)(w + L.ybuf), topk_w, T, k, c.H, (uint16_t*)out, stream);
@@ -497,10 +497,8 @@ int moe_prefill_sort(const void* x, int T, const int32_t* topk_ids, int k, int E
     char* w = (char*)ws;
     hipError_t e = moe::launch_sort(topk_ids, T, k, E, kPassExperts, (int32_t*)(w + L.offsets),
                                     (int32_t*)(w + L.sorted), (int32_t*)(w + L.pass), w + L.sort_ws,
-                                    err_word, stream);
+                                    err_word, stream, (const uint16_t*)x, d->H, (uint16_t*)(w + L.xp));
     if (e != hipSuccess) return hip_fail(e, "sort launch");
-    e = moe::launch_permute_x((const uint16_t*)x, T, d->H, (uint16_t*)(w + L.xp), stream);
-    if (e != hipSuccess) return hip_fail(e, "permute launch");
     return MOE_OK;
 }
 

@@ -648,18 +648,6 @@ void mfma_lds_kernel(
     }
 }
 
-// x [T, H] bf16 -> P16 layout: within each 32-chunk, position 2i+h holds input i+16h.
-__global__ __launch_bounds__(256) void permute_x_kernel(const uint16_t* __restrict__ x, int64_t n_dw,
-                                                        uint32_t* __restrict__ xp)
-{
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // output dword
-    if (q >= n_dw) return;
-    const int64_t chunk = q >> 4;
-    const int i = (int)(q & 15);
-    const uint16_t* src = x + chunk * 32;
-    xp[q] = (uint32_t)src[i] | ((uint32_t)src[i + 16] << 16);
-}
-
 // out[t, n] = bf16( sum_j w[t, j] * y[t*k + j, n] ), j ascending, in fp32 (y is
 // stored in bf16, like h: the weighted sum of the k expert outputs is the only
 // place they meet).
@@ -688,15 +676,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 }
 
 }  // namespace
-
-hipError_t launch_permute_x(const uint16_t* x, int T, int H, uint16_t* xp, hipStream_t s)
-{
-    const int64_t n_dw = (int64_t)T * H / 2;
-    const int64_t blocks = (n_dw + 255) / 256;
-    hipLaunchKernelGGL(permute_x_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n_dw,
-                       (uint32_t*)xp);
-    return hipGetLastError();
-}
 
 // Most hit experts passes [pass_lo, pass_hi) can hold: kPassExperts each, and no
 // more than the distinct experts the T*k pairs can reach.

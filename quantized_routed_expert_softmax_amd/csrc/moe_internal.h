@@ -43,9 +43,12 @@ hipError_t launch_router_logits(const uint16_t* x, int T, int H, const uint16_t*
                                 float* logits, hipStream_t s);
 
 size_t sort_ws_bytes(int T, int k, int E);
+// x_perm (may be null): also write x [T, H] in the P16 layout of the MFMA path
+// to xp, by extra workgroups of the sort's first launch (independent work, one
+// launch fewer than a separate permute)
 hipError_t launch_sort(const int32_t* ids, int T, int k, int E, int P, int32_t* offsets,
                        int32_t* sorted_pairs, int32_t* pass_table, void* ws, uint32_t* err,
-                       hipStream_t s);
+                       hipStream_t s, const uint16_t* x_perm = nullptr, int H = 0, uint16_t* xp = nullptr);
 
 // Decode path: dequant-GEMV gate/up + SwiGLU, then down + weighted combine.
 hipError_t launch_gemv_gateup(const uint16_t* x, int T, int k, int E, const SortView& sv,
@@ -75,9 +78,8 @@ hipError_t launch_decode1(const float* logits, const int32_t* ids_in, const floa
                           const uint8_t* pool, const ClassView& c, uint16_t* out, void* reserved,
                           uint32_t* err, hipStream_t s);
 
-// Prefill path: P16-permuted x, MFMA gate/up + SwiGLU, MFMA down (y in bf16),
-// combine (fp32 sum in j order).
-hipError_t launch_permute_x(const uint16_t* x, int T, int H, uint16_t* xp, hipStream_t s);
+// Prefill path: P16-permuted x (written by launch_sort's launch), MFMA gate/up +
+// SwiGLU, MFMA down (y in bf16), combine (fp32 sum in j order).
 // Both run the hit experts of passes [pass_lo, pass_hi) of the pass table only
 // (0 and ceil(E / kPassExperts) for every hit expert).
 hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const SortView& sv,

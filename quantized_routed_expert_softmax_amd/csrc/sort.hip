@@ -14,6 +14,8 @@
 //   n >  1024 : tile kernel (per-tile counts and in-tile ranks), one block that
 //               turns the counts into per-tile bases, offsets and the pass table,
 //               and a scatter kernel with one thread per pair.
+// The MFMA path's permute of x rides along in extra workgroups of the first
+// launch (it does not depend on the sort).
 #include "../../include/moe.h"
 #include "moe_internal.h"
 
@@ -22,6 +24,19 @@ namespace {
 
 constexpr int kTile = 256;
 constexpr int kSmallMax = 1024;
+
+// Dword q of x [T, H] bf16 in the P16 layout of the MFMA path: within each
+// 32-input chunk, position 2i + h holds input i + 16h (the permute that rides
+// along with the sort's first launch).
+__device__ __forceinline__ void permute_dw(const uint16_t* __restrict__ x, int64_t n_dw,
+                                           uint32_t* __restrict__ xp, int64_t q)
+{
+    if (q >= n_dw) return;
+    const int64_t chunk = q >> 4;
+    const int i = (int)(q & 15);
+    const uint16_t* src = x + chunk * 32;
+    xp[q] = (uint32_t)src[i] | ((uint32_t)src[i + 16] << 16);
+}
 
 // Inclusive scan over the 64 lanes of a wave (shuffles; integer, exact).
 __device__ inline int wave_inclusive_scan(int v, int lane)
@@ -90,13 +105,19 @@ __global__ __launch_bounds__(1024) void sort_small_kernel(const int32_t* __restr
                                                           int E, int P, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted_pairs,
                                                           int32_t* __restrict__ pass_table,
-                                                          uint32_t* __restrict__ err)
+                                                          uint32_t* __restrict__ err,
+                                                          const uint16_t* __restrict__ x, int64_t n_dw,
+                                                          uint32_t* __restrict__ xp)
 {
     __shared__ int s_e[kSmallMax];
     __shared__ int s_cnt[1024];
     __shared__ int s_tmp[1024];
     __shared__ int s_hit[1024];
     const int tid = threadIdx.x;
+    if (blockIdx.x > 0) {  // workgroups past the first: the permute of x
+        permute_dw(x, n_dw, xp, (int64_t)(blockIdx.x - 1) * 1024 + tid);
+        return;
+    }
     int e = -1;
     if (tid < n) {
         e = ids[tid];
@@ -121,11 +142,17 @@ __global__ __launch_bounds__(1024) void sort_small_kernel(const int32_t* __restr
 __global__ __launch_bounds__(kTile) void sort_tile_kernel(const int32_t* __restrict__ ids, int n,
                                                           int E, int32_t* __restrict__ tile_counts,
                                                           int32_t* __restrict__ rank_out,
-                                                          uint32_t* __restrict__ err)
+                                                          uint32_t* __restrict__ err, int tiles,
+                                                          const uint16_t* __restrict__ x, int64_t n_dw,
+                                                          uint32_t* __restrict__ xp)
 {
     __shared__ int s_e[kTile];
     __shared__ int s_cnt[1024];
     const int tid = threadIdx.x;
+    if ((int)blockIdx.x >= tiles) {  // workgroups past the tiles: the permute of x
+        permute_dw(x, n_dw, xp, (int64_t)(blockIdx.x - tiles) * kTile + tid);
+        return;
+    }
     const int p = blockIdx.x * kTile + tid;
     for (int i = tid; i < E; i += kTile) s_cnt[i] = 0;
     int e = -1;
@@ -208,19 +235,22 @@ size_t sort_ws_bytes(int T, int k, int E)
 
 hipError_t launch_sort(const int32_t* ids, int T, int k, int E, int P, int32_t* offsets,
                        int32_t* sorted_pairs, int32_t* pass_table, void* ws, uint32_t* err,
-                       hipStream_t s)
+                       hipStream_t s, const uint16_t* x_perm, int H, uint16_t* xp)
 {
     const int n = T * k;
+    const int64_t n_dw = x_perm ? (int64_t)T * H / 2 : 0;  // permute dwords riding along
     if (n <= kSmallMax) {
-        hipLaunchKernelGGL(sort_small_kernel, dim3(1), dim3(1024), 0, s, ids, n, E, P, offsets,
-                           sorted_pairs, pass_table, err);
+        const int64_t pb = (n_dw + 1023) / 1024;
+        hipLaunchKernelGGL(sort_small_kernel, dim3((unsigned)(1 + pb)), dim3(1024), 0, s, ids, n, E, P, offsets,
+                           sorted_pairs, pass_table, err, x_perm, n_dw, (uint32_t*)xp);
         return hipGetLastError();
     }
     const int tiles = (n + kTile - 1) / kTile;
+    const int64_t pb = (n_dw + kTile - 1) / kTile;
     int32_t* tile_counts = (int32_t*)ws;
     int32_t* ranks = tile_counts + (size_t)tiles * E;
-    hipLaunchKernelGGL(sort_tile_kernel, dim3(tiles), dim3(kTile), 0, s, ids, n, E, tile_counts,
-                       ranks, err);
+    hipLaunchKernelGGL(sort_tile_kernel, dim3((unsigned)(tiles + pb)), dim3(kTile), 0, s, ids, n, E, tile_counts,
+                       ranks, err, tiles, x_perm, n_dw, (uint32_t*)xp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), 0, s, E, P, tiles, tile_counts, offsets,
