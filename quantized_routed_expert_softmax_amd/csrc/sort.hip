@@ -11,9 +11,10 @@
 // a pair's place is offsets[e] + (pairs of e in earlier tiles) + (pairs of e
 // earlier in its own tile), which is the stable order by pair id.
 //   n <= 1024 : one block does everything (decode and small batches).
-//   n >  1024 : tile kernel (per-tile counts and in-tile ranks), one block that
-//               turns the counts into per-tile bases, offsets and the pass table,
-//               and a scatter kernel with one thread per pair.
+//   n >  1024 : tile kernel (per-tile counts and in-tile ranks), then one block
+//               per tile that sums the counts into totals and its tile's bases,
+//               scans the totals into offsets (block 0 writes them and the pass
+//               table) and places its tile's pairs: two launches.
 // The MFMA path's permute of x rides along in extra workgroups of the first
 // launch (it does not depend on the sort).
 #include "../../include/moe.h"
@@ -71,10 +72,15 @@ __device__ int block_exclusive_scan(int* s, int E, int* s_tmp)
 }
 
 // Offsets, pass table and hit list from per-expert counts (s_cnt, length E),
-// leaving exclusive offsets in s_cnt.  Runs on a full 1024-thread block.
+// leaving exclusive offsets in s_cnt.  Runs on a full 1024-thread block; with
+// offsets and pass_table null it only computes the offsets in s_cnt.
 __device__ void write_offsets_and_passes(int* s_cnt, int* s_tmp, int* s_hit, int E, int P,
                                          int32_t* offsets, int32_t* pass_table)
 {
+    if (!offsets) {
+        block_exclusive_scan(s_cnt, E, s_tmp);
+        return;
+    }
     const int tid = threadIdx.x;
     const int cnt = tid < E ? s_cnt[tid] : 0;
     if (tid < E) s_hit[tid] = cnt > 0 ? 1 : 0;
@@ -175,52 +181,52 @@ __global__ __launch_bounds__(kTile) void sort_tile_kernel(const int32_t* __restr
     for (int i = tid; i < E; i += kTile) tc[i] = s_cnt[i];
 }
 
-// One block: per-expert running sums over tiles (tile_counts becomes the base of
-// each expert within each tile), offsets and the pass table.
-__global__ __launch_bounds__(1024) void sort_scan_kernel(int E, int P, int n_tiles,
-                                                         int32_t* __restrict__ tile_counts,
-                                                         int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ pass_table)
+// One block per tile, after the tile kernel: every block sums the tile counts of
+// all experts (the totals, and its own tile's base per expert: the counts of the
+// tiles before it) and scans the totals into offsets itself, so no launch has
+// to wait for a single scan block; block 0 also writes the offsets and the pass
+// table.  Then each pair goes to offsets[e] + base of e in its tile + its rank in
+// the tile.
+__global__ __launch_bounds__(1024) void sort_place_kernel(const int32_t* __restrict__ ids, int n, int E, int P,
+                                                          int n_tiles, const int32_t* __restrict__ tile_counts,
+                                                          const int32_t* __restrict__ rank_in,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ pass_table,
+                                                          int32_t* __restrict__ sorted_pairs)
 {
     __shared__ int s_cnt[1024];
     __shared__ int s_tmp[1024];
     __shared__ int s_hit[1024];
-    const int tid = threadIdx.x;
+    __shared__ int s_base[1024];
+    const int tid = threadIdx.x, b = blockIdx.x;
     if (tid < E) {
-        // running sum over tiles; 16 independent loads per round trip
-        int run = 0;
+        // 16 independent loads per round trip
+        int run = 0, base = 0;
         for (int b0 = 0; b0 < n_tiles; b0 += 16) {
             int v[16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                v[j] = b0 + j < n_tiles ? tile_counts[(size_t)(b0 + j) * E + tid] : 0;
+            for (int j = 0; j < 16; ++j) v[j] = b0 + j < n_tiles ? tile_counts[(size_t)(b0 + j) * E + tid] : 0;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                if (b0 + j < n_tiles) {
-                    tile_counts[(size_t)(b0 + j) * E + tid] = run;  // tile base of expert tid
-                    run += v[j];
-                }
+                if (b0 + j == b) base = run;
+                run += v[j];
             }
         }
         s_cnt[tid] = run;
+        s_base[tid] = base;
     }
     __syncthreads();
-    write_offsets_and_passes(s_cnt, s_tmp, s_hit, E, P, offsets, pass_table);
-}
-
-// One thread per pair: place = offsets[e] + base of e in the pair's tile + rank in tile.
-__global__ __launch_bounds__(kTile) void sort_scatter_kernel(const int32_t* __restrict__ ids, int n, int E,
-                                                             const int32_t* __restrict__ tile_base,
-                                                             const int32_t* __restrict__ rank_in,
-                                                             const int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ sorted_pairs)
-{
-    const int p = blockIdx.x * kTile + threadIdx.x;
-    if (p >= n) return;
-    const int e = ids[p];
-    if (e < 0 || e >= E) return;  // flagged by the tile kernel
-    const int r = rank_in[p];
-    sorted_pairs[offsets[e] + tile_base[(size_t)blockIdx.x * E + e] + r] = p;
+    write_offsets_and_passes(s_cnt, s_tmp, s_hit, E, P, b == 0 ? offsets : nullptr,
+                             b == 0 ? pass_table : nullptr);
+    __syncthreads();
+    if (tid < kTile) {
+        const int p = b * kTile + tid;
+        if (p < n) {
+            const int e = ids[p];
+            if (e >= 0 && e < E)  // (out-of-range ids are flagged by the tile kernel)
+                sorted_pairs[s_cnt[e] + s_base[e] + rank_in[p]] = p;
+        }
+    }
 }
 
 }  // namespace
@@ -253,12 +259,8 @@ hipError_t launch_sort(const int32_t* ids, int T, int k, int E, int P, int32_t* 
                        ranks, err, tiles, x_perm, n_dw, (uint32_t*)xp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), 0, s, E, P, tiles, tile_counts, offsets,
-                       pass_table);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sort_scatter_kernel, dim3(tiles), dim3(kTile), 0, s, ids, n, E, tile_counts, ranks,
-                       offsets, sorted_pairs);
+    hipLaunchKernelGGL(sort_place_kernel, dim3(tiles), dim3(1024), 0, s, ids, n, E, P, tiles, tile_counts, ranks,
+                       offsets, pass_table, sorted_pairs);
     return hipGetLastError();
 }
 
