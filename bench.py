@@ -453,7 +453,7 @@ def bf16_lines(torch, B, synth, wl, dev, err):
         "decode_us_per_layer": round(us, 2),
         "decode_hbm_gbs": round(dec_bytes / (us * 1e-6) / 1e9, 1),
         "decode_hbm_frac": round(dec_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-        "decode_path": "fused decode kernel decode_layer_kernel<16,16,1,1,8>: routing, sort, gate/up + SwiGLU, down and combine in one launch per layer, 48 layer-steps in one HIP graph",
+        "decode_path": "one-token kernel decode1_kernel<16,16,16,1,10,1,1,2>: routing, gate/up + SwiGLU, down and combine in one launch per layer, 48 layer-steps in one HIP graph",
         "prefill_chunk_us": round(p_us, 2),
         "prefill_hbm_gbs": round(p_bytes / (p_us * 1e-6) / 1e9, 1),
         "prefill_hbm_frac": round(p_bytes / (p_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -724,8 +724,8 @@ def mixed_lines(torch, B, mb, synth, dev, err, steps):
     res["workload"] = ("mixed: 48 layers x (hidden 2048, 128 experts, intermediate 768, top-8), 4-bit "
                        "experts, 6-bit down on layers l % 4 == 3 (two size classes: 2654208 and 3047424 B), "
                        "every expert resident, pre-norm residual chain, one HIP graph per step")
-    res["kernel"] = ("moe_layer_forward, one launch per layer at batch 1: decode1_kernel<4,4,8,3,8> on the "
-                     "4-bit layers, decode1_kernel<4,6,8,3,8> on the 6-bit-down layers; batch 8: routing, sort, "
+    res["kernel"] = ("moe_layer_forward, one launch per layer at batch 1: decode1_kernel<4,4,8,3,8,2,2,4> on the "
+                     "4-bit layers, decode1_kernel<4,6,8,3,8,2,2,4> on the 6-bit-down layers; batch 8: routing, sort, "
                      "permute, mfma_grouped_kernel gate/up and down, combine")
     res["frac_basis"] = "distinct routed experts' bytes per step / the 48 layer launches' time (graph of layer launches only)"
     return res
@@ -1045,7 +1045,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "decode1_kernel<3,3,16,1,10> (moe_layer_forward: route + hit list + "
+                     "kernel": "decode1_kernel<3,3,16,1,10,2,2,4> (moe_layer_forward: route + hit list + "
                                "gate/up + SwiGLU + down + combine, one launch per layer)",
                      "avg_launch_us": round(fwd_ms_avg * 1000.0, 3),
                      "bytes_per_launch": int(bytes_per_launch)},

@@ -60,9 +60,8 @@ namespace moe {
 namespace {
 
 constexpr int kD1MaxK = 16;   // routed experts per token on this path
-constexpr int kD1MaxItems = 2;  // phase-1 items per wave
-constexpr int kD1MaxHits = 2;   // phase-2 experts per wave
-constexpr int kD1MaxLoads = 4;  // phase-2 row loads per expert and wave
+// Per variant: MI phase-1 items per wave, MH phase-2 experts per wave and ML
+// phase-2 row loads per expert and wave at most (registers are sized for them).
 
 struct D1Params {
     const float* logits;    // route in-kernel when not null
@@ -183,7 +182,7 @@ __device__ __forceinline__ void load_unit1(Unit<B>& u, const uint8_t* __restrict
     else u.sb = 0u;
 }
 
-template <int BG, int BD, int LPRD, int UD, int W>
+template <int BG, int BD, int LPRD, int UD, int W, int MI, int MH, int ML>
 __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
 {
     static_assert(W >= 8, "eight list waves route 512 logits");
@@ -196,7 +195,7 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
     __shared__ int s_bad[8];
     __shared__ uint32_t s_h[W][512];        // h of the wave's current expert (P16, layout swz)
     __shared__ float s_hs[W][32];           // its unit sums
-    __shared__ float s_y[kD1MaxHits][W][64];  // down rows of each wave's experts
+    __shared__ float s_y[MH][W][64];        // down rows of each wave's experts
     __shared__ float s_hw[kD1MaxK];         // weight of each hit
     __shared__ int32_t s_hslot[kD1MaxK];    // slot of each hit, -1 not resident (slow path)
     __shared__ int32_t s_ord[kD1MaxK];      // hits by ascending expert id
@@ -344,11 +343,11 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
     const int half_i = I >> 1;
     const int n_items = n_hit * half_i;
     const int ipw = P.ipw;
-    Unit<BG> gu[kD1MaxItems][4];
-    int it_hit[kD1MaxItems], it_p[kD1MaxItems], it_slot[kD1MaxItems];
+    Unit<BG> gu[MI][4];
+    int it_hit[MI], it_p[MI], it_slot[MI];
     const uint32_t g_row_b = (uint32_t)(H * BG / 8), g_sb_b = (uint32_t)(H / 16);
 #pragma unroll
-    for (int q = 0; q < kD1MaxItems; ++q) {
+    for (int q = 0; q < MI; ++q) {
         const int li = wave + W * q;
         const int it = blockIdx.x * ipw + li;
         const bool on = li < ipw && it < n_items;
@@ -372,16 +371,16 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
     const int n_ld = P.rows_per_wg / RPL;  // row loads per hit
     const int seg = lane & (LPRD - 1), rl = lane / LPRD;
     const uint32_t d_row_b = (uint32_t)(I * BD / 8), d_sb_b = (uint32_t)(I / 16);
-    RowLoad<BD, UD> dr[kD1MaxHits][kD1MaxLoads];
-    int hs_slot[kD1MaxHits];
+    RowLoad<BD, UD> dr[MH][ML];
+    int hs_slot[MH];
 #pragma unroll
-    for (int q = 0; q < kD1MaxHits; ++q) {
+    for (int q = 0; q < MH; ++q) {
         const int h = wave + W * q;
         hs_slot[q] = h >= n_hit ? -1 : fast ? __builtin_amdgcn_readlane(hsl, h) : s_hslot[h];
         if (hs_slot[q] >= 0) {
             const uint8_t* base = P.pool + (size_t)hs_slot[q] * (size_t)P.slot_bytes;
 #pragma unroll
-            for (int ld = 0; ld < kD1MaxLoads; ++ld) {
+            for (int ld = 0; ld < ML; ++ld) {
                 const int row = row0 + ld * RPL + rl;
                 if (ld < n_ld && row < H)
                     load_row<BD, UD>(dr[q][ld], base, (uint32_t)P.off_d_codes + (uint32_t)row * d_row_b,
@@ -407,7 +406,7 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
 #pragma unroll
         for (int i = 0; i < 16; ++i) xsum = dot2(xp[i], MOE_ONES_PAIR, xsum);
 #pragma unroll
-        for (int q = 0; q < kD1MaxItems; ++q) {
+        for (int q = 0; q < MI; ++q) {
             if (it_hit[q] < 0) continue;
             uint64_t word = tag_hi;  // not resident: zeros, so readers are not kept waiting
             if (it_slot[q] >= 0) {
@@ -491,12 +490,12 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
     // ---- 6. phase 2: own experts' h, down rows ----
     const int Ud = I >> 5;
 #pragma unroll
-    for (int q = 0; q < kD1MaxHits; ++q) {
+    for (int q = 0; q < MH; ++q) {
         const int h = wave + W * q;
         if (h >= n_hit) continue;
         if (hs_slot[q] < 0) {  // not resident (flagged): contributes zeros
 #pragma unroll
-            for (int ld = 0; ld < kD1MaxLoads; ++ld)
+            for (int ld = 0; ld < ML; ++ld)
                 if (ld < n_ld && seg == 0) s_y[q][wave][ld * RPL + rl] = 0.0f;
             continue;
         }
@@ -549,7 +548,7 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
 #pragma unroll
-        for (int ld = 0; ld < kD1MaxLoads; ++ld) {
+        for (int ld = 0; ld < ML; ++ld) {
             if (ld >= n_ld) continue;
             float y = row_dot_raw<BD, UD>(dr[q][ld], s_h[wave], s_hs[wave], seg, LPRD);
             y = seg_sum_w<LPRD>(y);
@@ -576,34 +575,38 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
 }
 
 struct D1Variant {
-    int bg, bd, lprd, ud, w;
+    int bg, bd, lprd, ud, w, mi, mh, ml;
     hipError_t (*launch)(const D1Params&, int, hipStream_t);
     int (*occ)();
 };
 
-template <int BG, int BD, int LPRD, int UD, int W>
+template <int BG, int BD, int LPRD, int UD, int W, int MI, int MH, int ML>
 hipError_t d1_launch(const D1Params& P, int G, hipStream_t s)
 {
-    hipLaunchKernelGGL((decode1_kernel<BG, BD, LPRD, UD, W>), dim3(G), dim3(64 * W), 0, s, P);
+    hipLaunchKernelGGL((decode1_kernel<BG, BD, LPRD, UD, W, MI, MH, ML>), dim3(G), dim3(64 * W), 0, s, P);
     return hipGetLastError();
 }
 
-template <int BG, int BD, int LPRD, int UD, int W>
+template <int BG, int BD, int LPRD, int UD, int W, int MI, int MH, int ML>
 int d1_occ()
 {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode1_kernel<BG, BD, LPRD, UD, W>, 64 * W, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode1_kernel<BG, BD, LPRD, UD, W, MI, MH, ML>, 64 * W,
+                                                     0) != hipSuccess)
         return 0;
     return nb;
 }
 
-#define MOE_D1(BG, BD, LPRD, UD, W) {BG, BD, LPRD, UD, W, d1_launch<BG, BD, LPRD, UD, W>, d1_occ<BG, BD, LPRD, UD, W>}
+#define MOE_D1(BG, BD, LPRD, UD, W, MI, MH, ML)                                    \
+    {BG, BD, LPRD, UD, W, MI, MH, ML, d1_launch<BG, BD, LPRD, UD, W, MI, MH, ML>, \
+     d1_occ<BG, BD, LPRD, UD, W, MI, MH, ML>}
 const D1Variant kD1Variants[] = {
-    MOE_D1(3, 3, 16, 1, 10),  // hidden 2048, intermediate 512, 3-bit
-    MOE_D1(4, 4, 16, 1, 10),
-    MOE_D1(8, 8, 16, 1, 10),
-    MOE_D1(4, 4, 8, 3, 8),    // hidden 2048, intermediate 768, 4-bit
-    MOE_D1(4, 6, 8, 3, 8),    // ... with 6-bit down
+    MOE_D1(3, 3, 16, 1, 10, 2, 2, 4),  // hidden 2048, intermediate 512, 3-bit
+    MOE_D1(4, 4, 16, 1, 10, 2, 2, 4),
+    MOE_D1(8, 8, 16, 1, 10, 2, 2, 4),
+    MOE_D1(4, 4, 8, 3, 8, 2, 2, 4),    // hidden 2048, intermediate 768, 4-bit
+    MOE_D1(4, 6, 8, 3, 8, 2, 2, 4),    // ... with 6-bit down
+    MOE_D1(16, 16, 16, 1, 10, 1, 1, 2),  // bf16 experts, intermediate 512: one item, expert and two down loads per wave
 };
 #undef MOE_D1
 
@@ -650,7 +653,7 @@ bool d1_grid(const ClassView& c, const D1Variant* v, int* G, int* rows_per_wg)
     int g = n_rg < cus ? n_rg : cus;
     if (g > kMaxGrid) g = kMaxGrid;
     const int rows = ((n_rg + g - 1) / g) * rpl;
-    if (rows / rpl > kD1MaxLoads || rows > 64) return false;
+    if (rows / rpl > v->ml || rows > 64) return false;
     *G = g;
     *rows_per_wg = rows;
     return true;
@@ -671,8 +674,8 @@ bool decode1_supported(int T, int k, int E, int mode, bool routes, const ClassVi
     if (!d1_grid(c, v, &G, &rows)) return false;
     // phase-1 items and phase-2 experts per wave within the kernel's limits
     const int64_t items = (int64_t)k * (c.I / 2);
-    if ((items + G - 1) / G > (int64_t)kD1MaxItems * v->w) return false;
-    if ((k + v->w - 1) / v->w > kD1MaxHits) return false;
+    if ((items + G - 1) / G > (int64_t)v->mi * v->w) return false;
+    if ((k + v->w - 1) / v->w > v->mh) return false;
     if ((int64_t)k * (c.I / 2) > MOE_WS_XWORDS) return false;
     return v->occ() >= 1;
 }
