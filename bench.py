@@ -725,7 +725,7 @@ def mixed_lines(torch, B, mb, synth, dev, err, steps):
                        "experts, 6-bit down on layers l % 4 == 3 (two size classes: 2654208 and 3047424 B), "
                        "every expert resident, pre-norm residual chain, one HIP graph per step")
     res["kernel"] = ("moe_layer_forward, one launch per layer at batch 1: decode1_kernel<4,4,8,3,8,2,2,4> on the "
-                     "4-bit layers, decode1_kernel<4,6,8,3,8,2,2,4> on the 6-bit-down layers; batch 8: routing, sort, "
+                     "4-bit layers, decode1_kernel<4,6,8,3,8,2,2,4> on the 6-bit-down layers; batch 8: routing, "
                      "sort (with the permute of x), mfma_lds_kernel gate/up and down, combine")
     res["frac_basis"] = "distinct routed experts' bytes per step / the 48 layer launches' time (graph of layer launches only)"
     return res
