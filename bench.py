@@ -76,7 +76,7 @@ DECODE_SOURCES = ["quantized_routed_expert_softmax_amd/csrc/decode1.hip",
                   "quantized_routed_expert_softmax_amd/csrc/route_dev.h",
                   "quantized_routed_expert_softmax_amd/csrc/moe_dev.h",
                   "include/moe.h"]
-TRAFFIC_SUMMARY = "profiles/decode1_kernel_3_3_16_1_10-decode48.md"
+TRAFFIC_SUMMARY = "profiles/decode1_kernel_3_3_16_1_10_2_2_4-decode48.md"
 
 
 def decode_sources_sha256():
