@@ -429,10 +429,12 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
         }
     }
 
-    // ---- 5. routing weights, by wave 0 after its phase-1 items (nothing before
-    // the final combine needs them; computed earlier they would hold up wave 0's
-    // share of phase 1, which every expert's consumers wait for) ----
-    if (wave == 0) {
+    // ---- 5. routing weights, after the wave's phase-1 items (nothing before the
+    // final combine needs them; computed earlier they would hold up phase 1,
+    // which every expert's consumers wait for).  On the fast path every wave has
+    // the routing, and wave 2 takes it: its SIMD runs two waves, not three; the
+    // slow path's routing lives in wave 0 ----
+    if (wave == (fast ? 2 : 0)) {
         if (P.logits && fast) {
             // m and Z of the contract over every logit, p of the chosen, ordered by
             // (p desc, id asc), weights = p / (their sum in that order)
