@@ -28,11 +28,12 @@
 //      workgroup's output rows of down for its own expert(s)), so the layer's
 //      bytes are in flight from the first microsecond of streaming;
 //   4. phase 1: SwiGLU pairs published as 64-bit (h pair, call tag) words;
-//   5. wave 0 then computes the routing weights (they need Z over all logits;
+//   5. one wave then computes the routing weights (they need Z over all logits;
 //      nothing before the final combine uses them, and computing them before
 //      its phase-1 item would delay words that every consumer waits for);
-//   6. phase 2: a wave polls only its own expert's h words (first one word with
-//      pauses, then all of them), stages them in its own LDS, computes its rows
+//   6. phase 2: a wave polls only its own expert's h words (first one word that
+//      a workgroup's last item slot writes, with pauses, then all of them),
+//      stages them in its own LDS, computes its rows
 //      of down and weights them; partial sums meet in LDS and become the bf16
 //      output rows, summed over the hits in ascending expert id (fixed order,
 //      the same whichever routing order the hits were numbered in).
@@ -40,7 +41,8 @@
 // first workgroup's start): routing done 1.9 us, rows requested 2.3 us, phase 1
 // done 3.9-5.3 us (the third wave on a SIMD finishes last: 10 items on 4 SIMDs,
 // ~0.6 us of VALU work each), h complete 7.2 us, end 8.4 us; plus ~1.4 us from
-// the previous kernel's end to this one's start.
+// the previous kernel's end to this one's start.  (Taken before the poll read a
+// last-slot word first, which moved the end about 0.4 us earlier.)
 // All workgroups are co-resident (one per compute unit, occupancy checked on the
 // host), so every polled word is eventually written; the poll is bounded and
 // reports MOE_ERRW_TIMEOUT instead of hanging.
