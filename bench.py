@@ -63,6 +63,8 @@ def parse():
                    help="skip the mixed, 8-bit substitution, bounded prefill and ceiling lines")
     p.add_argument("--ceilings", action="store_true",
                    help="only the ceiling microbenchmarks (full read curve, latency, MFMA peak, launch floor)")
+    p.add_argument("--bounded-only", action="store_true",
+                   help="run only the bounded-cache prefill line (for a copy/kernel timeline)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (to scale the FETCH_SIZE / WRITE_SIZE "
                         "counters of a profiling run)")
@@ -948,6 +950,10 @@ def main():
         return
     if args.ceilings:
         print(json.dumps({"ceilings": ceilings(torch, mb, dev)}), flush=True)
+        return
+    if args.bounded_only:
+        r = prefill_bounded_line(torch, B, synth, dev, torch.zeros(1, dtype=torch.int32, device=dev))
+        print(json.dumps({"prefill_bounded": r}), flush=True)
         return
     # the bounded-cache prefill first, before the decode pools exist: its pinned
     # host tier mapped after a 135 GB device allocate/free cycle made a share of

@@ -957,6 +957,11 @@ int moe_pipeline_prepare(moe_pipeline* p, int layer, const int32_t* ids, int n, 
     }
     const int t = (int)(p->table_next++ % kTableRing);
     lk.unlock();
+    // one wait per distinct fill event: the slots of a coalesced run share one
+    // (a wait costs several microseconds of host time; 64 of them per pass were
+    // most of a pass's prepare)
+    std::sort(evs.begin(), evs.end());
+    evs.erase(std::unique(evs.begin(), evs.end()), evs.end());
     for (int ev : evs)
         if (hipStreamWaitEvent(compute, p->fill_ring[ev], 0) != hipSuccess)
             return pfail(MOE_E_HIP, "moe_pipeline_prepare: stream wait failed");
