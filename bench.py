@@ -848,9 +848,10 @@ def prefill_bounded_line(torch, B, synth, dev, err, n_layers=4, slots=128, n_cop
         pool = torch.zeros(slots * lay.slot_bytes, dtype=torch.uint8, device=dev)
     cache = B.moe_cache_create([desc], [0] * n_layers, E)
     st = B.moe_store_open_memory(store, [desc], [0] * n_layers, E)
-    # four copy streams: measured 26.8 GB/s of installs per layer-chunk against
-    # 18.6 GB/s with two (each stream waits for the release of the pass before
-    # the last before its copies, so more streams keep more copies in flight)
+    # four copy streams: with one copy per row they gave 26.8 GB/s of installs per
+    # layer-chunk against 18.6 GB/s with two (each stream waits for the release
+    # of the pass before the last before its copies, so more streams keep more
+    # copies in flight); a pass is now one coalesced copy
     copies = [torch.cuda.Stream() for _ in range(n_copy)]
     p = B.moe_pipeline_create(cache, st, [pool], host_tier_bytes=store.nbytes, host_preload=True, io_threads=4,
                               staging_rows=8, copy_streams=copies)
