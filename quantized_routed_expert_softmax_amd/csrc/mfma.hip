@@ -450,7 +450,7 @@ __device__ __forceinline__ void dma4(const void* g, void* lds_wave_base)
 }
 
 template <int B, bool GU, int MT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 2 ? (GU ? 3 : 4) : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT <= 2 ? (GU ? 3 : 4) : 1)))
 void mfma_lds_kernel(
     const uint16_t* __restrict__ act, int H, int I, int k, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ sorted_pairs, const int32_t* __restrict__ pass_table, int E,
@@ -687,12 +687,15 @@ static int pass_hits_max(int T, int k, int E, int pass_lo, int pass_hi)
     return (int)(m < p ? m : p);
 }
 
-// M-tiles per sweep: 2 (32 rows) when experts average few rows, else 4.
+// M-tiles per sweep: 1 (16 rows) when experts average at most two rows (small
+// batches: half the activation loads and matrix work of 32-row sweeps, and room
+// for a fourth workgroup per CU), 2 (32 rows) when they average few, else 4.
+// Width 16's register-staged kernel has no 1-tile variant and takes 2.
 static int pick_mt(int T, int k, int E)
 {
     const int64_t pairs = (int64_t)T * k;
     const int64_t hits = pairs < E ? pairs : E;
-    return pairs > 40 * hits ? 4 : 2;
+    return pairs > 40 * hits ? 4 : pairs <= 2 * hits ? 1 : 2;
 }
 
 hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const SortView& sv,
@@ -714,10 +717,10 @@ hipError_t launch_mfma_gateup(const uint16_t* xp, int T, int k, int E, const Sor
                        E, pass_lo, pass_hi, table, pool, c.n_slots, c.slot_bytes, c.off_gu_codes, c.off_gu_sb, hbuf,    \
                        nullptr, err)
     switch (c.bits_gu) {
-    case 3: if (mt == 4) MOE_MG3(3, 4); else MOE_MG3(3, 2); break;
-    case 4: if (mt == 4) MOE_MG3(4, 4); else MOE_MG3(4, 2); break;
-    case 6: if (mt == 4) MOE_MG3(6, 4); else MOE_MG3(6, 2); break;
-    case 8: if (mt == 4) MOE_MG3(8, 4); else MOE_MG3(8, 2); break;
+    case 3: if (mt == 4) MOE_MG3(3, 4); else if (mt == 1) MOE_MG3(3, 1); else MOE_MG3(3, 2); break;
+    case 4: if (mt == 4) MOE_MG3(4, 4); else if (mt == 1) MOE_MG3(4, 1); else MOE_MG3(4, 2); break;
+    case 6: if (mt == 4) MOE_MG3(6, 4); else if (mt == 1) MOE_MG3(6, 1); else MOE_MG3(6, 2); break;
+    case 8: if (mt == 4) MOE_MG3(8, 4); else if (mt == 1) MOE_MG3(8, 1); else MOE_MG3(8, 2); break;
     case 16: MOE_MG2(16); break;
     default: return hipErrorInvalidValue;
     }
@@ -746,10 +749,10 @@ hipError_t launch_mfma_down(int T, int k, int E, const SortView& sv, int pass_lo
                        E, pass_lo, pass_hi, table, pool, c.n_slots, c.slot_bytes, c.off_d_codes, c.off_d_sb, nullptr,  \
                        ybuf, err)
     switch (c.bits_d) {
-    case 3: if (mt == 4) MOE_MD3(3, 4); else MOE_MD3(3, 2); break;
-    case 4: if (mt == 4) MOE_MD3(4, 4); else MOE_MD3(4, 2); break;
-    case 6: if (mt == 4) MOE_MD3(6, 4); else MOE_MD3(6, 2); break;
-    case 8: if (mt == 4) MOE_MD3(8, 4); else MOE_MD3(8, 2); break;
+    case 3: if (mt == 4) MOE_MD3(3, 4); else if (mt == 1) MOE_MD3(3, 1); else MOE_MD3(3, 2); break;
+    case 4: if (mt == 4) MOE_MD3(4, 4); else if (mt == 1) MOE_MD3(4, 1); else MOE_MD3(4, 2); break;
+    case 6: if (mt == 4) MOE_MD3(6, 4); else if (mt == 1) MOE_MD3(6, 1); else MOE_MD3(6, 2); break;
+    case 8: if (mt == 4) MOE_MD3(8, 4); else if (mt == 1) MOE_MD3(8, 1); else MOE_MD3(8, 2); break;
     case 16: MOE_MD2(16); break;
     default: return hipErrorInvalidValue;
     }

@@ -249,6 +249,26 @@ def test_forward_mfma_width3_k_tails(shape):
     check_close(out, ref, f"{shape} width 3")
 
 
+@pytest.mark.parametrize("bits", [(3, 3), (4, 6), (8, 8)])
+def test_forward_mfma_one_tile_sweeps(bits):
+    """Small batches over many experts (at most two pairs per expert on average)
+    run the MFMA kernels in sweeps of 16 rows: one expert given 40 of the 96
+    pairs takes three sweeps (16, 16, 8), the others one each."""
+    T, H, E, I, k = 48, 256, 96, 128, 2
+    bg, bd = bits
+    pr = synth.make_problem(950 + bg + bd, T, H, E, I, k, bg, bd, n_slots=E + 3)
+    ids = np.empty((T, k), np.int32)
+    ids[:, 0] = np.where(np.arange(T) < 40, 0, 1 + np.arange(T) % (E - 1))
+    ids[:, 1] = 1 + (np.arange(T) * 7) % (E - 1)
+    ids[:, 1] = np.where(ids[:, 1] == ids[:, 0], 1 + (ids[:, 1] % (E - 1)), ids[:, 1])
+    assert all(len(set(r)) == k for r in ids.tolist())
+    w = np.tile(np.array([0.625, 0.375], np.float32), (T, 1))
+    out, ew = run_forward(pr, ids, w, B.MOE_PATH_MFMA)
+    assert ew == 0
+    ref = oracle.layer(pr.x, ids, w, pr.table, pr.pool, H, I, bg, bd, E, threads=THREADS)
+    check_close(out, ref, f"one-tile sweeps {bits}")
+
+
 @pytest.mark.parametrize("path", [B.MOE_PATH_GEMV, B.MOE_PATH_GEMV3, B.MOE_PATH_MFMA])
 def test_forward_deterministic_and_placement_free(path):
     pr = synth.tiny_problem()
