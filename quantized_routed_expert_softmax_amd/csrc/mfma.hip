@@ -557,6 +557,10 @@ void mfma_lds_kernel(
             if (GU) arow_[i] = act + (size_t)(sorted_pairs[base + m0 + m] / k) * H;
             else arow_[i] = act + (size_t)(base + m0 + m) * I;
         }
+        // the row indices have landed before any stage load is issued (the compiler
+        // does not count LDS-DMA loads, so its own wait for them would be a vmcnt(0)
+        // behind stage 0's code loads)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         f32x4_t acc[NB][MT];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
