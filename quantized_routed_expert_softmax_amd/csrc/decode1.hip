@@ -375,21 +375,28 @@ __global__ __launch_bounds__(64 * W) void decode1_kernel(D1Params P)
     const uint32_t d_row_b = (uint32_t)(I * BD / 8), d_sb_b = (uint32_t)(I / 16);
     RowLoad<BD, UD> dr[MH][ML];
     int hs_slot[MH];
-#pragma unroll
-    for (int q = 0; q < MH; ++q) {
-        const int h = wave + W * q;
-        hs_slot[q] = h >= n_hit ? -1 : fast ? __builtin_amdgcn_readlane(hsl, h) : s_hslot[h];
-        if (hs_slot[q] >= 0) {
-            const uint8_t* base = P.pool + (size_t)hs_slot[q] * (size_t)P.slot_bytes;
-#pragma unroll
-            for (int ld = 0; ld < ML; ++ld) {
-                const int row = row0 + ld * RPL + rl;
-                if (ld < n_ld && row < H)
-                    load_row<BD, UD>(dr[q][ld], base, (uint32_t)P.off_d_codes + (uint32_t)row * d_row_b,
-                                     (uint32_t)P.off_d_sb + (uint32_t)row * d_sb_b, seg, LPRD);
-            }
-        }
+    // bf16 experts (a layer of ~63 MB, bound by bandwidth rather than by round
+    // trips): a wave requests its down rows only once its gate/up rows are in, so
+    // the bytes phase 1 waits for are not shared with bytes only phase 2 needs
+    constexpr bool late_down = (BG == 16);
+#define MOE_D1_REQUEST_DOWN                                                                   \
+    for (int q = 0; q < MH; ++q) {                                                            \
+        const int h = wave + W * q;                                                           \
+        hs_slot[q] = h >= n_hit ? -1 : fast ? __builtin_amdgcn_readlane(hsl, h) : s_hslot[h]; \
+        if (hs_slot[q] >= 0) {                                                                \
+            const uint8_t* base = P.pool + (size_t)hs_slot[q] * (size_t)P.slot_bytes;         \
+            _Pragma("unroll") for (int ld = 0; ld < ML; ++ld) {                               \
+                const int row = row0 + ld * RPL + rl;                                         \
+                if (ld < n_ld && row < H)                                                     \
+                    load_row<BD, UD>(dr[q][ld], base, (uint32_t)P.off_d_codes + (uint32_t)row * d_row_b, \
+                                     (uint32_t)P.off_d_sb + (uint32_t)row * d_sb_b, seg, LPRD);  \
+            }                                                                                 \
+        }                                                                                     \
     }
+    if constexpr (late_down) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's gate/up rows are in
+#pragma unroll
+    MOE_D1_REQUEST_DOWN
+#undef MOE_D1_REQUEST_DOWN
 
     // ---- 4. phase 1: gate/up + SwiGLU -> tagged h pair words ----
     const uint64_t tag_hi = (uint64_t)tag << 32;
